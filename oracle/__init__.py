@@ -1,0 +1,236 @@
+"""CPU oracle for block-quantized-weight matmuls (test infrastructure only).
+
+This package is the independent checker.  Only the test-suite, the smoke
+check and the benchmark's CPU-baseline leg may import it; the product path
+(the HIP library and its Python binding) never does, and shares no code with
+it.  The arithmetic lives in ``qmm_oracle.c`` (plain C, natural loop order,
+double accumulation, exact integers); this module only marshals numpy arrays.
+
+Every function cites the passage of the web pages it follows:
+
+* "onnx-runtime-ep-cpu matmul_nbits.rs" -- MatMulNBits: the module
+  documentation (layout ``[N, ceil(K/bs), bs*bits/8]``, LSB first), the
+  ``dequantize_nbits_value`` formula, ``quantize_activation_signed`` and the
+  CompInt8 block dot of ``int4_dot_row_scalar`` / ``int8_row``.
+* "rlx-cpu quant.rs" -- ``exec_q_mat_mul`` (int32 accumulate, requantize,
+  clamp) and the ``QConv2d`` attribute set.
+* "MNN ConvInt8TiledExecutor.cpp" -- zero-point padding of the im2col and the
+  clamp defaults.
+
+Parity is pinned (see ``tests/test_oracle_*.py``) against hand-decoded bytes,
+closed-form invariants, rounding-tie cases and independent brute-force numpy
+formulations.  The float matmul on the large seeded configurations has no
+printed values on the pages; there only the tolerance applies.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qmm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# -O2 without fast-math and without FMA contraction: the binary32 decisions
+# (activation quantization, conv requantization) must be the plain IEEE ops.
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+          "-shared", "-std=c99", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``qmm_oracle.c`` with gcc into ``liboracle.so`` (in-tree)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB_PATH)
+        i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        sig = {
+            "oracle_unpack_codes": [vp, i64, i64, i64, i32, vp],
+            "oracle_unpack_zero_points": [vp, i64, i64, i32, vp],
+            "oracle_pack_codes": [vp, i64, i64, i64, i32, vp],
+            "oracle_pack_zero_points": [vp, i64, i64, i32, vp],
+            "oracle_dequantize": [vp, vp, vp, i64, i64, i64, i32, vp],
+            "oracle_matmul_nbits": [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
+            "oracle_quantize_a": [vp, i64, i64, i64, vp, vp],
+            "oracle_compint8_block_dots": [vp, vp, vp, i64, i64, i64, i64, i32, vp],
+            "oracle_compint8_matmul": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
+            "oracle_conv_int8": [vp, vp, vp, vp, f32, f32, i32, i32, i32, i32, i32, i32,
+                                 i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp],
+        }
+        for name, argtypes in sig.items():
+            fn = getattr(_lib, name)
+            fn.argtypes = argtypes
+            fn.restype = None
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def n_blocks(K: int, block_size: int) -> int:
+    """ceil(K / block_size) (MatMulNBits module documentation)."""
+    return -(-K // block_size)
+
+
+def blob_bytes(block_size: int, bits: int) -> int:
+    return block_size * bits // 8
+
+
+def zp_row_bytes(k_blocks: int, bits: int) -> int:
+    return -(-(k_blocks * bits) // 8)
+
+
+# -- O1 codec ---------------------------------------------------------------
+
+def unpack_codes(B, N, K, block_size, bits):
+    """Codes ``[N, K]`` (uint8) from packed ``B`` (dequantize_nbits_value)."""
+    B = _c(B, np.uint8)
+    out = np.empty((N, K), np.uint8)
+    _load().oracle_unpack_codes(_ptr(B), N, K, block_size, bits, _ptr(out))
+    return out
+
+
+def unpack_zero_points(zp, N, k_blocks, bits):
+    """Zero points ``[N, kb]``; ``zp=None`` gives the default 2^(bits-1)."""
+    zp = _c(zp, np.uint8)
+    out = np.empty((N, k_blocks), np.uint8)
+    _load().oracle_unpack_zero_points(_ptr(zp), N, k_blocks, bits, _ptr(out))
+    return out
+
+
+def pack_codes(codes, block_size, bits):
+    """Inverse of :func:`unpack_codes`; ``codes`` is ``[N, K]``."""
+    codes = _c(codes, np.uint8)
+    N, K = codes.shape
+    kb = n_blocks(K, block_size)
+    out = np.empty((N, kb, blob_bytes(block_size, bits)), np.uint8)
+    _load().oracle_pack_codes(_ptr(codes), N, K, block_size, bits, _ptr(out))
+    return out
+
+
+def pack_zero_points(zps, bits):
+    """Inverse of :func:`unpack_zero_points`; ``zps`` is ``[N, kb]``."""
+    zps = _c(zps, np.uint8)
+    N, kb = zps.shape
+    out = np.empty((N, zp_row_bytes(kb, bits)), np.uint8)
+    _load().oracle_pack_zero_points(_ptr(zps), N, kb, bits, _ptr(out))
+    return out
+
+
+def dequantize(B, scales, zp, N, K, block_size, bits):
+    """Dense float64 ``[N, K]`` weight (code - zp) * scale."""
+    B = _c(B, np.uint8)
+    s = _c(scales, np.float64)
+    zp = _c(zp, np.uint8)
+    out = np.empty((N, K), np.float64)
+    _load().oracle_dequantize(_ptr(B), _ptr(s), _ptr(zp), N, K, block_size, bits, _ptr(out))
+    return out
+
+
+# -- O2 float matmul ---------------------------------------------------------
+
+def matmul_nbits(A, B, scales, zp, bias, N, K, block_size, bits):
+    """Y = A @ W_deq^T (+ bias) in float64, plus the tolerance base S.
+
+    ``A`` is ``[M, K]`` (any float dtype, widened exactly to float64).
+    Returns ``(Y, S)`` with ``S[m, n] = sum_k |A[m,k] w(n,k)| + |bias[n]|``.
+    """
+    A = _c(np.atleast_2d(A), np.float64)
+    M = A.shape[0]
+    B = _c(B, np.uint8)
+    s = _c(scales, np.float64)
+    zp = _c(zp, np.uint8)
+    bias = _c(bias, np.float64)
+    Y = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _load().oracle_matmul_nbits(_ptr(A), _ptr(B), _ptr(s), _ptr(zp), _ptr(bias), M, N, K,
+                                block_size, bits, _ptr(Y), _ptr(S))
+    return Y, S
+
+
+# -- O3/O4 CompInt8 ------------------------------------------------------------
+
+def quantize_a(A, K, block_size):
+    """Per-row, per-block symmetric int8 quantization of float32 activations.
+
+    Returns ``qa`` ``[M, kb*bs]`` int8 (zero past K) and ``sa`` ``[M, kb]``
+    float32 (quantize_activation_signed).
+    """
+    A = _c(np.atleast_2d(A), np.float32)
+    M = A.shape[0]
+    kb = n_blocks(K, block_size)
+    qa = np.empty((M, kb * block_size), np.int8)
+    sa = np.empty((M, kb), np.float32)
+    _load().oracle_quantize_a(_ptr(A), M, K, block_size, _ptr(qa), _ptr(sa))
+    return qa, sa
+
+
+def compint8_block_dots(qa, B, zp, N, K, block_size, bits):
+    """Exact int32 block dots ``[M, N, kb]``."""
+    qa = _c(qa, np.int8)
+    M = qa.shape[0]
+    kb = n_blocks(K, block_size)
+    out = np.empty((M, N, kb), np.int32)
+    _load().oracle_compint8_block_dots(_ptr(qa), _ptr(_c(B, np.uint8)), _ptr(_c(zp, np.uint8)),
+                                       M, N, K, block_size, bits, _ptr(out))
+    return out
+
+
+def compint8_matmul(qa, sa, B, scales, zp, bias, N, K, block_size, bits):
+    """CompInt8 output in float64 and its tolerance base ``S``."""
+    qa = _c(qa, np.int8)
+    sa = _c(sa, np.float32)
+    M = qa.shape[0]
+    Y = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _load().oracle_compint8_matmul(_ptr(qa), _ptr(sa), _ptr(_c(B, np.uint8)),
+                                   _ptr(_c(scales, np.float64)), _ptr(_c(zp, np.uint8)),
+                                   _ptr(_c(bias, np.float64)), M, N, K, block_size, bits,
+                                   _ptr(Y), _ptr(S))
+    return Y, S
+
+
+# -- O5 int8 conv --------------------------------------------------------------
+
+def conv_int8(X, W, bias, w_scale, in_scale, out_scale, in_zp=0, out_zp=0,
+              clamp_min=-128, clamp_max=127, stride=(1, 1), pad=(0, 0)):
+    """int8 NHWC conv (OHWI weights) with int32 bias and binary32 requant.
+
+    Returns ``(Y int8 [Nb, OH, OW, Co], acc int32 [Nb, OH, OW, Co])``.
+    """
+    X = _c(X, np.int8)
+    W = _c(W, np.int8)
+    Nb, H, Wd, C = X.shape
+    Co, KH, KW, C2 = W.shape
+    assert C2 == C
+    sh, sw = stride
+    ph, pw = pad
+    OH = (H + 2 * ph - KH) // sh + 1
+    OW = (Wd + 2 * pw - KW) // sw + 1
+    Y = np.empty((Nb, OH, OW, Co), np.int8)
+    acc = np.empty((Nb, OH, OW, Co), np.int32)
+    _load().oracle_conv_int8(_ptr(X), _ptr(W), _ptr(_c(bias, np.int32)),
+                             _ptr(_c(w_scale, np.float32)), float(in_scale), float(out_scale),
+                             int(in_zp), int(out_zp), int(clamp_min), int(clamp_max),
+                             Nb, H, Wd, C, Co, KH, KW, sh, sw, ph, pw, _ptr(Y), _ptr(acc))
+    return Y, acc

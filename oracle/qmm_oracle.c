@@ -1,0 +1,324 @@
+/*
+ * qmm_oracle.c -- plain, slow CPU oracle for block-quantized-weight matmuls.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header or table with the HIP
+ * library: every definition below is written out again from the sources it
+ * cites.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ORT]  onnx-runtime-ep-cpu 0.1.0-dev.5, src/kernels/matmul_nbits.rs
+ *          (MatMulNBits: module documentation, dequantize_nbits_value,
+ *           dequantize_weight, prepack_int8_weight, quantize_activation_signed,
+ *           int4_dot_row_scalar, int8_row, execute's bias step)
+ *   [RLX]  rlx-cpu 0.2.13, src/thunk/ops/quant.rs
+ *          (exec_q_mat_mul requantize step, compile_q_conv2d attributes)
+ *   [MNN]  MNN ConvInt8TiledExecutor.cpp
+ *          (initializeConvInt8QuantInfo defaults, im2col padding with the
+ *           input zero point, QuanPostTreatParameters clamp)
+ *
+ * Precision: float results are accumulated in double; integer results are
+ * exact (int32/int64).  Where a floating-point step decides an integer (the
+ * activation quantization of CompInt8, the conv requantization), the step is
+ * done in IEEE binary32 exactly as written, because the device does the same
+ * decision in binary32.  Build with -O2 -fno-fast-math (no contraction).
+ *
+ * Loops run in natural index order.  OpenMP only splits the outer output
+ * loop; each output element is computed by one thread in a fixed order, so
+ * results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* O1 codec                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Number of K blocks: ceil(K / block_size)  ([ORT] module documentation). */
+static int64_t n_blocks(int64_t K, int64_t bs) { return (K + bs - 1) / bs; }
+
+/* Bytes per block of packed codes: block_size * bits / 8  ([ORT] execute). */
+static int64_t blob_bytes(int64_t bs, int bits) { return bs * bits / 8; }
+
+/* Bytes per row of packed zero points: ceil(k_blocks * bits / 8). */
+static int64_t zp_row_bytes(int64_t kb, int bits) { return (kb * bits + 7) / 8; }
+
+/* Code of element k of output row n ([ORT] dequantize_nbits_value): inside
+ * block k / bs the element sits at bit offset (k % bs) * bits, counted from
+ * the least-significant bit of the block's first byte. */
+static unsigned code_at(const uint8_t *B, int64_t n, int64_t k, int64_t K,
+                        int64_t bs, int bits) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t blob = blob_bytes(bs, bits);
+    const uint8_t *row = B + n * kb * blob;
+    int64_t block = k / bs;
+    int64_t bit = (k % bs) * bits;
+    unsigned byte = row[block * blob + bit / 8];
+    unsigned mask = (1u << bits) - 1u;
+    return (byte >> (bit % 8)) & mask;
+}
+
+/* Zero point of block b of row n; the zero-point row packs one bits-wide
+ * value per block, LSB first; absent zero points mean 2^(bits-1)
+ * ([ORT] dequantize_nbits_value, default_zero_point). */
+static unsigned zp_at(const uint8_t *zp, int64_t n, int64_t b, int64_t kb,
+                      int bits) {
+    if (zp == NULL) return 1u << (bits - 1);
+    const uint8_t *row = zp + n * zp_row_bytes(kb, bits);
+    int64_t bit = b * bits;
+    unsigned mask = (1u << bits) - 1u;
+    return (row[bit / 8] >> (bit % 8)) & mask;
+}
+
+/* codes[n*K + k] for every n < N, k < K. */
+EXPORT void oracle_unpack_codes(const uint8_t *B, int64_t N, int64_t K,
+                                int64_t bs, int bits, uint8_t *codes) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            codes[n * K + k] = (uint8_t)code_at(B, n, k, K, bs, bits);
+}
+
+/* zps[n*kb + b]; zp may be NULL (default value). */
+EXPORT void oracle_unpack_zero_points(const uint8_t *zp, int64_t N, int64_t kb,
+                                      int bits, uint8_t *zps) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < kb; ++b)
+            zps[n * kb + b] = (uint8_t)zp_at(zp, n, b, kb, bits);
+}
+
+/* Inverse of oracle_unpack_codes: write codes[n*K + k] into the packed
+ * [N, kb, blob] layout.  Bits past K in the last block are left zero. */
+EXPORT void oracle_pack_codes(const uint8_t *codes, int64_t N, int64_t K,
+                              int64_t bs, int bits, uint8_t *B) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t blob = blob_bytes(bs, bits);
+    memset(B, 0, (size_t)(N * kb * blob));
+    unsigned mask = (1u << bits) - 1u;
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t *row = B + n * kb * blob;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t bit = (k % bs) * bits;
+            row[(k / bs) * blob + bit / 8] |=
+                (uint8_t)((codes[n * K + k] & mask) << (bit % 8));
+        }
+    }
+}
+
+/* Inverse of oracle_unpack_zero_points. */
+EXPORT void oracle_pack_zero_points(const uint8_t *zps, int64_t N, int64_t kb,
+                                    int bits, uint8_t *zp) {
+    int64_t rb = zp_row_bytes(kb, bits);
+    memset(zp, 0, (size_t)(N * rb));
+    unsigned mask = (1u << bits) - 1u;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < kb; ++b) {
+            int64_t bit = b * bits;
+            zp[n * rb + bit / 8] |= (uint8_t)((zps[n * kb + b] & mask) << (bit % 8));
+        }
+}
+
+/* Dequantized weight w[n*K + k] = (code - zp) * scale[n*kb + b], in double
+ * ([ORT] dequantize_nbits_value; scales are given already widened). */
+EXPORT void oracle_dequantize(const uint8_t *B, const double *scales,
+                              const uint8_t *zp, int64_t N, int64_t K,
+                              int64_t bs, int bits, double *W) {
+    int64_t kb = n_blocks(K, bs);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t b = k / bs;
+            double q = (double)code_at(B, n, k, K, bs, bits);
+            double z = (double)zp_at(zp, n, b, kb, bits);
+            W[n * K + k] = (q - z) * scales[n * kb + b];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2 float matmul: Y[m, n] = sum_k A[m, k] * w(n, k)  (+ bias[n])            */
+/* ([ORT] module documentation, execute: dequantize then GEMV/GEMM, bias      */
+/*  added after the product)                                                  */
+/* S[m, n] = sum_k |A[m, k] * w(n, k)| + |bias[n]| is the tolerance base.     */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_matmul_nbits(const double *A, const uint8_t *B,
+                                const double *scales, const uint8_t *zp,
+                                const double *bias, int64_t M, int64_t N,
+                                int64_t K, int64_t bs, int bits, double *Y,
+                                double *S) {
+    int64_t kb = n_blocks(K, bs);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t b = k / bs;
+                double q = (double)code_at(B, n, k, K, bs, bits);
+                double z = (double)zp_at(zp, n, b, kb, bits);
+                double w = (q - z) * scales[n * kb + b];
+                double t = A[m * K + k] * w;
+                acc += t;
+                mag += fabs(t);
+            }
+            if (bias) {
+                acc += bias[n];
+                mag += fabs(bias[n]);
+            }
+            Y[m * N + n] = acc;
+            if (S) S[m * N + n] = mag;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3 CompInt8 activation quantization ([ORT] quantize_activation_signed:    */
+/* per K-block of block_size elements, scale = max|x| / 127, codes rounded    */
+/* to nearest; the padded tail past K stays 0).                               */
+/* Readings: the block width is the weight block_size; the division is the    */
+/* IEEE binary32 quotient x / scale; ties round to even; codes are clamped to */
+/* [-127, 127]; a block whose scale is 0 gets all-zero codes.                 */
+/* qa is [M, kb*bs] int8, sa is [M, kb] float.                                */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_quantize_a(const float *A, int64_t M, int64_t K, int64_t bs,
+                              int8_t *qa, float *sa) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t padded = kb * bs;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < kb; ++b) {
+            int64_t k0 = b * bs;
+            int64_t k1 = k0 + bs < K ? k0 + bs : K;
+            float amax = 0.0f;
+            for (int64_t k = k0; k < k1; ++k) {
+                float a = fabsf(A[m * K + k]);
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 127.0f;
+            sa[m * kb + b] = scale;
+            for (int64_t k = k0; k < k0 + bs; ++k) {
+                int8_t v = 0;
+                if (k < K && scale != 0.0f) {
+                    float r = rintf(A[m * K + k] / scale);
+                    if (r > 127.0f) r = 127.0f;
+                    if (r < -127.0f) r = -127.0f;
+                    v = (int8_t)r;
+                }
+                qa[m * padded + k] = v;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4 CompInt8 block dot ([ORT] prepack_int8_weight + int4_dot_row_scalar /   */
+/* int8_row): dot[m, n, b] = sum over k of block b, k < K, of                 */
+/* qa[m, k] * (code(n, k) - zp(n, b)), exact in integers.                     */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_compint8_block_dots(const int8_t *qa, const uint8_t *B,
+                                       const uint8_t *zp, int64_t M, int64_t N,
+                                       int64_t K, int64_t bs, int bits,
+                                       int32_t *dots) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t padded = kb * bs;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t b = 0; b < kb; ++b) {
+                int64_t z = (int64_t)zp_at(zp, n, b, kb, bits);
+                int64_t acc = 0;
+                for (int64_t k = b * bs; k < (b + 1) * bs && k < K; ++k)
+                    acc += (int64_t)qa[m * padded + k] *
+                           ((int64_t)code_at(B, n, k, K, bs, bits) - z);
+                dots[(m * N + n) * kb + b] = (int32_t)acc;
+            }
+}
+
+/* CompInt8 output: Y[m, n] = sum_b dot[m,n,b] * sa[m,b] * s[n,b] (+ bias[n])
+ * in double ([ORT] int8_row: the signed block dot scaled by the product of the
+ * activation and weight scales, summed over blocks, bias added after).
+ * S[m, n] = sum_k |qa[m,k] * sa[m,b] * w(n,k)| + |bias[n]|. */
+EXPORT void oracle_compint8_matmul(const int8_t *qa, const float *sa,
+                                   const uint8_t *B, const double *scales,
+                                   const uint8_t *zp, const double *bias,
+                                   int64_t M, int64_t N, int64_t K, int64_t bs,
+                                   int bits, double *Y, double *S) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t padded = kb * bs;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < kb; ++b) {
+                int64_t z = (int64_t)zp_at(zp, n, b, kb, bits);
+                int64_t dot = 0, adot = 0;
+                for (int64_t k = b * bs; k < (b + 1) * bs && k < K; ++k) {
+                    int64_t t = (int64_t)qa[m * padded + k] *
+                                ((int64_t)code_at(B, n, k, K, bs, bits) - z);
+                    dot += t;
+                    adot += t < 0 ? -t : t;
+                }
+                double f = (double)sa[m * kb + b] * scales[n * kb + b];
+                acc += (double)dot * f;
+                mag += (double)adot * fabs(f);
+            }
+            if (bias) {
+                acc += bias[n];
+                mag += fabs(bias[n]);
+            }
+            Y[m * N + n] = acc;
+            if (S) S[m * N + n] = mag;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5 int8 convolution with requantization.                                   */
+/* acc = bias[oc] + sum over taps and input channels of                       */
+/*       (x - in_zp) * w, an out-of-bounds tap reading x = in_zp             */
+/*       ([MNN] im2col padding filled with the input zero point;              */
+/*        [RLX] exec_q_mat_mul: bias seeds the int32 accumulator)             */
+/* mult[oc] = (in_scale * w_scale[oc]) / out_scale in binary32                */
+/* y = clamp(rne(float(acc) * mult[oc]) + out_zp, clamp_min, clamp_max)       */
+/*       ([RLX] exec_q_mat_mul requantize; [MNN] clamp bounds; reading:       */
+/*        ties to even)                                                        */
+/* X is NHWC [Nb, H, W, C], Wt is OHWI [Co, KH, KW, C], Y is NHWC             */
+/* [Nb, OH, OW, Co]; groups = dilation = 1; bias may be NULL (zero).          */
+/* acc_out (nullable) receives the int32 accumulators, same layout as Y.      */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_conv_int8(const int8_t *X, const int8_t *Wt,
+                             const int32_t *bias, const float *w_scale,
+                             float in_scale, float out_scale, int in_zp,
+                             int out_zp, int clamp_min, int clamp_max, int Nb,
+                             int H, int W, int C, int Co, int KH, int KW,
+                             int sh, int sw, int ph, int pw, int8_t *Y,
+                             int32_t *acc_out) {
+    int OH = (H + 2 * ph - KH) / sh + 1;
+    int OW = (W + 2 * pw - KW) / sw + 1;
+    for (int nb = 0; nb < Nb; ++nb)
+        for (int oh = 0; oh < OH; ++oh)
+            for (int ow = 0; ow < OW; ++ow)
+                for (int oc = 0; oc < Co; ++oc) {
+                    int64_t acc = bias ? bias[oc] : 0;
+                    for (int kh = 0; kh < KH; ++kh)
+                        for (int kw = 0; kw < KW; ++kw) {
+                            int ih = oh * sh - ph + kh;
+                            int iw = ow * sw - pw + kw;
+                            int inside = ih >= 0 && ih < H && iw >= 0 && iw < W;
+                            for (int c = 0; c < C; ++c) {
+                                int x = inside
+                                    ? X[(((int64_t)nb * H + ih) * W + iw) * C + c]
+                                    : in_zp;
+                                int w = Wt[(((int64_t)oc * KH + kh) * KW + kw) * C + c];
+                                acc += (int64_t)(x - in_zp) * w;
+                            }
+                        }
+                    int64_t o = (((int64_t)nb * OH + oh) * OW + ow) * Co + oc;
+                    if (acc_out) acc_out[o] = (int32_t)acc;
+                    float mult = (in_scale * w_scale[oc]) / out_scale;
+                    float r = rintf((float)acc * mult);
+                    double v = (double)r + (double)out_zp;
+                    if (v < clamp_min) v = clamp_min;
+                    if (v > clamp_max) v = clamp_max;
+                    Y[o] = (int8_t)v;
+                }
+}
