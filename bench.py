@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized-weight matmul hot path on one MI355X.
+
+A step is one M = 1 decode pass over a Llama-3-8B-shaped layer: the seven
+projections (q, k, v, o, gate, up, down; 4-bit asymmetric, block 32, bf16
+activations and scales) run back to back through ``qmm_gemv``.  ``value`` is
+the layer's algorithmic bytes (packed codes + scales + zero points +
+activations + outputs) divided by the measured time per step, in GB/s.
+Weights rotate through enough copies (> 512 MB) that each step streams them
+from HBM instead of the 256 MB Infinity Cache.
+
+The JSON line also carries the roofline of the dominant kernel (the GEMV on
+the 4096 x 14336 gate/up shape, timed by HIP events around a run of its own
+back-to-back launches on the same stream) and the CPU oracle timed on the
+host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+POOL_BYTES = 640 << 20         # rotating weight pool, > 2x the Infinity Cache
+
+METRIC = "int4 GEMV weight GB/s (% HBM peak) at M=1; GEMM TFLOPS (% MFMA) at M=2048"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target wall time of the CPU-oracle sample")
+    return p.parse_args()
+
+
+def layer_bytes(case) -> int:
+    """Algorithmic bytes of one GEMV: codes + scales + zero points + x + y."""
+    return case.weight_bytes() + case.A.numel() * case.A.element_size() \
+        + case.N * case.A.element_size()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode GEMV shards by output column with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    from block_quantized_weight_matmulnbits_amd import qmm
+    from block_quantized_weight_matmulnbits_amd.workloads import decode_layer
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cases = decode_layer()
+    step_bytes = sum(layer_bytes(c) for c in cases)
+    n_copies = max(2, -(-POOL_BYTES // step_bytes))
+    # Copy 0 is the seeded weights; the others are byte-identical copies at
+    # different addresses (only the addresses matter for cache behaviour).
+    pools = []
+    for c in cases:
+        d = c.to(dev)
+        pools.append([(d.B, d.scales, d.zero_points)] +
+                     [(d.B.clone(), d.scales.clone(), d.zero_points.clone())
+                      for _ in range(n_copies - 1)])
+    xs = [c.to(dev).A.reshape(-1) for c in cases]
+    ys = [torch.empty(c.N, dtype=torch.bfloat16, device=dev) for c in cases]
+    stream = torch.cuda.current_stream(dev)
+    dom = [i for i, c in enumerate(cases) if (c.K, c.N) == (4096, 14336)]
+
+    def launch(i, j):
+        c = cases[i]
+        B, sc, zp = pools[i][j]
+        qmm.qmm_gemv(xs[i], B, sc, zp, None, ys[i], c.K, c.N, c.block_size, c.bits, 0, stream)
+
+    def step(s):
+        for i in range(len(cases)):
+            launch(i, s % n_copies)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Dominant kernel: the GEMV on the 4096 x 14336 gate/up shape, launched
+    # back to back (rotating weight copies) between one pair of HIP events on
+    # the launch stream; per-launch events would add their own overhead.
+    n_dom = max(20, args.steps)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(n_dom):
+        launch(dom[s % len(dom)], s % n_copies)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dom_avg_ms = e0.elapsed_time(e1) / n_dom
+    dom_bytes = layer_bytes(cases[dom[0]])
+    achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations x int4 weights, fp32 accumulate",
+        "data": "synthetic",
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {
+            "workload": "decode GEMV, one Llama-3-8B-shaped layer (q,k,v,o,gate,up,down), M=1, "
+                        "bf16 activations, 4-bit asymmetric block 32, bf16 scales, packed zero points",
+            "M": 1,
+            "shapes_KxN": [[c.K, c.N] for c in cases],
+            "bytes_per_step": step_bytes,
+            "weight_copies_rotated": n_copies,
+        },
+        "roofline": {
+            "kernel": "gemv_kernel (4-bit, bf16, zero points) on K=4096 N=14336",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dom_avg_ms * 1e3, 3),
+            "bytes_per_launch": dom_bytes,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cases, seconds):
+    """The oracle (as it stands) on the same layer, on the host cores."""
+    import numpy as np
+
+    import oracle
+    prepared = []
+    for c in cases:
+        prepared.append((c.A.double().numpy().reshape(1, -1), c.B.numpy(), c.scales.double().numpy(),
+                         c.zero_points.numpy(), None, c.N, c.K, c.block_size, c.bits))
+    step_bytes = sum(layer_bytes(c) for c in cases)
+    oracle.matmul_nbits(*prepared[1])            # load + warm the library
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for p in prepared:
+            oracle.matmul_nbits(*p)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {
+        "value": round(step_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the full decode layer (all 7 projections, all outputs), {reps} passes in "
+                  f"{el:.1f} s, OpenMP over output columns",
+        "ms_per_step": round(el / reps * 1e3, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+// qmm_api.cpp -- the extern "C" entry points declared in include/qmm.h:
+// argument validation (mirroring MatMulNBitsFactory::create and execute of
+// onnx-runtime-ep-cpu matmul_nbits.rs, with errors that say what, why and how
+// to fix), then dispatch to the kernel launchers.  Nothing here allocates
+// device memory or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+using qmm::MatArgs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return QMM_OK;
+  return fail(QMM_ERR_HIP, "%s: the HIP runtime reported '%s' while enqueueing the kernel. "
+              "Why: the launch or an earlier asynchronous operation on this device failed. "
+              "How to fix: check the device state and earlier errors on the stream.",
+              fn, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int dtype_size(int dt) {
+  switch (dt) {
+    case QMM_F32: return 4;
+    case QMM_F16: return 2;
+    case QMM_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+enum class Route { Float, CompInt8 };
+
+// Validation shared by qmm_gemv, qmm_gemm and qmm_gemm_compint8.
+int validate_matmul(const char* fn, Route route, const void* A, int a_dtype, const uint8_t* B,
+                    int b_layout, const void* scales, int s_dtype, const uint8_t* zp,
+                    const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
+                    int bits, int accuracy_level, MatArgs* out) {
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: bits must be 2, 4 or 8, got bits=%d. Why: other packed widths have no "
+                "validated unpacking path. How to fix: export the weight with bits=2, 4 or 8.",
+                fn, bits);
+  if (block_size < 16 || !is_pow2(block_size))
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: block_size must be a power of two and at least 16, got %d. Why: the "
+                "operator defines blocks of block_size codes that fill whole bytes. How to fix: "
+                "re-quantize with block_size 16, 32, 64, 128, ...",
+                fn, block_size);
+  if (K <= 0 || N <= 0)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: K and N must be positive, got K=%lld N=%lld. Why: they are required "
+                "positive attributes of the operator. How to fix: pass the weight's K and N.",
+                fn, (long long)K, (long long)N);
+  if (M < 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: M must be >= 0, got %lld. How to fix: pass the "
+                "product of A's leading dimensions.", fn, (long long)M);
+  if (K > INT32_MAX / 2 || N > INT32_MAX / 2 || M > INT32_MAX / 2)
+    return fail(QMM_ERR_UNSUPPORTED,
+                "%s: M, K and N must each be below 2^30 (got M=%lld K=%lld N=%lld). Why: kernel "
+                "indices are 32-bit. How to fix: split the matmul along M or N.",
+                fn, (long long)M, (long long)K, (long long)N);
+  if (dtype_size(a_dtype) == 0 || dtype_size(s_dtype) == 0)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: a_dtype=%d / s_dtype=%d is not a qmm_dtype. Why: A, scales, bias and Y must "
+                "be a float compute dtype. How to fix: pass QMM_F32, QMM_F16 or QMM_BF16.",
+                fn, a_dtype, s_dtype);
+  if (b_layout != QMM_LAYOUT_ORT)
+    return fail(QMM_ERR_UNSUPPORTED,
+                "%s: b_layout=%d is not supported. Why: only the operator's own layout "
+                "[N, kb, block_size*bits/8] is accepted. How to fix: pass QMM_LAYOUT_ORT.",
+                fn, b_layout);
+  if (route == Route::Float && accuracy_level == 4)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: accuracy_level=4 requests int8 activations (CompInt8). Why: this entry "
+                "point computes with float activations and takes no workspace for the int8 "
+                "activations. How to fix: call qmm_gemm_compint8 with a workspace of "
+                "qmm_compint8_workspace_size(M, K, block_size) bytes.", fn);
+  if (route == Route::CompInt8 && accuracy_level != 4)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: accuracy_level must be 4 here, got %d. Why: this entry point implements "
+                "the int8-activation (CompInt8) computation only. How to fix: use qmm_gemm for "
+                "accuracy levels 0-3.", fn, accuracy_level);
+  if (accuracy_level < 0 || accuracy_level > 4)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: accuracy_level must be in 0..4, got %d. Why: 0 = default, 1 = fp32, "
+                "2 = fp16, 3 = bf16, 4 = int8. How to fix: pass one of these.", fn,
+                accuracy_level);
+  if (B == nullptr || scales == nullptr || (M > 0 && (A == nullptr || Y == nullptr)))
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: A, B, scales and Y must be non-null device pointers. Why: they are the "
+                "required inputs and output. How to fix: pass allocated device buffers.", fn);
+  if (!aligned(B, 16))
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: B must be 16-byte aligned. Why: the kernels read packed codes with "
+                "128-bit loads. How to fix: pass a contiguous, freshly allocated tensor.", fn);
+  const int asz = dtype_size(a_dtype);
+  if (!aligned(A, asz) || !aligned(Y, asz) || !aligned(bias, asz) ||
+      !aligned(scales, dtype_size(s_dtype)))
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: A, Y, bias and scales must be aligned to their element size. How to fix: "
+                "pass contiguous tensors.", fn);
+  out->A = A;
+  out->B = B;
+  out->scales = scales;
+  out->zp = zp;
+  out->bias = bias;
+  out->Y = Y;
+  out->M = M;
+  out->K = K;
+  out->N = N;
+  out->block_size = block_size;
+  out->kb = (K + block_size - 1) / block_size;
+  out->blob = (int64_t)block_size * bits / 8;
+  out->zp_row_bytes = (out->kb * bits + 7) / 8;
+  out->bits = bits;
+  out->a_dtype = a_dtype;
+  out->s_dtype = s_dtype;
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmm_last_error(void) { return g_last_error.c_str(); }
+
+int qmm_gemv(const void* A, int a_dtype, const uint8_t* B, int b_layout, const void* scales,
+             int s_dtype, const uint8_t* zero_points, const void* bias, void* Y, int64_t K,
+             int64_t N, int block_size, int bits, int accuracy_level, void* stream) {
+  MatArgs a;
+  int st = validate_matmul("qmm_gemv", Route::Float, A, a_dtype, B, b_layout, scales, s_dtype,
+                           zero_points, bias, Y, 1, K, N, block_size, bits, accuracy_level, &a);
+  if (st != QMM_OK) return st;
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_gemv(a), "qmm_gemv");
+}
+
+int qmm_gemm(const void* A, int a_dtype, const uint8_t* B, int b_layout, const void* scales,
+             int s_dtype, const uint8_t* zero_points, const void* bias, void* Y, int64_t M,
+             int64_t K, int64_t N, int block_size, int bits, int accuracy_level, void* stream) {
+  MatArgs a;
+  int st = validate_matmul("qmm_gemm", Route::Float, A, a_dtype, B, b_layout, scales, s_dtype,
+                           zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level, &a);
+  if (st != QMM_OK) return st;
+  a.stream = (hipStream_t)stream;
+  if (M == 0) return QMM_OK;
+  if (M == 1) return hip_status(qmm::launch_gemv(a), "qmm_gemm");
+  return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm: M > 1 is not built yet.");
+}
+
+size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size) {
+  if (M < 0 || K <= 0 || block_size <= 0) return 0;
+  const int64_t kb = (K + block_size - 1) / block_size;
+  auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
+  // qa [M, kb*bs] int8, sa [M, kb] float, per-block code sums [M, kb] int32.
+  return (size_t)(up(M * kb * block_size) + up(M * kb * 4) + up(M * kb * 4));
+}
+
+int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout,
+                      const void* scales, int s_dtype, const uint8_t* zero_points,
+                      const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
+                      int bits, int accuracy_level, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  MatArgs a;
+  int st = validate_matmul("qmm_gemm_compint8", Route::CompInt8, A, a_dtype, B, b_layout, scales,
+                           s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
+                           accuracy_level, &a);
+  if (st != QMM_OK) return st;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8 is not built yet.");
+}
+
+int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,
+               float in_scale, float out_scale, int in_zp, int out_zp, int clamp_min,
+               int clamp_max, int Nb, int H, int W, int C, int Co, int KH, int KW, int stride_h,
+               int stride_w, int pad_h, int pad_w, int8_t* Y, void* stream) {
+  (void)X; (void)Wt; (void)bias; (void)w_scale; (void)in_scale; (void)out_scale; (void)in_zp;
+  (void)out_zp; (void)clamp_min; (void)clamp_max; (void)Nb; (void)H; (void)W; (void)C; (void)Co;
+  (void)KH; (void)KW; (void)stride_h; (void)stride_w; (void)pad_h; (void)pad_w; (void)Y;
+  (void)stream;
+  return fail(QMM_ERR_UNSUPPORTED, "qconv_int8 is not built yet.");
+}
+
+int qmm_debug_unpack(const uint8_t* B, int b_layout, const void* scales, int s_dtype,
+                     const uint8_t* zero_points, int64_t K, int64_t N, int block_size, int bits,
+                     uint8_t* codes, uint8_t* zps, float* w, void* stream) {
+  (void)B; (void)b_layout; (void)scales; (void)s_dtype; (void)zero_points; (void)K; (void)N;
+  (void)block_size; (void)bits; (void)codes; (void)zps; (void)w; (void)stream;
+  return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_unpack is not built yet.");
+}
+
+int qmm_debug_quantize_a(const void* A, int a_dtype, int64_t M, int64_t K, int block_size,
+                         int8_t* qa, float* sa, void* stream) {
+  (void)A; (void)a_dtype; (void)M; (void)K; (void)block_size; (void)qa; (void)sa; (void)stream;
+  return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_quantize_a is not built yet.");
+}
+
+int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, int b_layout,
+                                  const uint8_t* zero_points, int64_t M, int64_t K, int64_t N,
+                                  int block_size, int bits, int32_t* dots, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  (void)A; (void)a_dtype; (void)B; (void)b_layout; (void)zero_points; (void)M; (void)K; (void)N;
+  (void)block_size; (void)bits; (void)dots; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_compint8_block_dots is not built yet.");
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+"""Thin ctypes binding of libqmm.so (include/qmm.h).
+
+Functions carry the C names and only marshal arguments: torch tensors become
+device pointers, torch dtypes become ``qmm_dtype`` values, and the current
+HIP stream is passed unless one is given.  A negative status raises
+:class:`QmmError` with the library's message.  The library is required:
+importing this module fails loudly when ``libqmm.so`` has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmm.so")
+
+QMM_F32, QMM_F16, QMM_BF16 = 0, 1, 2
+QMM_LAYOUT_ORT = 0
+QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED, QMM_ERR_WORKSPACE, QMM_ERR_HIP = 0, -1, -2, -3, -4
+
+_TORCH_TO_QMM = {torch.float32: QMM_F32, torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m block_quantized_weight_matmulnbits_amd.build). There is no CPU fallback.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_SIGS = {
+    "qmm_last_error": ([], ctypes.c_char_p),
+    "qmm_gemv": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "qmm_gemm": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "qmm_compint8_workspace_size": ([_i64, _i64, _i32], _sz),
+    "qmm_gemm_compint8": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                           _i32, _vp, _sz, _vp], _i32),
+    "qconv_int8": ([_vp, _vp, _vp, _vp, _f32, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "qmm_debug_unpack": ([_vp, _i32, _vp, _i32, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "qmm_debug_quantize_a": ([_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp], _i32),
+    "qmm_debug_compint8_block_dots": ([_vp, _i32, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
+                                       _sz, _vp], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[qmm status {status}] {message}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != QMM_OK:
+        raise QmmError(status, lib.qmm_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dt(t) -> int:
+    return _TORCH_TO_QMM[t.dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def qmm_last_error() -> str:
+    return lib.qmm_last_error().decode()
+
+
+def qmm_gemv(A, B, scales, zero_points, bias, Y, K, N, block_size, bits, accuracy_level=0,
+             stream=None):
+    _check(lib.qmm_gemv(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales),
+                        _ptr(zero_points), _ptr(bias), _ptr(Y), K, N, block_size, bits,
+                        accuracy_level, _stream(stream)))
+
+
+def qmm_gemm(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level=0,
+             stream=None):
+    _check(lib.qmm_gemm(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales),
+                        _ptr(zero_points), _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
+                        accuracy_level, _stream(stream)))
+
+
+def qmm_compint8_workspace_size(M, K, block_size) -> int:
+    return int(lib.qmm_compint8_workspace_size(M, K, block_size))
+
+
+def qmm_gemm_compint8(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, workspace,
+                      accuracy_level=4, stream=None):
+    _check(lib.qmm_gemm_compint8(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales),
+                                 _dt(scales), _ptr(zero_points), _ptr(bias), _ptr(Y), M, K, N,
+                                 block_size, bits, accuracy_level, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def qconv_int8(X, W, bias, w_scale, in_scale, out_scale, in_zp, out_zp, clamp_min, clamp_max,
+               stride, pad, Y, stream=None):
+    Nb, H, Wd, C = X.shape
+    Co, KH, KW, _ = W.shape
+    _check(lib.qconv_int8(_ptr(X), _ptr(W), _ptr(bias), _ptr(w_scale), in_scale, out_scale,
+                          in_zp, out_zp, clamp_min, clamp_max, Nb, H, Wd, C, Co, KH, KW,
+                          stride[0], stride[1], pad[0], pad[1], _ptr(Y), _stream(stream)))
+
+
+def qmm_debug_unpack(B, scales, zero_points, K, N, block_size, bits, codes=None, zps=None, w=None,
+                     stream=None):
+    _check(lib.qmm_debug_unpack(_ptr(B), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales),
+                                _ptr(zero_points), K, N, block_size, bits, _ptr(codes), _ptr(zps),
+                                _ptr(w), _stream(stream)))
+
+
+def qmm_debug_quantize_a(A, M, K, block_size, qa, sa, stream=None):
+    _check(lib.qmm_debug_quantize_a(_ptr(A), _dt(A), M, K, block_size, _ptr(qa), _ptr(sa),
+                                    _stream(stream)))
+
+
+def qmm_debug_compint8_block_dots(A, B, zero_points, M, K, N, block_size, bits, dots, workspace,
+                                  stream=None):
+    _check(lib.qmm_debug_compint8_block_dots(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT,
+                                             _ptr(zero_points), M, K, N, block_size, bits,
+                                             _ptr(dots), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream)))

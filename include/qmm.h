@@ -1,0 +1,163 @@
+/*
+ * qmm.h -- C ABI of the block-quantized-weight matmul library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the MatMulNBits operator as described on the
+ * "onnx-runtime-ep-cpu matmul_nbits.rs" page (module documentation,
+ * MatMulNBitsFactory::create and execute):
+ *
+ *   Y[m, n] = sum_k A[m, k] * w(n, k)  (+ bias[n])
+ *   w(n, k) = (code(n, k) - zp(n, b)) * scale[n, b],   b = k / block_size
+ *
+ * with the weight codes packed least-significant bits first as
+ * B[N, kb, block_size*bits/8] bytes, kb = ceil(K / block_size); scales
+ * [N, kb]; optional packed zero points [N, ceil(kb*bits/8)] bytes (absent
+ * zero points mean 2^(bits-1)).  The dequantized weight is never written to
+ * memory: every kernel unpacks codes in registers.
+ *
+ * Conventions shared by every entry point:
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *    library keeps no pointer after a call returns and never allocates
+ *    device memory during a call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; nothing synchronizes.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    negative qmm_status is returned on error and qmm_last_error() gives a
+ *    thread-local "what / why / how to fix" message.  A failed launch returns
+ *    QMM_ERR_HIP.
+ *  - Arrays are dense and row-major with the shapes given below.
+ *  - dtypes: A, bias and Y share one float dtype (qmm_dtype); scales may
+ *    have any float dtype.  Float results accumulate in fp32.
+ */
+#ifndef QMM_H_
+#define QMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qmm_dtype {
+    QMM_F32 = 0,
+    QMM_F16 = 1,
+    QMM_BF16 = 2
+} qmm_dtype;
+
+typedef enum qmm_layout {
+    /* The operator's own layout: B[N, kb, block_size*bits/8]. */
+    QMM_LAYOUT_ORT = 0
+} qmm_layout;
+
+typedef enum qmm_status {
+    QMM_OK = 0,
+    QMM_ERR_INVALID_ARG = -1,  /* a shape, dtype, pointer or attribute is wrong */
+    QMM_ERR_UNSUPPORTED = -2,  /* valid for the operator, not implemented here  */
+    QMM_ERR_WORKSPACE = -3,    /* workspace missing or too small                */
+    QMM_ERR_HIP = -4           /* the HIP runtime reported an error             */
+} qmm_status;
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char *qmm_last_error(void);
+
+/*
+ * M = 1 decode GEMV (matmul_nbits.rs: execute, the m == 1 routes).
+ *   A      [K]            a_dtype
+ *   B      [N, kb, blob]  uint8, 16-byte aligned, layout QMM_LAYOUT_ORT
+ *   scales [N, kb]        s_dtype
+ *   zero_points [N, ceil(kb*bits/8)] uint8 or NULL
+ *   bias   [N]            a_dtype or NULL
+ *   Y      [N]            a_dtype (written)
+ * bits in {2, 4, 8}; block_size a power of two >= 16 (MatMulNBitsFactory::
+ * create).  accuracy_level 0..3 select float compute; the hint can only raise
+ * precision and every level computes fp32-accumulated products here.
+ * accuracy_level 4 (int8 activations) is rejected: use qmm_gemm_compint8.
+ */
+int qmm_gemv(const void *A, int a_dtype, const uint8_t *B, int b_layout,
+             const void *scales, int s_dtype, const uint8_t *zero_points,
+             const void *bias, void *Y, int64_t K, int64_t N, int block_size,
+             int bits, int accuracy_level, void *stream);
+
+/*
+ * Batched / prefill matmul, A [M, K] -> Y [M, N]; the other arguments as for
+ * qmm_gemv.  M = 0 is a no-op.  bf16 and f16 activations run on the matrix
+ * cores with weights dequantized tile by tile to the activation dtype; f32
+ * activations are computed in fp32.
+ */
+int qmm_gemm(const void *A, int a_dtype, const uint8_t *B, int b_layout,
+             const void *scales, int s_dtype, const uint8_t *zero_points,
+             const void *bias, void *Y, int64_t M, int64_t K, int64_t N,
+             int block_size, int bits, int accuracy_level, void *stream);
+
+/*
+ * CompInt8 (accuracy_level 4; matmul_nbits.rs: quantize_activation_signed,
+ * int4_dot_row_scalar, int8_row).  Each row of A is quantized per K-block of
+ * block_size elements to int8 with scale sa = max|x| / 127 (IEEE binary32
+ * division, round half to even, clamp to [-127, 127]; a block with sa == 0
+ * quantizes to 0).  Then
+ *   dot[m, n, b] = sum_{k in b, k < K} qa[m, k] * (code(n, k) - zp(n, b))
+ * exactly in int32 and Y[m, n] = sum_b float(dot) * (sa[m, b] * scale[n, b])
+ * (+ bias[n]) in fp32.
+ * workspace: device memory of at least qmm_compint8_workspace_size(M, K,
+ * block_size) bytes, 256-byte aligned, owned by the caller, overwritten.
+ * accuracy_level must be 4.  Arguments otherwise as for qmm_gemm.
+ */
+size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size);
+
+int qmm_gemm_compint8(const void *A, int a_dtype, const uint8_t *B,
+                      int b_layout, const void *scales, int s_dtype,
+                      const uint8_t *zero_points, const void *bias, void *Y,
+                      int64_t M, int64_t K, int64_t N, int block_size,
+                      int bits, int accuracy_level, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * int8 convolution with requantization (MNN ConvInt8TiledExecutor.cpp:
+ * initializeConvInt8QuantInfo, im2col padding with the input zero point,
+ * QuanPostTreatParameters clamp; rlx-cpu quant.rs: exec_q_mat_mul).
+ *   X  [Nb, H, W, C]        int8 NHWC
+ *   Wt [Co, KH, KW, C]      int8 OHWI, symmetric (weight zero point 0)
+ *   bias [Co] int32 or NULL; w_scale [Co] float32
+ *   Y  [Nb, OH, OW, Co]     int8 NHWC, OH = (H + 2 pad_h - KH) / stride_h + 1
+ * acc = bias + sum (x - in_zp) * w, a tap outside the image reading in_zp;
+ * mult = (in_scale * w_scale[oc]) / out_scale in binary32;
+ * y = clamp(round_half_even(float(acc) * mult) + out_zp, clamp_min, clamp_max).
+ * A ReLU is expressed as clamp_min = out_zp.  Groups and dilation are 1.
+ * Requires C % 4 == 0 (rows of 4-byte words), |acc| < 2^24.
+ */
+int qconv_int8(const int8_t *X, const int8_t *Wt, const int32_t *bias,
+               const float *w_scale, float in_scale, float out_scale,
+               int in_zp, int out_zp, int clamp_min, int clamp_max, int Nb,
+               int H, int W, int C, int Co, int KH, int KW, int stride_h,
+               int stride_w, int pad_h, int pad_w, int8_t *Y, void *stream);
+
+/*
+ * Test exports: the integer intermediates, for bit-exact comparison.
+ *  qmm_debug_unpack: codes [N, K] uint8, zps [N, kb] uint8 (defaults filled
+ *    in), w [N, K] float32 = (code - zp) * scale; any output may be NULL.
+ *  qmm_debug_quantize_a: qa [M, kb*block_size] int8 (zero past K), sa [M, kb]
+ *    float32, exactly as the first step of qmm_gemm_compint8.
+ *  qmm_debug_compint8_block_dots: dots [M, N, kb] int32 as computed inside
+ *    qmm_gemm_compint8 (same workspace contract).
+ */
+int qmm_debug_unpack(const uint8_t *B, int b_layout, const void *scales,
+                     int s_dtype, const uint8_t *zero_points, int64_t K,
+                     int64_t N, int block_size, int bits, uint8_t *codes,
+                     uint8_t *zps, float *w, void *stream);
+
+int qmm_debug_quantize_a(const void *A, int a_dtype, int64_t M, int64_t K,
+                         int block_size, int8_t *qa, float *sa, void *stream);
+
+int qmm_debug_compint8_block_dots(const void *A, int a_dtype, const uint8_t *B,
+                                  int b_layout, const uint8_t *zero_points,
+                                  int64_t M, int64_t K, int64_t N,
+                                  int block_size, int bits, int32_t *dots,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H_ */
