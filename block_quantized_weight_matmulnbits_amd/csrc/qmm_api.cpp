@@ -171,9 +171,21 @@ int qmm_gemm(const void* A, int a_dtype, const uint8_t* B, int b_layout, const v
 size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size) {
   if (M < 0 || K <= 0 || block_size <= 0) return 0;
   const int64_t kb = (K + block_size - 1) / block_size;
-  auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
-  // qa [M, kb*bs] int8, sa [M, kb] float, per-block code sums [M, kb] int32.
-  return (size_t)(up(M * kb * block_size) + up(M * kb * 4) + up(M * kb * 4));
+  return qmm::ws_total_bytes(M, kb, block_size);
+}
+
+static int check_workspace(const char* fn, const MatArgs& a, void* workspace, size_t bytes) {
+  const size_t need = qmm::ws_total_bytes(a.M, a.kb, a.block_size);
+  if (workspace == nullptr || bytes < need)
+    return fail(QMM_ERR_WORKSPACE,
+                "%s: the workspace holds %zu bytes at %p, %zu are needed. Why: CompInt8 stores the "
+                "int8 activations and their per-block scales there (the library never allocates). "
+                "How to fix: pass qmm_compint8_workspace_size(M, K, block_size) bytes of device "
+                "memory.", fn, bytes, workspace, need);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(QMM_ERR_WORKSPACE, "%s: the workspace must be 256-byte aligned. How to fix: "
+                "pass the start of a fresh allocation.", fn);
+  return QMM_OK;
 }
 
 int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout,
@@ -186,10 +198,15 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
                            s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
                            accuracy_level, &a);
   if (st != QMM_OK) return st;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
-  return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8 is not built yet.");
+  if (M == 0) return QMM_OK;
+  st = check_workspace("qmm_gemm_compint8", a, workspace, workspace_bytes);
+  if (st != QMM_OK) return st;
+  a.stream = (hipStream_t)stream;
+  int8_t* qa = (int8_t*)workspace;
+  float* sa = (float*)((char*)workspace + qmm::ws_qa_bytes(a.M, a.kb, a.block_size));
+  hipError_t e = qmm::launch_quantize_a(a, qa, sa);
+  if (e == hipSuccess) e = qmm::launch_compint8(a, qa, sa);
+  return hip_status(e, "qmm_gemm_compint8");
 }
 
 int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,
@@ -206,24 +223,59 @@ int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const flo
 int qmm_debug_unpack(const uint8_t* B, int b_layout, const void* scales, int s_dtype,
                      const uint8_t* zero_points, int64_t K, int64_t N, int block_size, int bits,
                      uint8_t* codes, uint8_t* zps, float* w, void* stream) {
-  (void)B; (void)b_layout; (void)scales; (void)s_dtype; (void)zero_points; (void)K; (void)N;
-  (void)block_size; (void)bits; (void)codes; (void)zps; (void)w; (void)stream;
-  return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_unpack is not built yet.");
+  MatArgs a;
+  // Validate as a matmul with a dummy activation/output (never touched).
+  const void* dummy = B;
+  if (w != nullptr && scales == nullptr)
+    return fail(QMM_ERR_INVALID_ARG, "qmm_debug_unpack: scales are required to write w.");
+  int st = validate_matmul("qmm_debug_unpack", Route::Float, dummy, QMM_BF16, B, b_layout,
+                           scales ? scales : dummy, scales ? s_dtype : QMM_BF16, zero_points,
+                           nullptr, (void*)dummy, 0, K, N, block_size, bits, 0, &a);
+  if (st != QMM_OK) return st;
+  a.scales = scales;
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_unpack(a, codes, zps, w), "qmm_debug_unpack");
 }
 
 int qmm_debug_quantize_a(const void* A, int a_dtype, int64_t M, int64_t K, int block_size,
                          int8_t* qa, float* sa, void* stream) {
-  (void)A; (void)a_dtype; (void)M; (void)K; (void)block_size; (void)qa; (void)sa; (void)stream;
-  return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_quantize_a is not built yet.");
+  if (qa == nullptr || sa == nullptr)
+    return fail(QMM_ERR_INVALID_ARG, "qmm_debug_quantize_a: qa and sa must be non-null.");
+  MatArgs a;
+  static const uint8_t* const kAligned = reinterpret_cast<const uint8_t*>(256);
+  int st = validate_matmul("qmm_debug_quantize_a", Route::CompInt8, A, a_dtype, kAligned, 0,
+                           kAligned, QMM_F32, nullptr, nullptr, (void*)qa, M, K, 1, block_size,
+                           4, 4, &a);
+  if (st != QMM_OK) return st;
+  if (M == 0) return QMM_OK;
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_quantize_a(a, qa, sa), "qmm_debug_quantize_a");
 }
 
 int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, int b_layout,
                                   const uint8_t* zero_points, int64_t M, int64_t K, int64_t N,
                                   int block_size, int bits, int32_t* dots, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  (void)A; (void)a_dtype; (void)B; (void)b_layout; (void)zero_points; (void)M; (void)K; (void)N;
-  (void)block_size; (void)bits; (void)dots; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_compint8_block_dots is not built yet.");
+  if (dots == nullptr)
+    return fail(QMM_ERR_INVALID_ARG, "qmm_debug_compint8_block_dots: dots must be non-null.");
+  MatArgs a;
+  int st = validate_matmul("qmm_debug_compint8_block_dots", Route::CompInt8, A, a_dtype, B,
+                           b_layout, B, QMM_F32, zero_points, nullptr, (void*)dots, M, K, N,
+                           block_size, bits, 4, &a);
+  if (st != QMM_OK) return st;
+  if (M == 0) return QMM_OK;
+  st = check_workspace("qmm_debug_compint8_block_dots", a, workspace, workspace_bytes);
+  if (st != QMM_OK) return st;
+  a.scales = nullptr;   // the block dots need no scales
+  a.Y = nullptr;
+  a.stream = (hipStream_t)stream;
+  int8_t* qa = (int8_t*)workspace;
+  float* sa = (float*)((char*)workspace + qmm::ws_qa_bytes(a.M, a.kb, a.block_size));
+  hipError_t e = qmm::launch_quantize_a(a, qa, sa);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(dots, 0, (size_t)(a.M * a.N * a.kb) * sizeof(int32_t), a.stream);
+  if (e == hipSuccess) e = qmm::launch_compint8_dots(a, qa, sa, dots);
+  return hip_status(e, "qmm_debug_compint8_block_dots");
 }
 
 }  // extern "C"

@@ -28,4 +28,22 @@ using GemvArgs = MatArgs;
 
 hipError_t launch_gemv(const MatArgs& a);
 
+// CompInt8: quantize A into qa [M, kb*bs] int8 and sa [M, kb] float, then
+// the int8 block-dot matmul (or, for the test export, the exact int32 block
+// dots [M, N, kb] accumulated into a zeroed buffer).
+hipError_t launch_quantize_a(const MatArgs& a, int8_t* qa, float* sa);
+hipError_t launch_compint8(const MatArgs& a, const int8_t* qa, const float* sa);
+hipError_t launch_compint8_dots(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots);
+
+// Codec export: codes [N, K], zero points [N, kb], dequantized weight [N, K].
+hipError_t launch_unpack(const MatArgs& a, uint8_t* codes, uint8_t* zps, float* w);
+
+// Workspace layout of CompInt8: qa [M, kb*bs] int8, then sa [M, kb] float,
+// each region 256-byte aligned.
+inline size_t ws_align(size_t v) { return (v + 255) / 256 * 256; }
+inline size_t ws_qa_bytes(int64_t M, int64_t kb, int64_t bs) { return ws_align((size_t)(M * kb * bs)); }
+inline size_t ws_total_bytes(int64_t M, int64_t kb, int64_t bs) {
+  return ws_qa_bytes(M, kb, bs) + ws_align((size_t)(M * kb * 4));
+}
+
 }  // namespace qmm

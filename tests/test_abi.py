@@ -78,9 +78,13 @@ def test_compint8_requires_level_4_and_workspace_size(qmm):
     st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096, 4096, 128,
                                    4, 0, FAKE, 1 << 20, None)
     assert st == -1 and "accuracy_level must be 4" in qmm.qmm_last_error()
+    # int8 activations [M, kb*bs] + float scales [M, kb], regions 256-byte aligned.
     ws = qmm.qmm_compint8_workspace_size(16, 4096, 128)
-    assert ws >= 16 * 4096 + 2 * 4 * 16 * 32 and ws % 256 == 0
+    assert ws >= 16 * 4096 + 4 * 16 * 32 and ws % 256 == 0
     assert qmm.qmm_compint8_workspace_size(1, 100, 64) >= 128 + 4 * 2
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096, 4096, 128,
+                                   4, 4, FAKE, 100, None)
+    assert st == -3 and "workspace" in qmm.qmm_last_error()
 
 
 def test_gemm_with_m_zero_is_a_noop(qmm):
