@@ -152,10 +152,81 @@ def main():
         },
     }
 
+    out["prefill_gemm"] = bench_prefill(qmm, dev, stream, args)
+    out["compint8"] = bench_compint8(qmm, dev, stream, args)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def _time_launches(fn, n, stream):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def bench_prefill(qmm, dev, stream, args):
+    """Prefill GEMM M=2048, K=4096, N=14336 (4-bit asymmetric bs 32, bf16)."""
+    from block_quantized_weight_matmulnbits_amd.workloads import prefill_gemm
+    c = prefill_gemm().to(dev)
+    Y = torch.empty(c.M, c.N, dtype=torch.bfloat16, device=dev)
+
+    def run(_):
+        qmm.qmm_gemm(c.A, c.B, c.scales, c.zero_points, None, Y, c.M, c.K, c.N, c.block_size,
+                      c.bits, 0, stream)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    ms = _time_launches(run, max(5, args.steps // 20), stream)
+    flop = 2.0 * c.M * c.N * c.K
+    tflops = flop / (ms * 1e-3) / 1e12
+    return {"workload": "prefill GEMM M=2048 K=4096 N=14336, bf16 activations, 4-bit asymmetric "
+                        "block 32, bf16 output, fp32 accumulate",
+            "ms": round(ms, 4), "tflops": round(tflops, 2), "unit": "TFLOP/s",
+            "bound": "mfma", "peak": BF16_PEAK_TFLOPS,
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop}
+
+
+def bench_compint8(qmm, dev, stream, args):
+    """Batched-decode CompInt8, K=4096 N=14336, M in {1,4,16} x 3 weight formats;
+    weights rotate through copies so each launch streams them from HBM."""
+    from block_quantized_weight_matmulnbits_amd.workloads import COMPINT8_VARIANTS, compint8_case
+    res = {}
+    for bits, bs, asym in COMPINT8_VARIANTS:
+        base = compint8_case(1, bits, bs, asym).to(dev)
+        nbytes = base.weight_bytes()
+        copies = [(base.B, base.scales, base.zero_points)] + [
+            (base.B.clone(), base.scales.clone(),
+             None if base.zero_points is None else base.zero_points.clone())
+            for _ in range(max(1, -(-POOL_BYTES // nbytes)) - 1)]
+        for M in (1, 4, 16):
+            c = compint8_case(M, bits, bs, asym)
+            A = c.A.to(dev)
+            Y = torch.empty(M, c.N, dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(qmm.qmm_compint8_workspace_size(M, c.K, bs), dtype=torch.uint8,
+                             device=dev)
+
+            def run(i):
+                B, sc, zp = copies[i % len(copies)]
+                qmm.qmm_gemm_compint8(A, B, sc, zp, None, Y, M, c.K, c.N, bs, bits, ws, 4, stream)
+
+            for i in range(3):
+                run(i)
+            torch.cuda.synchronize()
+            ms = _time_launches(run, max(10, args.steps // 4), stream)
+            byts = nbytes + A.numel() * 2 + M * c.N * 2
+            res[f"b{bits}_bs{bs}_M{M}"] = {"us": round(ms * 1e3, 2),
+                                          "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                                          "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def cpu_baseline(cases, seconds):

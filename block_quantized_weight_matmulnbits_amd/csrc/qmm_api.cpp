@@ -165,7 +165,7 @@ int qmm_gemm(const void* A, int a_dtype, const uint8_t* B, int b_layout, const v
   a.stream = (hipStream_t)stream;
   if (M == 0) return QMM_OK;
   if (M == 1) return hip_status(qmm::launch_gemv(a), "qmm_gemm");
-  return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm: M > 1 is not built yet.");
+  return hip_status(qmm::launch_gemm(a), "qmm_gemm");
 }
 
 size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size) {

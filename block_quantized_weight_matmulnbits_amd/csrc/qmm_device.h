@@ -39,6 +39,13 @@ template <> struct dt<DT_BF16> {
   }
 };
 
+// Widen the raw 16-bit pattern of an f16 or bf16 value to fp32 (exact).
+template <int DT>
+__device__ __forceinline__ float bits16_to_f32(uint16_t h) {
+  if constexpr (DT == DT_BF16) return __uint_as_float((uint32_t)h << 16);
+  else return (float)__builtin_bit_cast(_Float16, h);
+}
+
 __device__ __forceinline__ half2_t as_half2(uint32_t u) {
   return __builtin_bit_cast(half2_t, u);
 }

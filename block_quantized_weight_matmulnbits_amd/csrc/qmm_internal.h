@@ -28,6 +28,10 @@ using GemvArgs = MatArgs;
 
 hipError_t launch_gemv(const MatArgs& a);
 
+// Batched / prefill matmul (M > 1): bf16/f16 MFMA kernel, or the fp32
+// multi-row fallback.
+hipError_t launch_gemm(const MatArgs& a);
+
 // CompInt8: quantize A into qa [M, kb*bs] int8 and sa [M, kb] float, then
 // the int8 block-dot matmul (or, for the test export, the exact int32 block
 // dots [M, N, kb] accumulated into a zeroed buffer).
