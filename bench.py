@@ -154,6 +154,7 @@ def main():
 
     out["prefill_gemm"] = bench_prefill(qmm, dev, stream, args)
     out["compint8"] = bench_compint8(qmm, dev, stream, args)
+    out["conv_int8"] = bench_conv(qmm, dev, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
@@ -227,6 +228,28 @@ def bench_compint8(qmm, dev, stream, args):
                                           "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
                                           "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return res
+
+
+def bench_conv(qmm, dev, stream, args):
+    """int8 conv 1x56x56x64, 3x3, stride 1, pad 1, 64 output channels."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_conv_case
+    c = make_conv_case().to(dev)
+    Y = torch.empty(1, 56, 56, 64, dtype=torch.int8, device=dev)
+
+    def run(_):
+        qmm.qconv_int8(c.X, c.W, c.bias, c.w_scale, c.in_scale, c.out_scale, c.in_zp, c.out_zp,
+                       c.clamp_min, c.clamp_max, c.stride, c.pad, Y, stream)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    ms = _time_launches(run, max(20, args.steps), stream)
+    ops = 2 * 56 * 56 * 64 * 3 * 3 * 64
+    byts = c.X.numel() + c.W.numel() + 4 * 64 + 4 * 64 + Y.numel()
+    return {"workload": "int8 conv NHWC 1x56x56x64, 3x3, stride 1, pad 1, Co=64, requant to int8",
+            "us": round(ms * 1e3, 2), "int8_tops": round(ops / (ms * 1e-3) / 1e12, 3),
+            "GBps": round(byts / (ms * 1e-3) / 1e9, 2), "int_ops_per_launch": ops,
+            "bytes_per_launch": byts}
 
 
 def cpu_baseline(cases, seconds):

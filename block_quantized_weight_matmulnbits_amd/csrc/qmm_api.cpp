@@ -213,11 +213,47 @@ int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const flo
                float in_scale, float out_scale, int in_zp, int out_zp, int clamp_min,
                int clamp_max, int Nb, int H, int W, int C, int Co, int KH, int KW, int stride_h,
                int stride_w, int pad_h, int pad_w, int8_t* Y, void* stream) {
-  (void)X; (void)Wt; (void)bias; (void)w_scale; (void)in_scale; (void)out_scale; (void)in_zp;
-  (void)out_zp; (void)clamp_min; (void)clamp_max; (void)Nb; (void)H; (void)W; (void)C; (void)Co;
-  (void)KH; (void)KW; (void)stride_h; (void)stride_w; (void)pad_h; (void)pad_w; (void)Y;
-  (void)stream;
-  return fail(QMM_ERR_UNSUPPORTED, "qconv_int8 is not built yet.");
+  const char* fn = "qconv_int8";
+  if (X == nullptr || Wt == nullptr || w_scale == nullptr || Y == nullptr)
+    return fail(QMM_ERR_INVALID_ARG, "%s: X, Wt, w_scale and Y must be non-null device "
+                "pointers (bias may be NULL).", fn);
+  if (Nb < 1 || H < 1 || W < 1 || C < 1 || Co < 1 || KH < 1 || KW < 1 || stride_h < 1 ||
+      stride_w < 1 || pad_h < 0 || pad_w < 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: sizes, kernel and strides must be >= 1 and pads >= 0 "
+                "(got Nb=%d H=%d W=%d C=%d Co=%d KH=%d KW=%d stride=%d,%d pad=%d,%d).", fn, Nb, H,
+                W, C, Co, KH, KW, stride_h, stride_w, pad_h, pad_w);
+  if (H + 2 * pad_h < KH || W + 2 * pad_w < KW)
+    return fail(QMM_ERR_INVALID_ARG, "%s: the padded input (%dx%d) is smaller than the kernel "
+                "(%dx%d), so there is no output pixel.", fn, H + 2 * pad_h, W + 2 * pad_w, KH, KW);
+  if (C % 4 != 0)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: C=%d must be a multiple of 4. Why: the kernel reads "
+                "input channels and weight rows as 4-byte words. How to fix: pad the channels "
+                "with zero weights.", fn, C);
+  if (((uintptr_t)X & 3) || ((uintptr_t)Wt & 3))
+    return fail(QMM_ERR_INVALID_ARG, "%s: X and Wt must be 4-byte aligned.", fn);
+  if (in_zp < -128 || in_zp > 127 || clamp_min < -128 || clamp_max > 127 || clamp_min > clamp_max)
+    return fail(QMM_ERR_INVALID_ARG, "%s: in_zp must be an int8 value and -128 <= clamp_min <= "
+                "clamp_max <= 127 (got in_zp=%d clamp=[%d,%d]). Why: the output is int8; a ReLU "
+                "is clamp_min = out_zp.", fn, in_zp, clamp_min, clamp_max);
+  if (!(out_scale != 0.0f) || !(in_scale == in_scale))
+    return fail(QMM_ERR_INVALID_ARG, "%s: out_scale must be nonzero and the scales must not be "
+                "NaN. Why: the requantization multiplier is (in_scale * w_scale) / out_scale.", fn);
+  const int64_t K = (int64_t)KH * KW * C;
+  const int64_t OH = (H + 2 * pad_h - KH) / stride_h + 1, OW = (W + 2 * pad_w - KW) / stride_w + 1;
+  if (K * 128 * 128 >= (int64_t)1 << 31 || (int64_t)Nb * OH * OW * Co >= (int64_t)1 << 31 ||
+      (int64_t)Nb * H * W * C >= (int64_t)1 << 31)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: the reduction (KH*KW*C = %lld) or a tensor is too large "
+                "for the exact int32 accumulator / 32-bit indices. How to fix: split the "
+                "convolution.", fn, (long long)K);
+  qmm::ConvArgs c;
+  c.X = X; c.Wt = Wt; c.bias = bias; c.w_scale = w_scale;
+  c.in_scale = in_scale; c.out_scale = out_scale; c.in_zp = in_zp; c.out_zp = out_zp;
+  c.clamp_min = clamp_min; c.clamp_max = clamp_max;
+  c.Nb = Nb; c.H = H; c.W = W; c.C = C; c.Co = Co; c.KH = KH; c.KW = KW;
+  c.stride_h = stride_h; c.stride_w = stride_w; c.pad_h = pad_h; c.pad_w = pad_w;
+  c.Y = Y;
+  c.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_conv_int8(c), fn);
 }
 
 int qmm_debug_unpack(const uint8_t* B, int b_layout, const void* scales, int s_dtype,

@@ -39,6 +39,21 @@ hipError_t launch_quantize_a(const MatArgs& a, int8_t* qa, float* sa);
 hipError_t launch_compint8(const MatArgs& a, const int8_t* qa, const float* sa);
 hipError_t launch_compint8_dots(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots);
 
+// int8 convolution (validated NHWC / OHWI problem).
+struct ConvArgs {
+  const int8_t* X = nullptr;
+  const int8_t* Wt = nullptr;
+  const int32_t* bias = nullptr;
+  const float* w_scale = nullptr;
+  float in_scale = 1.f, out_scale = 1.f;
+  int in_zp = 0, out_zp = 0, clamp_min = -128, clamp_max = 127;
+  int Nb = 0, H = 0, W = 0, C = 0, Co = 0, KH = 0, KW = 0;
+  int stride_h = 1, stride_w = 1, pad_h = 0, pad_w = 0;
+  int8_t* Y = nullptr;
+  hipStream_t stream = nullptr;
+};
+hipError_t launch_conv_int8(const ConvArgs& c);
+
 // Codec export: codes [N, K], zero points [N, kb], dequantized weight [N, K].
 hipError_t launch_unpack(const MatArgs& a, uint8_t* codes, uint8_t* zps, float* w);
 

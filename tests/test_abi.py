@@ -90,3 +90,30 @@ def test_compint8_requires_level_4_and_workspace_size(qmm):
 def test_gemm_with_m_zero_is_a_noop(qmm):
     st = qmm.lib.qmm_gemm(None, 2, FAKE, 0, FAKE, 2, None, None, None, 0, 64, 64, 32, 4, 0, None)
     assert st == 0
+
+
+def conv(qmm, **kw):
+    a = dict(X=FAKE, W=FAKE, bias=None, ws=FAKE, in_scale=0.02, out_scale=0.05, in_zp=0, out_zp=0,
+             lo=-128, hi=127, Nb=1, H=56, Wd=56, C=64, Co=64, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1,
+             Y=FAKE)
+    a.update(kw)
+    return qmm.lib.qconv_int8(a["X"], a["W"], a["bias"], a["ws"], a["in_scale"], a["out_scale"],
+                              a["in_zp"], a["out_zp"], a["lo"], a["hi"], a["Nb"], a["H"], a["Wd"],
+                              a["C"], a["Co"], a["KH"], a["KW"], a["sh"], a["sw"], a["ph"], a["pw"],
+                              a["Y"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(C=6), -2, "multiple of 4"),
+    (dict(X=None), -1, "non-null"),
+    (dict(sh=0), -1, "strides must be >= 1"),
+    (dict(KH=9, ph=0, H=4), -1, "smaller than the kernel"),
+    (dict(lo=10, hi=5), -1, "clamp_min"),
+    (dict(in_zp=300), -1, "in_zp"),
+    (dict(out_scale=0.0), -1, "out_scale"),
+    (dict(X=FAKE + 2), -1, "4-byte aligned"),
+    (dict(C=1 << 20), -2, "too large"),
+])
+def test_conv_rejects_bad_arguments(qmm, kw, code, needle):
+    assert conv(qmm, **kw) == code
+    assert needle in qmm.qmm_last_error(), qmm.qmm_last_error()
