@@ -28,12 +28,14 @@
 namespace qmm {
 
 constexpr int GEMM_THREADS = 256;
-constexpr int GBM = 256, GBN = 256, GBK = 32;
-constexpr int LDS_ROW = GBK + 8;             // padded row, in 16-bit elements
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int LDS_ROW = GBK + 8;             // padded LDS row, in 16-bit elements
+constexpr int STAGE = GBM * LDS_ROW;         // one operand tile, in 16-bit elements
 constexpr int BUF_WORD3 = 0x00020000;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int XDT> struct MfmaOp;
 template <> struct MfmaOp<DT_BF16> {
@@ -44,6 +46,11 @@ template <> struct MfmaOp<DT_BF16> {
   static __device__ __forceinline__ uint16_t round(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
   }
+  // Two values rounded to nearest even and packed (v_cvt_pk_bf16_f32).
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
 };
 template <> struct MfmaOp<DT_F16> {
   using V = f16x8;
@@ -53,42 +60,163 @@ template <> struct MfmaOp<DT_F16> {
   static __device__ __forceinline__ uint16_t round(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
   }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    const half2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
 };
+
+// Codes of one 32-bit word as fp32 values, in element order.
+template <int BITS>
+__device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
+  if constexpr (BITS == 8) {
+    q[0] = (float)(w & 0xFF); q[1] = (float)((w >> 8) & 0xFF);
+    q[2] = (float)((w >> 16) & 0xFF); q[3] = (float)(w >> 24);
+  } else if constexpr (BITS == 4) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      q[2 * j] = (float)((lo >> (8 * j)) & 0xFF);
+      q[2 * j + 1] = (float)((hi >> (8 * j)) & 0xFF);
+    }
+  } else {
+    const uint32_t f[4] = {w & 0x03030303u, (w >> 2) & 0x03030303u, (w >> 4) & 0x03030303u,
+                           (w >> 6) & 0x03030303u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[4 * j + i] = (float)((f[i] >> (8 * j)) & 0xFF);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // MFMA kernel.  Requirements checked by the launcher: K % 8 == 0 and A 16-byte
 // aligned (A rows are read as 16-byte chunks of 8 activations).
+// Per K-step of GBK = 64: A tile 256 x 64 (8 chunks of 16 B per thread) and
+// this thread's B column (64 codes) are prefetched into registers one step
+// ahead; after the step's MFMAs they are written (B dequantized) to the other
+// LDS buffer; one barrier per step.
 // ---------------------------------------------------------------------------
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
-    int log2_bs, int log2_blob, int zp_row_bytes, int tiles_n) {
+    int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m) {
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int P = 32 / BITS;                 // codes per 32-bit word
   constexpr int WPS = GBK / P;                 // code words per column per K-step
-  __shared__ __attribute__((aligned(16))) uint16_t As[GBM * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[GBN * LDS_ROW];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_g[];
+  uint16_t* As = lds_g;                        // [2][GBM][LDS_ROW]
+  uint16_t* Bs = lds_g + 2 * STAGE;            // [2][GBN][LDS_ROW]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
+  // Consecutive workgroups take consecutive M tiles of one N tile: with the
+  // round-robin dispatch over the 8 XCDs, each XCD keeps re-using the same A
+  // rows in its L2 while the B columns stream.
+  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
   const int m0 = tile_m * GBM, n0 = tile_n * GBN;
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
 
-  // Whole-matrix descriptors; rows past M read zeros through the extent.
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)A, 0, (int)std::min<int64_t>((int64_t)M * K * 2, 0x7FFFFFFF), BUF_WORD3);
-  const int64_t row_bytes = (int64_t)kb << log2_blob;
-  // This thread's dequantization column.
+  // Whole-matrix descriptors (wave-uniform: a lane-varying descriptor would
+  // make the compiler loop over the lanes for every load).  The launcher
+  // guarantees every byte offset below fits in 31 bits; this thread's column
+  // is addressed by offset, and a column past N gets an offset past the
+  // extent, which reads zeros.
+  const int row_bytes = kb << log2_blob;
   const int ncol = n0 + tid;
   const bool ncol_ok = ncol < N;
-  const int nc = ncol_ok ? ncol : N - 1;
   const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B + (int64_t)nc * row_bytes), 0, ncol_ok ? (int)row_bytes : 0, BUF_WORD3);
+      (void*)B, 0, N * row_bytes, BUF_WORD3);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)scales, 0, N * kb * (int)sizeof(ST), BUF_WORD3);
+  const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)zp, 0, HAS_ZP ? N * zp_row_bytes : 0, BUF_WORD3);
+  constexpr int OOB = 0x7FFFFFF0;
+  const int col_code0 = ncol_ok ? ncol * row_bytes : OOB;
+  const int col_sc0 = ncol_ok ? ncol * kb : OOB / 4;
+  const int col_zp0 = ncol_ok ? ncol * zp_row_bytes : OOB;
+
+  // Prefetch registers for one K-step: A chunks, this column's codes, and the
+  // scales / zero-point bytes of the (at most 4, block_size >= 16) blocks the
+  // step touches, clamped to the last block.
+  u32x4 av[8];
+  uint32_t cw[WPS];
+  ST scr[4];
+  uint32_t zbr[4];
+  auto load_step = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + i * GEMM_THREADS;
+      const int r = c >> 3, kc = (c & 7) * 8;
+      const int row = m0 + r, k = k0 + kc;
+      const bool ok = row < M && k < K;    // K % 8 == 0: a chunk is all in or all out
+      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (row * K + k) * 2 : 0x7FFFFFF0, 0, 0);
+    }
+    // Codes past the row's last block (k0 + 64 > kb * bs) would come from the
+    // next row; they meet zero activations (k >= K), so they add nothing.
+    const int byte0 = col_code0 + ((k0 * BITS) >> 3);
+#pragma unroll
+    for (int w = 0; w < WPS; w += 4) {
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rbc, byte0 + 4 * w, 0, 0);
+      cw[w] = t.x; cw[w + 1] = t.y; cw[w + 2] = t.z; cw[w + 3] = t.w;
+    }
+    const int blk0 = k0 >> log2_bs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = min(blk0 + i, kb - 1);
+      if constexpr (sizeof(ST) == 4)
+        scr[i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, (col_sc0 + b) * 4, 0, 0));
+      else
+        scr[i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, (col_sc0 + b) * 2, 0, 0));
+      if constexpr (HAS_ZP)
+        zbr[i] = __builtin_amdgcn_raw_buffer_load_b8(rzp, col_zp0 + ((b * BITS) >> 3), 0, 0);
+    }
+  };
+  // Write the prefetched step into LDS buffer `buf`, dequantizing B.
+  auto store_step = [&](int k0, int buf) {
+    uint16_t* as = As + buf * STAGE;
+    uint16_t* bs = Bs + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + i * GEMM_THREADS;
+      const int r = c >> 3, kc = (c & 7) * 8;
+      *reinterpret_cast<u32x4*>(&as[r * LDS_ROW + kc]) = av[i];
+    }
+    uint32_t pk[GBK / 2];
+    const int blk0 = k0 >> log2_bs;
+#pragma unroll
+    for (int w = 0; w < WPS; ++w) {
+      const int kw = k0 + w * P;
+      // Block of this word relative to the step's first block (0..3).
+      const int rel = min(kw >> log2_bs, kb - 1) - min(blk0, kb - 1);
+      const ST sraw = rel == 0 ? scr[0] : rel == 1 ? scr[1] : rel == 2 ? scr[2] : scr[3];
+      const float s = dt<SDT>::to_f32(sraw);
+      uint32_t z = 1u << (BITS - 1);
+      if constexpr (HAS_ZP) {
+        constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+        const uint32_t zb = rel == 0 ? zbr[0] : rel == 1 ? zbr[1] : rel == 2 ? zbr[2] : zbr[3];
+        const int blk = min(kw >> log2_bs, kb - 1);
+        z = (zb >> ((blk * BITS) & 7)) & zm;
+      }
+      const float zs = (float)z * s;
+      float q[P];
+      word_codes_f32<BITS>(cw[w], q);
+      // (q - z) * s = q * s - z * s: both products exact, the difference
+      // exact, one rounding to the activation dtype.
+#pragma unroll
+      for (int j = 0; j < P; j += 2) pk[(w * P + j) / 2] = Op::pack(fmaf(q[j], s, -zs), fmaf(q[j + 1], s, -zs));
+    }
+#pragma unroll
+    for (int j = 0; j < GBK / 8; ++j)
+      *reinterpret_cast<u32x4*>(&bs[tid * LDS_ROW + 8 * j]) =
+          u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
+  };
 
   f32x4 acc[8][8];
 #pragma unroll
@@ -96,85 +224,37 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < K; k0 += GBK) {
-    // ---- A tile: 256 rows x 32 activations = 1024 chunks of 8; 4 per thread.
-    u32x4 av[4];
+  const int nsteps = (K + GBK - 1) / GBK;
+  load_step(0);
+  store_step(0, 0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nsteps;
+    if (more) load_step((s + 1) * GBK);
+    const uint16_t* as = As + buf * STAGE;
+    const uint16_t* bs = Bs + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * GEMM_THREADS;
-      const int r = c >> 2, kc = (c & 3) * 8;
-      const int row = m0 + r, k = k0 + kc;
-      const bool ok = row < M && k < K;      // K % 8 == 0: a chunk is all in or all out
-      const int off = ok ? (row * K + k) * 2 : 0x7FFFFFF0;
-      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-    }
-    // ---- B codes of this thread's column for k in [k0, k0 + 32).
-    uint32_t cw[WPS];
-    const int byte0 = (k0 * BITS) >> 3;
+    for (int kk = 0; kk < GBK; kk += 32) {
+      typename Op::V bf[8];
 #pragma unroll
-    for (int w = 0; w < WPS; ++w) cw[w] = __builtin_amdgcn_raw_buffer_load_b32(rbc, byte0 + 4 * w, 0, 0);
-
-    __syncthreads();   // previous K-step's fragment reads are done
+      for (int j = 0; j < 8; ++j)
+        bf[j] = __builtin_bit_cast(typename Op::V,
+                                   *reinterpret_cast<const u32x4*>(&bs[(wn + j * 16 + fr) * LDS_ROW + kk + fk]));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * GEMM_THREADS;
-      const int r = c >> 2, kc = (c & 3) * 8;
-      *reinterpret_cast<u32x4*>(&As[r * LDS_ROW + kc]) = av[i];
-    }
-    // Dequantize: each word lies inside one block.
-    uint16_t wq[GBK];
+      for (int i = 0; i < 8; ++i) {
+        const typename Op::V af = __builtin_bit_cast(
+            typename Op::V, *reinterpret_cast<const u32x4*>(&as[(wm + i * 16 + fr) * LDS_ROW + kk + fk]));
 #pragma unroll
-    for (int w = 0; w < WPS; ++w) {
-      const int kw = k0 + w * P;
-      const int blk = min(kw >> log2_bs, kb - 1);
-      float s = 0.0f;
-      uint32_t z = 1u << (BITS - 1);
-      if (ncol_ok) {
-        s = dt<SDT>::to_f32(scales[(int64_t)ncol * kb + blk]);
-        if constexpr (HAS_ZP) {
-          constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
-          const int zbit = blk * BITS;
-          z = ((uint32_t)zp[(int64_t)ncol * zp_row_bytes + (zbit >> 3)] >> (zbit & 7)) & zm;
-        }
-      }
-      const float zs = (float)z * s;
-#pragma unroll
-      for (int j = 0; j < P; ++j) {
-        constexpr uint32_t cm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
-        const float q = (float)((cw[w] >> (j * BITS)) & cm);
-        // (q - z) * s as q * s - z * s: both products exact, one rounding.
-        wq[w * P + j] = Op::round(fmaf(q, s, -zs));
+        for (int j = 0; j < 8; ++j) acc[i][j] = Op::run(af, bf[j], acc[i][j]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < GBK / 8; ++j) {
-      u32x4 t;
-      t.x = wq[8 * j + 0] | ((uint32_t)wq[8 * j + 1] << 16);
-      t.y = wq[8 * j + 2] | ((uint32_t)wq[8 * j + 3] << 16);
-      t.z = wq[8 * j + 4] | ((uint32_t)wq[8 * j + 5] << 16);
-      t.w = wq[8 * j + 6] | ((uint32_t)wq[8 * j + 7] << 16);
-      *reinterpret_cast<u32x4*>(&Bs[tid * LDS_ROW + 8 * j]) = t;
-    }
+    if (more) store_step((s + 1) * GBK, buf ^ 1);
     __syncthreads();
-
-    // ---- MFMA: lane l takes row/column (l % 16) and activations
-    // [8 * (l / 16), +8) of the 32-wide K-step.
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-    typename Op::V bf[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bf[j] = __builtin_bit_cast(typename Op::V,
-                                 *reinterpret_cast<const u32x4*>(&Bs[(wn + j * 16 + fr) * LDS_ROW + fk]));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const typename Op::V af = __builtin_bit_cast(
-          typename Op::V, *reinterpret_cast<const u32x4*>(&As[(wm + i * 16 + fr) * LDS_ROW + fk]));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = Op::run(af, bf[j], acc[i][j]);
-    }
   }
 
-  // ---- Epilogue: lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16 of
+  // Epilogue: lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16 of
   // each 16 x 16 tile.
   const int cc = lane & 15, rr = (lane >> 4) * 4;
 #pragma unroll
@@ -301,16 +381,27 @@ static hipError_t launch_rows(const MatArgs& a) {
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 static hipError_t launch_gemm_t(const MatArgs& a) {
   using ST = typename dt<SDT>::T;
+  // Every buffer offset of the MFMA kernel must fit in 31 bits.
   const bool mfma_ok = XDT != DT_F32 && a.M > 16 && (a.K % 8) == 0 &&
-                       ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 < 0x7FFFFFF0LL;
+                       ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 < 0x7FFFFF00LL &&
+                       a.N * a.kb * a.blob + 64 < 0x7FFFFF00LL &&
+                       a.N * a.kb * (int64_t)sizeof(ST) < 0x7FFFFF00LL;
   if constexpr (XDT != DT_F32) {
     if (mfma_ok) {
       const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
+      constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);   // double-buffered A and B
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
       hipLaunchKernelGGL((gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP>), dim3(tiles_m * tiles_n),
-                         dim3(GEMM_THREADS), 0, a.stream, (const uint16_t*)a.A, a.B,
+                         dim3(GEMM_THREADS), lds, a.stream, (const uint16_t*)a.A, a.B,
                          (const ST*)a.scales, a.zp, (const uint16_t*)a.bias, (uint16_t*)a.Y,
                          (int)a.M, (int)a.K, (int)a.N, (int)a.kb, ilog2i(a.block_size),
-                         ilog2i(a.blob), (int)a.zp_row_bytes, tiles_n);
+                         ilog2i(a.blob), (int)a.zp_row_bytes, tiles_m);
       return hipGetLastError();
     }
   }
