@@ -21,6 +21,7 @@
 // LDS as fp32 and accumulates exact (code - zp) * x products per block in fp32
 // before scaling.
 #include <algorithm>
+#include <type_traits>
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
@@ -90,26 +91,44 @@ __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel.  Requirements checked by the launcher: K % 8 == 0 and A 16-byte
-// aligned (A rows are read as 16-byte chunks of 8 activations).
-// Per K-step of GBK = 64: A tile 256 x 64 (8 chunks of 16 B per thread) and
-// this thread's B column (64 codes) are prefetched into registers one step
-// ahead; after the step's MFMAs they are written (B dequantized) to the other
-// LDS buffer; one barrier per step.
+// MFMA kernel.  Requirements checked by the launcher: K % 8 == 0, A 16-byte
+// aligned (A rows are read as 16-byte chunks of 8 activations), and every
+// buffer byte offset below 2^31.
+//
+// Tile GBM x BN with BN = 32 * TN (TN = 8: 256 columns, TN = 7: 224 columns,
+// which splits N = 14336 into whole tiles and 2048 x 14336 into exactly two
+// rounds of 256 workgroups).  8 waves, two per SIMD so one wave's waits hide
+// under the other's MFMAs, arranged 4 (M) x 2 (N); each wave owns 64 x 16*TN
+// outputs as 4 x TN v_mfma_f32_16x16x32 tiles.
+// Per K-step of GBK = 64: thread t dequantizes 32 codes of column t % BN
+// (half t / BN of the step); threads t >= 2 * BN only copy A.
+// Pipeline: A chunks are prefetched into registers one step ahead, the codes,
+// scales and zero points two steps ahead (register stage = step parity, fixed
+// at compile time by unrolling the loop by two); after a step's MFMAs the
+// next step is written to the other LDS buffer; one barrier per step.  The
+// loop body has no branch around its loads (loads past the last step use
+// out-of-range offsets or harmless in-range addresses), so the compiler's
+// waits on the load counter stay exact.
 // ---------------------------------------------------------------------------
-template <int BITS, int XDT, int SDT, bool HAS_ZP>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_mfma_kernel(
+constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_TPB = 64 * GEMM_WAVES;
+
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN>
+__global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
     int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m) {
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
+  constexpr int BN = 32 * TN;
   constexpr int P = 32 / BITS;                 // codes per 32-bit word
-  constexpr int WPS = GBK / P;                 // code words per column per K-step
+  constexpr int HK = GBK / 2;                  // codes per thread per K-step
+  constexpr int WPT = HK / P;                  // code words per thread per K-step
+  constexpr int TM = 4;                        // MFMA row tiles per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_g[];
   uint16_t* As = lds_g;                        // [2][GBM][LDS_ROW]
-  uint16_t* Bs = lds_g + 2 * STAGE;            // [2][GBN][LDS_ROW]
+  uint16_t* Bs = lds_g + 2 * STAGE;            // [2][BN][LDS_ROW]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,152 +137,182 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_mfma_kernel(
   // round-robin dispatch over the 8 XCDs, each XCD keeps re-using the same A
   // rows in its L2 while the B columns stream.
   const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
-  const int m0 = tile_m * GBM, n0 = tile_n * GBN;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int m0 = tile_m * GBM, n0 = tile_n * BN;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * (16 * TN);
 
+  constexpr int OOB = 0x7FFFFFF0;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)A, 0, (int)std::min<int64_t>((int64_t)M * K * 2, 0x7FFFFFFF), BUF_WORD3);
+      (void*)A, 0, M * K * 2, BUF_WORD3);
   // Whole-matrix descriptors (wave-uniform: a lane-varying descriptor would
-  // make the compiler loop over the lanes for every load).  The launcher
-  // guarantees every byte offset below fits in 31 bits; this thread's column
-  // is addressed by offset, and a column past N gets an offset past the
-  // extent, which reads zeros.
+  // make the compiler loop over the lanes for every load).  This thread's
+  // column is addressed by offset; a column past N (or a thread with no
+  // column) gets an offset past the extent, which reads zeros.
   const int row_bytes = kb << log2_blob;
-  const int ncol = n0 + tid;
-  const bool ncol_ok = ncol < N;
+  const bool dq = tid < 2 * BN;                // this thread dequantizes
+  const int bcol = tid % BN;
+  const int ncol = n0 + bcol;
+  const int khalf = (tid / BN) * HK;           // which half of the K-step
+  const bool ncol_ok = dq && ncol < N;
   const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)B, 0, N * row_bytes, BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)scales, 0, N * kb * (int)sizeof(ST), BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
       (void*)zp, 0, HAS_ZP ? N * zp_row_bytes : 0, BUF_WORD3);
-  constexpr int OOB = 0x7FFFFFF0;
   const int col_code0 = ncol_ok ? ncol * row_bytes : OOB;
   const int col_sc0 = ncol_ok ? ncol * kb : OOB / 4;
   const int col_zp0 = ncol_ok ? ncol * zp_row_bytes : OOB;
 
-  // Prefetch registers for one K-step: A chunks, this column's codes, and the
-  // scales / zero-point bytes of the (at most 4, block_size >= 16) blocks the
-  // step touches, clamped to the last block.
-  u32x4 av[8];
-  uint32_t cw[WPS];
-  ST scr[4];
-  uint32_t zbr[4];
-  auto load_step = [&](int k0) {
+  // Register stages.
+  u32x4 av[4];                       // A chunks of the next step
+  uint32_t cw[2][WPT];               // codes, two steps
+  ST scr[2][2];                      // scales of the (at most 2) blocks of 32 codes
+  uint32_t zbr[2][2];                // zero-point bytes of those blocks
+
+  auto load_a = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + i * GEMM_THREADS;
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * GEMM_TPB;
       const int r = c >> 3, kc = (c & 7) * 8;
       const int row = m0 + r, k = k0 + kc;
       const bool ok = row < M && k < K;    // K % 8 == 0: a chunk is all in or all out
-      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (row * K + k) * 2 : 0x7FFFFFF0, 0, 0);
-    }
-    // Codes past the row's last block (k0 + 64 > kb * bs) would come from the
-    // next row; they meet zero activations (k >= K), so they add nothing.
-    const int byte0 = col_code0 + ((k0 * BITS) >> 3);
-#pragma unroll
-    for (int w = 0; w < WPS; w += 4) {
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rbc, byte0 + 4 * w, 0, 0);
-      cw[w] = t.x; cw[w + 1] = t.y; cw[w + 2] = t.z; cw[w + 3] = t.w;
-    }
-    const int blk0 = k0 >> log2_bs;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = min(blk0 + i, kb - 1);
-      if constexpr (sizeof(ST) == 4)
-        scr[i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, (col_sc0 + b) * 4, 0, 0));
-      else
-        scr[i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, (col_sc0 + b) * 2, 0, 0));
-      if constexpr (HAS_ZP)
-        zbr[i] = __builtin_amdgcn_raw_buffer_load_b8(rzp, col_zp0 + ((b * BITS) >> 3), 0, 0);
+      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (row * K + k) * 2 : OOB, 0, 0);
     }
   };
-  // Write the prefetched step into LDS buffer `buf`, dequantizing B.
-  auto store_step = [&](int k0, int buf) {
-    uint16_t* as = As + buf * STAGE;
-    uint16_t* bs = Bs + buf * STAGE;
+  // Codes past the row's last block (k0 + 64 > kb * bs) come from the next
+  // row (or read zeros past the matrix); they meet zero activations
+  // (k >= K), so they add nothing.
+  auto load_b = [&](int k0, int st) {
+    const int kt = k0 + khalf;
+    const int byte0 = col_code0 + ((kt * BITS) >> 3);
+    if constexpr (WPT >= 4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + i * GEMM_THREADS;
+      for (int w = 0; w < WPT; w += 4) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rbc, byte0 + 4 * w, 0, 0);
+        cw[st][w] = t.x; cw[st][w + 1] = t.y; cw[st][w + 2] = t.z; cw[st][w + 3] = t.w;
+      }
+    } else {
+      const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbc, byte0, 0, 0);
+      cw[st][0] = t.x; cw[st][1] = t.y;
+    }
+    const int blk0 = kt >> log2_bs;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int b = min(blk0 + i, kb - 1);
+      if constexpr (sizeof(ST) == 4)
+        scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, (col_sc0 + b) * 4, 0, 0));
+      else
+        scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, (col_sc0 + b) * 2, 0, 0));
+      if constexpr (HAS_ZP)
+        zbr[st][i] = __builtin_amdgcn_raw_buffer_load_b8(rzp, col_zp0 + ((b * BITS) >> 3), 0, 0);
+    }
+  };
+  auto store_a = [&](int buf) {
+    uint16_t* as = As + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * GEMM_TPB;
       const int r = c >> 3, kc = (c & 7) * 8;
       *reinterpret_cast<u32x4*>(&as[r * LDS_ROW + kc]) = av[i];
     }
-    uint32_t pk[GBK / 2];
-    const int blk0 = k0 >> log2_bs;
+  };
+  // Dequantize register stage `st` (step starting at k0) into LDS buffer buf.
+  auto store_b = [&](int k0, int st, int buf) {
+    if (!dq) return;
+    uint16_t* bs = Bs + buf * STAGE;
+    const int kt = k0 + khalf;
+    const int blk0 = min(kt >> log2_bs, kb - 1);
+    float sf[2], zs[2];
 #pragma unroll
-    for (int w = 0; w < WPS; ++w) {
-      const int kw = k0 + w * P;
-      // Block of this word relative to the step's first block (0..3).
-      const int rel = min(kw >> log2_bs, kb - 1) - min(blk0, kb - 1);
-      const ST sraw = rel == 0 ? scr[0] : rel == 1 ? scr[1] : rel == 2 ? scr[2] : scr[3];
-      const float s = dt<SDT>::to_f32(sraw);
+    for (int i = 0; i < 2; ++i) {
+      sf[i] = dt<SDT>::to_f32(scr[st][i]);
       uint32_t z = 1u << (BITS - 1);
       if constexpr (HAS_ZP) {
         constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
-        const uint32_t zb = rel == 0 ? zbr[0] : rel == 1 ? zbr[1] : rel == 2 ? zbr[2] : zbr[3];
-        const int blk = min(kw >> log2_bs, kb - 1);
-        z = (zb >> ((blk * BITS) & 7)) & zm;
+        const int b = min(blk0 + i, kb - 1);
+        z = (zbr[st][i] >> ((b * BITS) & 7)) & zm;
       }
-      const float zs = (float)z * s;
+      zs[i] = (float)z * sf[i];
+    }
+    uint32_t pk[HK / 2];
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) {
+      // Block of this word relative to the thread's first block (0 or 1).
+      const bool second = min((kt + w * P) >> log2_bs, kb - 1) != blk0;
+      const float s = second ? sf[1] : sf[0];
+      const float z = second ? zs[1] : zs[0];
       float q[P];
-      word_codes_f32<BITS>(cw[w], q);
+      word_codes_f32<BITS>(cw[st][w], q);
       // (q - z) * s = q * s - z * s: both products exact, the difference
       // exact, one rounding to the activation dtype.
 #pragma unroll
-      for (int j = 0; j < P; j += 2) pk[(w * P + j) / 2] = Op::pack(fmaf(q[j], s, -zs), fmaf(q[j + 1], s, -zs));
+      for (int j = 0; j < P; j += 2) pk[(w * P + j) / 2] = Op::pack(fmaf(q[j], s, -z), fmaf(q[j + 1], s, -z));
     }
 #pragma unroll
-    for (int j = 0; j < GBK / 8; ++j)
-      *reinterpret_cast<u32x4*>(&bs[tid * LDS_ROW + 8 * j]) =
+    for (int j = 0; j < HK / 8; ++j)
+      *reinterpret_cast<u32x4*>(&bs[bcol * LDS_ROW + khalf + 8 * j]) =
           u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = (K + GBK - 1) / GBK;
-  load_step(0);
-  store_step(0, 0);
-  __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) load_step((s + 1) * GBK);
+  auto mfma_step = [&](int buf) {
     const uint16_t* as = As + buf * STAGE;
     const uint16_t* bs = Bs + buf * STAGE;
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 32) {
-      typename Op::V bf[8];
+      typename Op::V af[TM];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bf[j] = __builtin_bit_cast(typename Op::V,
-                                   *reinterpret_cast<const u32x4*>(&bs[(wn + j * 16 + fr) * LDS_ROW + kk + fk]));
+      for (int i = 0; i < TM; ++i)
+        af[i] = __builtin_bit_cast(typename Op::V,
+                                   *reinterpret_cast<const u32x4*>(&as[(wm + i * 16 + fr) * LDS_ROW + kk + fk]));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const typename Op::V af = __builtin_bit_cast(
-            typename Op::V, *reinterpret_cast<const u32x4*>(&as[(wm + i * 16 + fr) * LDS_ROW + kk + fk]));
+      for (int j = 0; j < TN; ++j) {
+        const typename Op::V bf = __builtin_bit_cast(
+            typename Op::V, *reinterpret_cast<const u32x4*>(&bs[(wn + j * 16 + fr) * LDS_ROW + kk + fk]));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = Op::run(af, bf[j], acc[i][j]);
+        for (int i = 0; i < TM; ++i) acc[i][j] = Op::run(af[i], bf, acc[i][j]);
       }
     }
-    if (more) store_step((s + 1) * GBK, buf ^ 1);
+  };
+  // One pipelined step s (register stage and LDS buffer = s & 1 = ST).
+  auto step = [&](int s, auto st_tag) {
+    constexpr int ST_ = decltype(st_tag)::value;
+    load_a((s + 1) * GBK);
+    load_b((s + 2) * GBK, ST_);
+    mfma_step(ST_);
+    store_a(ST_ ^ 1);
+    store_b((s + 1) * GBK, ST_ ^ 1, ST_ ^ 1);
     __syncthreads();
+  };
+
+  const int nsteps = (K + GBK - 1) / GBK;
+  load_a(0);
+  load_b(0, 0);
+  load_b(GBK, 1);
+  store_a(0);
+  store_b(0, 0, 0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
   }
 
   // Epilogue: lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16 of
   // each 16 x 16 tile.
   const int cc = lane & 15, rr = (lane >> 4) * 4;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < TN; ++j) {
     const int n = n0 + wn + j * 16 + cc;
     if (n >= N) continue;
     const float bv = bias ? bits16_to_f32<XDT>(bias[n]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm + i * 16 + rr + e;
@@ -388,20 +437,25 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
                        a.N * a.kb * (int64_t)sizeof(ST) < 0x7FFFFF00LL;
   if constexpr (XDT != DT_F32) {
     if (mfma_ok) {
-      const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
+      // 224-column tiles when they divide N evenly (no partial tiles), else 256.
+      const bool n224 = (a.N % 224) == 0;
+      const int bn = n224 ? 224 : 256;
+      const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + bn - 1) / bn);
       constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);   // double-buffered A and B
-      static bool attr_set = false;
-      if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP>,
+      auto kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7>
+                       : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8>;
+      static bool attr_set[2] = {false, false};
+      if (!attr_set[n224]) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set[n224] = true;
       }
-      hipLaunchKernelGGL((gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP>), dim3(tiles_m * tiles_n),
-                         dim3(GEMM_THREADS), lds, a.stream, (const uint16_t*)a.A, a.B,
-                         (const ST*)a.scales, a.zp, (const uint16_t*)a.bias, (uint16_t*)a.Y,
-                         (int)a.M, (int)a.K, (int)a.N, (int)a.kb, ilog2i(a.block_size),
-                         ilog2i(a.blob), (int)a.zp_row_bytes, tiles_m);
+      hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
+                         (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
+                         (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
+                         (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), (int)a.zp_row_bytes,
+                         tiles_m);
       return hipGetLastError();
     }
   }
