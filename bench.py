@@ -174,26 +174,31 @@ def _time_launches(fn, n, stream):
 
 
 def bench_prefill(qmm, dev, stream, args):
-    """Prefill GEMM M=2048, K=4096, N=14336 (4-bit asymmetric bs 32, bf16)."""
+    """Prefill GEMM M=2048, K=4096, N=14336 (4-bit asymmetric bs 32, bf16), on
+    the operator's layout and on the tiled layout (weights repacked once,
+    before the timed region, as an inference session does at load time)."""
     from block_quantized_weight_matmulnbits_amd.workloads import prefill_gemm
     c = prefill_gemm().to(dev)
     Y = torch.empty(c.M, c.N, dtype=torch.bfloat16, device=dev)
-
-    def run(_):
-        qmm.qmm_gemm(c.A, c.B, c.scales, c.zero_points, None, Y, c.M, c.K, c.N, c.block_size,
-                      c.bits, 0, stream)
-
-    for i in range(3):
-        run(i)
-    torch.cuda.synchronize()
-    ms = _time_launches(run, max(5, args.steps // 20), stream)
+    t = qmm.qmm_repack(c.B, c.scales, c.zero_points, c.K, c.N, c.block_size, c.bits,
+                       stream=stream)
     flop = 2.0 * c.M * c.N * c.K
-    tflops = flop / (ms * 1e-3) / 1e12
-    return {"workload": "prefill GEMM M=2048 K=4096 N=14336, bf16 activations, 4-bit asymmetric "
-                        "block 32, bf16 output, fp32 accumulate",
-            "ms": round(ms, 4), "tflops": round(tflops, 2), "unit": "TFLOP/s",
-            "bound": "mfma", "peak": BF16_PEAK_TFLOPS,
-            "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop}
+    res = {"workload": "prefill GEMM M=2048 K=4096 N=14336, bf16 activations, 4-bit asymmetric "
+                       "block 32, bf16 output, fp32 accumulate",
+           "bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flop_per_launch": flop}
+    for name, B, S, Z in (("tiled", t, None, None), ("operator_layout", c.B, c.scales,
+                                                    c.zero_points)):
+        def run(_):
+            qmm.qmm_gemm(c.A, B, S, Z, None, Y, c.M, c.K, c.N, c.block_size, c.bits, 0, stream)
+
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        ms = _time_launches(run, max(5, args.steps // 20), stream)
+        tflops = flop / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tflops, 2),
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    return res
 
 
 def bench_compint8(qmm, dev, stream, args):

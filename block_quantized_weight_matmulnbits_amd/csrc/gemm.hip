@@ -25,6 +25,7 @@
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_layout.h"
 
 namespace qmm {
 
@@ -113,12 +114,12 @@ __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
 constexpr int GEMM_WAVES = 8;
 constexpr int GEMM_TPB = 64 * GEMM_WAVES;
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN>
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL>
 __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
-    int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m) {
+    int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m, int chunks) {
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int BN = 32 * TN;
@@ -147,21 +148,43 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   // make the compiler loop over the lanes for every load).  This thread's
   // column is addressed by offset; a column past N (or a thread with no
   // column) gets an offset past the extent, which reads zeros.
+  // Thread t dequantizes half t & 1 (32 codes) of column t >> 1 of the tile,
+  // so adjacent lanes read adjacent 16-byte pieces.
+  //   operator layout: codes at n * row_bytes + k * bits / 8; scale (n, b) at
+  //     n * kb + b; zero point (n, b) at bit n * zp_row_bytes * 8 + b * bits.
+  //   tiled layout (qmm_layout.h): codes at ((g * chunks + c) * 32 + i) *
+  //     chunk_bytes + half; scale at (g * kb + b) * 32 + i; zero point at bit
+  //     ((g * kb + b) * 32 + i) * bits, with n = 32 g + i and c = k / 64.
   const int row_bytes = kb << log2_blob;
+  constexpr int CHUNK_BYTES = TKC * BITS / 8;
   const bool dq = tid < 2 * BN;                // this thread dequantizes
-  const int bcol = tid % BN;
+  const int bcol = tid >> 1;
   const int ncol = n0 + bcol;
-  const int khalf = (tid / BN) * HK;           // which half of the K-step
+  const int khalf = (tid & 1) * HK;            // which half of the K-step
   const bool ncol_ok = dq && ncol < N;
+  const int ngroups = (N + TG - 1) / TG;
+  const int code_extent = TL ? ngroups * chunks * TG * CHUNK_BYTES : N * row_bytes;
+  const int sc_extent = TL ? ngroups * kb * TG : N * kb;
+  const int zp_extent = TL ? ngroups * kb * TG * BITS / 8 : N * zp_row_bytes;
   const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)B, 0, N * row_bytes, BUF_WORD3);
+      (void*)B, 0, code_extent, BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)scales, 0, N * kb * (int)sizeof(ST), BUF_WORD3);
+      (void*)scales, 0, sc_extent * (int)sizeof(ST), BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)zp, 0, HAS_ZP ? N * zp_row_bytes : 0, BUF_WORD3);
-  const int col_code0 = ncol_ok ? ncol * row_bytes : OOB;
-  const int col_sc0 = ncol_ok ? ncol * kb : OOB / 4;
-  const int col_zp0 = ncol_ok ? ncol * zp_row_bytes : OOB;
+      (void*)zp, 0, HAS_ZP ? zp_extent : 0, BUF_WORD3);
+  const int cg = ncol / TG, ci = ncol % TG;
+  // Byte offset of this thread's codes for the K-step starting at k0 = 64 s:
+  // col_code0 + s * code_step.
+  const int col_code0 = !ncol_ok ? OOB
+                        : TL ? (cg * chunks * TG + ci) * CHUNK_BYTES + (khalf * BITS) / 8
+                             : ncol * row_bytes + (khalf * BITS) / 8;
+  const int code_step = TL ? TG * CHUNK_BYTES : CHUNK_BYTES;
+  // Scale index of block b: col_sc0 + b * sc_stride.
+  const int col_sc0 = !ncol_ok ? OOB / 4 : TL ? cg * kb * TG + ci : ncol * kb;
+  const int sc_stride = TL ? TG : 1;
+  // Zero-point bit of block b: col_zb0 + b * zb_stride.
+  const int col_zb0 = TL ? (cg * kb * TG + ci) * BITS : ncol * zp_row_bytes * 8;
+  const int zb_stride = TL ? TG * BITS : BITS;
 
   // Register stages.
   u32x4 av[4];                       // A chunks of the next step
@@ -184,7 +207,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   // (k >= K), so they add nothing.
   auto load_b = [&](int k0, int st) {
     const int kt = k0 + khalf;
-    const int byte0 = col_code0 + ((kt * BITS) >> 3);
+    const int byte0 = col_code0 + (k0 >> 6) * code_step;
     if constexpr (WPT >= 4) {
 #pragma unroll
       for (int w = 0; w < WPT; w += 4) {
@@ -199,12 +222,14 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int b = min(blk0 + i, kb - 1);
+      const int si = col_sc0 + b * sc_stride;
       if constexpr (sizeof(ST) == 4)
-        scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, (col_sc0 + b) * 4, 0, 0));
+        scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, si * 4, 0, 0));
       else
-        scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, (col_sc0 + b) * 2, 0, 0));
+        scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, si * 2, 0, 0));
       if constexpr (HAS_ZP)
-        zbr[st][i] = __builtin_amdgcn_raw_buffer_load_b8(rzp, col_zp0 + ((b * BITS) >> 3), 0, 0);
+        zbr[st][i] = __builtin_amdgcn_raw_buffer_load_b8(
+            rzp, ncol_ok ? (col_zb0 + b * zb_stride) >> 3 : OOB, 0, 0);
     }
   };
   auto store_a = [&](int buf) {
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
       if constexpr (HAS_ZP) {
         constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
         const int b = min(blk0 + i, kb - 1);
-        z = (zbr[st][i] >> ((b * BITS) & 7)) & zm;
+        z = (zbr[st][i] >> ((col_zb0 + b * zb_stride) & 7)) & zm;
       }
       zs[i] = (float)z * sf[i];
     }
@@ -330,12 +355,12 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
 // ---------------------------------------------------------------------------
 constexpr int ROWS_CHUNK = 2048;   // activations per LDS chunk and row
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int MT>
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int MT, bool TL>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(
     const typename dt<XDT>::T* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const typename dt<XDT>::T* __restrict__ bias, typename dt<XDT>::T* __restrict__ Y, int Mp,
-    int K, int N, int kb, int log2_blob, int zp_row_bytes) {
+    int K, int N, int kb, int log2_blob, int zp_row_bytes, int chunks) {
   constexpr int P = 32 / BITS;
   __shared__ float xs[MT * ROWS_CHUNK];
   const int lane = threadIdx.x & 63;
@@ -368,9 +393,27 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(
       for (int r = 0; r < R; ++r) {
         if (r >= nrows) continue;
         const int n = row0 + r;
-        const uint32_t cwd = reinterpret_cast<const uint32_t*>(B + (int64_t)n * row_bytes)[w];
-        const float s = dt<SDT>::to_f32(scales[(int64_t)n * kb + blk]);
-        const int z = (int)load_zp<BITS, HAS_ZP>(zp + (int64_t)n * zp_row_bytes, blk);
+        uint32_t cwd;
+        float s;
+        int z = 1 << (BITS - 1);
+        if constexpr (TL) {
+          // Tiled layout (qmm_layout.h): word w of the row lies in chunk
+          // w / chunk_words of group n / 32, column n % 32.
+          constexpr int CW = TKC * BITS / 32;     // words per column chunk
+          const int64_t g = n / TG, i = n % TG;
+          cwd = reinterpret_cast<const uint32_t*>(B)[((g * chunks + w / CW) * TG + i) * CW + w % CW];
+          const int64_t si = (g * kb + blk) * TG + i;
+          s = dt<SDT>::to_f32(scales[si]);
+          if constexpr (HAS_ZP) {
+            constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+            const int64_t bit = si * BITS;
+            z = (int)(((uint32_t)zp[bit >> 3] >> (bit & 7)) & zm);
+          }
+        } else {
+          cwd = reinterpret_cast<const uint32_t*>(B + (int64_t)n * row_bytes)[w];
+          s = dt<SDT>::to_f32(scales[(int64_t)n * kb + blk]);
+          z = (int)load_zp<BITS, HAS_ZP>(zp + (int64_t)n * zp_row_bytes, blk);
+        }
         float qz[P];
 #pragma unroll
         for (int j = 0; j < P; ++j) {
@@ -417,10 +460,12 @@ static hipError_t launch_rows(const MatArgs& a) {
   const int grid = (int)((a.N + 4 * R - 1) / (4 * R));
   for (int64_t m0 = 0; m0 < a.M; m0 += MT) {
     const int Mp = (int)std::min<int64_t>(MT, a.M - m0);
-    hipLaunchKernelGGL((gemm_rows_kernel<BITS, XDT, SDT, HAS_ZP, R, MT>), dim3(grid), dim3(256),
-                       0, a.stream, (const XT*)a.A + m0 * a.K, a.B, (const ST*)a.scales, a.zp,
-                       (const XT*)a.bias, (XT*)a.Y + m0 * a.N, Mp, (int)a.K, (int)a.N,
-                       (int)a.kb, ilog2i(a.blob), (int)a.zp_row_bytes);
+    auto kern = a.tiled ? gemm_rows_kernel<BITS, XDT, SDT, HAS_ZP, R, MT, true>
+                        : gemm_rows_kernel<BITS, XDT, SDT, HAS_ZP, R, MT, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, a.stream, (const XT*)a.A + m0 * a.K, a.B,
+                       (const ST*)a.scales, a.zp, (const XT*)a.bias, (XT*)a.Y + m0 * a.N, Mp,
+                       (int)a.K, (int)a.N, (int)a.kb, ilog2i(a.blob), (int)a.zp_row_bytes,
+                       (int)a.chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -433,8 +478,9 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
   // Every buffer offset of the MFMA kernel must fit in 31 bits.
   const bool mfma_ok = XDT != DT_F32 && a.M > 16 && (a.K % 8) == 0 &&
                        ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 < 0x7FFFFF00LL &&
-                       a.N * a.kb * a.blob + 64 < 0x7FFFFF00LL &&
-                       a.N * a.kb * (int64_t)sizeof(ST) < 0x7FFFFF00LL;
+                       (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
+                       (a.N + 32) * (a.chunks + 2) * 64 * BITS / 8 < 0x7FFFFF00LL &&
+                       (a.N + 32) * a.kb * (int64_t)sizeof(ST) < 0x7FFFFF00LL;
   if constexpr (XDT != DT_F32) {
     if (mfma_ok) {
       // 224-column tiles when they divide N evenly (no partial tiles), else 256.
@@ -442,20 +488,24 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
       const int bn = n224 ? 224 : 256;
       const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + bn - 1) / bn);
       constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);   // double-buffered A and B
-      auto kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7>
-                       : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8>;
-      static bool attr_set[2] = {false, false};
-      if (!attr_set[n224]) {
+      decltype(&gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>) kern;
+      if (a.tiled) kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, true>
+                               : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, true>;
+      else kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, false>
+                       : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>;
+      const int which = (n224 ? 1 : 0) + (a.tiled ? 2 : 0);
+      static bool attr_set[4] = {false, false, false, false};
+      if (!attr_set[which]) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_set[n224] = true;
+        attr_set[which] = true;
       }
       hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
                          (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
                          (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
                          (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), (int)a.zp_row_bytes,
-                         tiles_m);
+                         tiles_m, (int)a.chunks);
       return hipGetLastError();
     }
   }

@@ -10,6 +10,7 @@
 
 #include "../../include/qmm.h"
 #include "qmm_internal.h"
+#include "qmm_layout.h"
 
 using qmm::MatArgs;
 
@@ -84,11 +85,23 @@ int validate_matmul(const char* fn, Route route, const void* A, int a_dtype, con
                 "%s: a_dtype=%d / s_dtype=%d is not a qmm_dtype. Why: A, scales, bias and Y must "
                 "be a float compute dtype. How to fix: pass QMM_F32, QMM_F16 or QMM_BF16.",
                 fn, a_dtype, s_dtype);
-  if (b_layout != QMM_LAYOUT_ORT)
-    return fail(QMM_ERR_UNSUPPORTED,
-                "%s: b_layout=%d is not supported. Why: only the operator's own layout "
-                "[N, kb, block_size*bits/8] is accepted. How to fix: pass QMM_LAYOUT_ORT.",
-                fn, b_layout);
+  if (b_layout != QMM_LAYOUT_ORT && b_layout != QMM_LAYOUT_TILED &&
+      b_layout != QMM_LAYOUT_TILED_ZP)
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: b_layout=%d is not a qmm_layout. How to fix: pass QMM_LAYOUT_ORT for the "
+                "operator's [N, kb, block_size*bits/8] bytes, or QMM_LAYOUT_TILED[_ZP] for a "
+                "buffer written by qmm_repack.", fn, b_layout);
+  const bool tiled = b_layout != QMM_LAYOUT_ORT;
+  if (tiled && (scales != nullptr || zp != nullptr))
+    return fail(QMM_ERR_INVALID_ARG,
+                "%s: with a tiled layout the scales and zero_points arguments must be NULL. "
+                "Why: the repacked buffer carries them. How to fix: pass NULL and the layout "
+                "that matches how the buffer was repacked (QMM_LAYOUT_TILED_ZP if it was "
+                "repacked with zero points).", fn);
+  if (tiled && ((uintptr_t)B & 255) != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: a repacked buffer must be 256-byte aligned. How to "
+                "fix: pass the start of the buffer given to qmm_repack.", fn);
+  if (tiled) scales = B;   // placeholder for the null check below; replaced at the end
   if (route == Route::Float && accuracy_level == 4)
     return fail(QMM_ERR_INVALID_ARG,
                 "%s: accuracy_level=4 requests int8 activations (CompInt8). Why: this entry "
@@ -135,6 +148,14 @@ int validate_matmul(const char* fn, Route route, const void* A, int a_dtype, con
   out->bits = bits;
   out->a_dtype = a_dtype;
   out->s_dtype = s_dtype;
+  if (tiled) {
+    const qmm::TiledGeom g = qmm::tiled_geom(K, N, block_size, bits, dtype_size(s_dtype),
+                                             b_layout == QMM_LAYOUT_TILED_ZP);
+    out->tiled = 1;
+    out->chunks = g.chunks;
+    out->scales = B + g.scales_off;
+    out->zp = b_layout == QMM_LAYOUT_TILED_ZP ? B + g.zps_off : nullptr;
+  }
   return QMM_OK;
 }
 
@@ -198,6 +219,9 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
                            s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
                            accuracy_level, &a);
   if (st != QMM_OK) return st;
+  if (a.tiled)
+    return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8: the tiled layout is not supported by "
+                "the CompInt8 kernels. How to fix: pass the operator's layout (QMM_LAYOUT_ORT).");
   if (M == 0) return QMM_OK;
   st = check_workspace("qmm_gemm_compint8", a, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
@@ -256,10 +280,57 @@ int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const flo
   return hip_status(qmm::launch_conv_int8(c), fn);
 }
 
+size_t qmm_repacked_bytes(int64_t K, int64_t N, int block_size, int bits, int s_dtype,
+                          int has_zero_points) {
+  if (K <= 0 || N <= 0 || block_size < 16 || !is_pow2(block_size) ||
+      (bits != 2 && bits != 4 && bits != 8) || dtype_size(s_dtype) == 0)
+    return 0;
+  return (size_t)qmm::tiled_geom(K, N, block_size, bits, dtype_size(s_dtype),
+                                 has_zero_points != 0).total;
+}
+
+int qmm_repack(const uint8_t* B, const void* scales, int s_dtype, const uint8_t* zero_points,
+               int64_t K, int64_t N, int block_size, int bits, void* out, size_t out_bytes,
+               void* stream) {
+  MatArgs a;
+  int st = validate_matmul("qmm_repack", Route::Float, B, QMM_BF16, B, QMM_LAYOUT_ORT, scales,
+                           s_dtype, zero_points, nullptr, (void*)B, 0, K, N, block_size, bits, 0,
+                           &a);
+  if (st != QMM_OK) return st;
+  const size_t need = qmm_repacked_bytes(K, N, block_size, bits, s_dtype, zero_points != nullptr);
+  if (out == nullptr || out_bytes < need || ((uintptr_t)out & 255) != 0)
+    return fail(QMM_ERR_INVALID_ARG, "qmm_repack: out must be a 256-byte aligned device buffer "
+                "of at least %zu bytes (got %zu at %p). How to fix: allocate "
+                "qmm_repacked_bytes(K, N, block_size, bits, s_dtype, has_zero_points) bytes.",
+                need, out_bytes, out);
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_repack(a, (uint8_t*)out, false, nullptr, nullptr, nullptr),
+                    "qmm_repack");
+}
+
+int qmm_unrepack(const void* tiled, int has_zero_points, int64_t K, int64_t N, int block_size,
+                 int bits, int s_dtype, uint8_t* B, void* scales, uint8_t* zero_points,
+                 void* stream) {
+  MatArgs a;
+  int st = validate_matmul("qmm_unrepack", Route::Float, B, QMM_BF16, B, QMM_LAYOUT_ORT, scales,
+                           s_dtype, nullptr, nullptr, (void*)B, 0, K, N, block_size, bits, 0, &a);
+  if (st != QMM_OK) return st;
+  if (tiled == nullptr || ((uintptr_t)tiled & 255) != 0 || (has_zero_points && !zero_points))
+    return fail(QMM_ERR_INVALID_ARG, "qmm_unrepack: tiled must be a 256-byte aligned repacked "
+                "buffer, and zero_points non-NULL when it holds zero points.");
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_repack(a, (uint8_t*)tiled, true, B, scales,
+                                       has_zero_points ? zero_points : nullptr),
+                    "qmm_unrepack");
+}
+
 int qmm_debug_unpack(const uint8_t* B, int b_layout, const void* scales, int s_dtype,
                      const uint8_t* zero_points, int64_t K, int64_t N, int block_size, int bits,
                      uint8_t* codes, uint8_t* zps, float* w, void* stream) {
   MatArgs a;
+  if (b_layout != QMM_LAYOUT_ORT)
+    return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_unpack: only the operator's layout is decoded "
+                "here. How to fix: qmm_unrepack the buffer first.");
   // Validate as a matmul with a dummy activation/output (never touched).
   const void* dummy = B;
   if (w != nullptr && scales == nullptr)

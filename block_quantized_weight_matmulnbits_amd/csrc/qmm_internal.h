@@ -20,6 +20,10 @@ struct MatArgs {
   int64_t block_size = 0, kb = 0, blob = 0, zp_row_bytes = 0;
   int bits = 4;
   int a_dtype = 0, s_dtype = 0;
+  // 0: operator layout; 1: tiled (qmm_layout.h), B / scales / zp then point
+  // at the regions of the repacked buffer.
+  int tiled = 0;
+  int64_t chunks = 0;     // tiled: 64-code chunks per column
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
   hipStream_t stream = nullptr;
@@ -53,6 +57,10 @@ struct ConvArgs {
   hipStream_t stream = nullptr;
 };
 hipError_t launch_conv_int8(const ConvArgs& c);
+
+// Repack into / out of the tiled layout (qmm_layout.h).
+hipError_t launch_repack(const MatArgs& a, uint8_t* tiled, bool inverse, uint8_t* B_out,
+                         void* scales_out, uint8_t* zp_out);
 
 // Codec export: codes [N, K], zero points [N, kb], dequantized weight [N, K].
 hipError_t launch_unpack(const MatArgs& a, uint8_t* codes, uint8_t* zps, float* w);

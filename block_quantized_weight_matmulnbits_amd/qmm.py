@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
 QMM_F32, QMM_F16, QMM_BF16 = 0, 1, 2
-QMM_LAYOUT_ORT = 0
+QMM_LAYOUT_ORT, QMM_LAYOUT_TILED, QMM_LAYOUT_TILED_ZP = 0, 1, 2
 QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED, QMM_ERR_WORKSPACE, QMM_ERR_HIP = 0, -1, -2, -3, -4
 
 _TORCH_TO_QMM = {torch.float32: QMM_F32, torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
@@ -39,6 +39,9 @@ _SIGS = {
                            _i32, _vp, _sz, _vp], _i32),
     "qconv_int8": ([_vp, _vp, _vp, _vp, _f32, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "qmm_repacked_bytes": ([_i64, _i64, _i32, _i32, _i32, _i32], _sz),
+    "qmm_repack": ([_vp, _vp, _i32, _vp, _i64, _i64, _i32, _i32, _vp, _sz, _vp], _i32),
+    "qmm_unrepack": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "qmm_debug_unpack": ([_vp, _i32, _vp, _i32, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "qmm_debug_quantize_a": ([_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp], _i32),
     "qmm_debug_compint8_block_dots": ([_vp, _i32, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
@@ -81,18 +84,60 @@ def qmm_last_error() -> str:
     return lib.qmm_last_error().decode()
 
 
+class Repacked:
+    """A device buffer written by :func:`qmm_repack`: pass it as ``B`` (with
+    ``scales=None`` and ``zero_points=None``) to qmm_gemv / qmm_gemm."""
+
+    def __init__(self, buf, s_dtype, has_zero_points):
+        self.buf = buf
+        self.s_dtype = s_dtype
+        self.layout = QMM_LAYOUT_TILED_ZP if has_zero_points else QMM_LAYOUT_TILED
+
+
+def _weights(B, scales):
+    """(B pointer, layout, scales pointer, scales dtype) for either layout."""
+    if isinstance(B, Repacked):
+        if scales is not None:
+            raise ValueError("a repacked buffer carries its scales: pass scales=None")
+        return B.buf.data_ptr(), B.layout, None, B.s_dtype
+    return B.data_ptr(), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales)
+
+
 def qmm_gemv(A, B, scales, zero_points, bias, Y, K, N, block_size, bits, accuracy_level=0,
              stream=None):
-    _check(lib.qmm_gemv(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales),
-                        _ptr(zero_points), _ptr(bias), _ptr(Y), K, N, block_size, bits,
-                        accuracy_level, _stream(stream)))
+    b, layout, s, sdt = _weights(B, scales)
+    _check(lib.qmm_gemv(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
+                        _ptr(Y), K, N, block_size, bits, accuracy_level, _stream(stream)))
 
 
 def qmm_gemm(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level=0,
              stream=None):
-    _check(lib.qmm_gemm(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales),
-                        _ptr(zero_points), _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
-                        accuracy_level, _stream(stream)))
+    b, layout, s, sdt = _weights(B, scales)
+    _check(lib.qmm_gemm(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
+                        _ptr(Y), M, K, N, block_size, bits, accuracy_level, _stream(stream)))
+
+
+def qmm_repacked_bytes(K, N, block_size, bits, s_dtype, has_zero_points) -> int:
+    sdt = s_dtype if isinstance(s_dtype, int) else _TORCH_TO_QMM[s_dtype]
+    return int(lib.qmm_repacked_bytes(K, N, block_size, bits, sdt, int(bool(has_zero_points))))
+
+
+def qmm_repack(B, scales, zero_points, K, N, block_size, bits, out=None, stream=None):
+    """Repack (B, scales, zero_points) into ``out`` (allocated when None) and
+    return it as a :class:`Repacked`."""
+    nbytes = qmm_repacked_bytes(K, N, block_size, bits, scales.dtype, zero_points is not None)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=B.device)
+    _check(lib.qmm_repack(_ptr(B), _ptr(scales), _dt(scales), _ptr(zero_points), K, N, block_size,
+                          bits, _ptr(out), out.numel() * out.element_size(), _stream(stream)))
+    return Repacked(out, _dt(scales), zero_points is not None)
+
+
+def qmm_unrepack(tiled, K, N, block_size, bits, B, scales, zero_points, stream=None):
+    buf = tiled.buf if isinstance(tiled, Repacked) else tiled
+    _check(lib.qmm_unrepack(_ptr(buf), int(zero_points is not None), K, N, block_size, bits,
+                            _dt(scales), _ptr(B), _ptr(scales), _ptr(zero_points),
+                            _stream(stream)))
 
 
 def qmm_compint8_workspace_size(M, K, block_size) -> int:

@@ -46,8 +46,15 @@ typedef enum qmm_dtype {
 } qmm_dtype;
 
 typedef enum qmm_layout {
-    /* The operator's own layout: B[N, kb, block_size*bits/8]. */
-    QMM_LAYOUT_ORT = 0
+    /* The operator's own layout: B[N, kb, block_size*bits/8], with separate
+     * scales and (optional) zero-point tensors. */
+    QMM_LAYOUT_ORT = 0,
+    /* The tiled layout written by qmm_repack (see there), without / with zero
+     * points.  B then points to the whole repacked buffer, which carries the
+     * scales and zero points: the scales and zero_points arguments must be
+     * NULL and s_dtype names the dtype the scales were repacked from. */
+    QMM_LAYOUT_TILED = 1,
+    QMM_LAYOUT_TILED_ZP = 2
 } qmm_layout;
 
 typedef enum qmm_status {
@@ -64,7 +71,8 @@ const char *qmm_last_error(void);
 /*
  * M = 1 decode GEMV (matmul_nbits.rs: execute, the m == 1 routes).
  *   A      [K]            a_dtype
- *   B      [N, kb, blob]  uint8, 16-byte aligned, layout QMM_LAYOUT_ORT
+ *   B      [N, kb, blob]  uint8, 16-byte aligned, layout QMM_LAYOUT_ORT (or the
+ *          buffer written by qmm_repack, layout QMM_LAYOUT_TILED[_ZP])
  *   scales [N, kb]        s_dtype
  *   zero_points [N, ceil(kb*bits/8)] uint8 or NULL
  *   bias   [N]            a_dtype or NULL
@@ -124,13 +132,43 @@ int qmm_gemm_compint8(const void *A, int a_dtype, const uint8_t *B,
  * mult = (in_scale * w_scale[oc]) / out_scale in binary32;
  * y = clamp(round_half_even(float(acc) * mult) + out_zp, clamp_min, clamp_max).
  * A ReLU is expressed as clamp_min = out_zp.  Groups and dilation are 1.
- * Requires C % 4 == 0 (rows of 4-byte words), |acc| < 2^24.
+ * Requires C % 4 == 0 (rows of 4-byte words) and KH*KW*C*2^14 < 2^31 (an
+ * exact int32 accumulator); float(acc) is the round-to-nearest conversion.
  */
 int qconv_int8(const int8_t *X, const int8_t *Wt, const int32_t *bias,
                const float *w_scale, float in_scale, float out_scale,
                int in_zp, int out_zp, int clamp_min, int clamp_max, int Nb,
                int H, int W, int C, int Co, int KH, int KW, int stride_h,
                int stride_w, int pad_h, int pad_w, int8_t *Y, void *stream);
+
+/*
+ * One-time repack of constant weights into the tiled layout (a byte
+ * permutation; onnx-runtime-ep-cpu matmul_nbits.rs caches its prepacked
+ * weights once per constant input, and the AMX path repacks B into tile
+ * order the same way).  Output columns form groups of 32 and K is cut into
+ * chunks of 64 codes; the buffer holds three regions, each 256-byte aligned:
+ *   codes  [group][chunk][32 columns][64*bits/8 bytes]  (each column chunk
+ *          is that column's bytes of B for codes [64c, 64c + 64), zero past
+ *          its row)
+ *   scales [group][block][32 columns]                  (s_dtype)
+ *   zps    [group][block][32 columns], bits per entry packed LSB first
+ *          (only when zero_points is non-NULL)
+ * Columns past N hold zeros.  qmm_repacked_bytes gives the buffer size.
+ * qmm_unrepack restores B and the scales exactly, and the zero points (the
+ * unused bits of each zero-point row's last byte are written as zero).
+ * Arguments as for qmm_gemv; out / tiled are device buffers of at least
+ * qmm_repacked_bytes bytes, 256-byte aligned.
+ */
+size_t qmm_repacked_bytes(int64_t K, int64_t N, int block_size, int bits, int s_dtype,
+                          int has_zero_points);
+
+int qmm_repack(const uint8_t *B, const void *scales, int s_dtype, const uint8_t *zero_points,
+               int64_t K, int64_t N, int block_size, int bits, void *out, size_t out_bytes,
+               void *stream);
+
+int qmm_unrepack(const void *tiled, int has_zero_points, int64_t K, int64_t N, int block_size,
+                 int bits, int s_dtype, uint8_t *B, void *scales, uint8_t *zero_points,
+                 void *stream);
 
 /*
  * Test exports: the integer intermediates, for bit-exact comparison.

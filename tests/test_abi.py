@@ -57,7 +57,9 @@ def gemv(qmm, **kw):
     (dict(K=0), -1, "K and N must be positive"),
     (dict(N=-3), -1, "K and N must be positive"),
     (dict(a_dtype=7), -1, "not a qmm_dtype"),
-    (dict(b_layout=5), -2, "layout"),
+    (dict(b_layout=5), -1, "not a qmm_layout"),
+    (dict(b_layout=1), -1, "must be NULL"),
+    (dict(b_layout=2, scales=None, B=FAKE + 16), -1, "256-byte aligned"),
     (dict(acc=4), -1, "qmm_gemm_compint8"),
     (dict(acc=9), -1, "accuracy_level must be in 0..4"),
     (dict(B=None), -1, "non-null"),
@@ -117,3 +119,37 @@ def conv(qmm, **kw):
 def test_conv_rejects_bad_arguments(qmm, kw, code, needle):
     assert conv(qmm, **kw) == code
     assert needle in qmm.qmm_last_error(), qmm.qmm_last_error()
+
+
+def test_repacked_bytes_geometry(qmm):
+    # 4-bit, K=4096, N=4096, bs=32, bf16 scales, zero points: 128 groups of 32
+    # columns, 64 chunks of 64 codes (32 bytes per column chunk), 128 blocks.
+    codes = 128 * 64 * 32 * 32
+    scales = 128 * 128 * 32 * 2
+    zps = 128 * 128 * 32 * 4 // 8
+    assert qmm.qmm_repacked_bytes(4096, 4096, 32, 4, 2, True) == codes + scales + zps
+    assert qmm.qmm_repacked_bytes(4096, 4096, 32, 4, 2, False) == codes + scales
+    # Ragged: K=100 (kb=4 blocks of 32 -> 128 codes -> 2 chunks), N=33 (2 groups),
+    # each region rounded up to 256 bytes.
+    r = lambda v: (v + 255) // 256 * 256
+    assert qmm.qmm_repacked_bytes(100, 33, 32, 8, 0, True) == (
+        r(2 * 2 * 32 * 64) + r(2 * 4 * 32 * 4) + r(2 * 4 * 32))
+    assert qmm.qmm_repacked_bytes(100, 33, 24, 4, 2, True) == 0      # bad block size
+    assert qmm.qmm_repacked_bytes(100, 33, 32, 3, 2, True) == 0      # bad bits
+
+
+def test_repack_rejects_bad_arguments(qmm):
+    st = qmm.lib.qmm_repack(FAKE, FAKE, 2, None, 4096, 4096, 32, 4, FAKE, 100, None)
+    assert st == -1 and "at least" in qmm.qmm_last_error()
+    st = qmm.lib.qmm_repack(FAKE, FAKE, 2, None, 4096, 4096, 32, 4, FAKE + 64, 1 << 30, None)
+    assert st == -1 and "256-byte aligned" in qmm.qmm_last_error()
+    st = qmm.lib.qmm_repack(FAKE, FAKE, 2, None, 4096, 4096, 32, 5, FAKE, 1 << 30, None)
+    assert st == -1 and "bits" in qmm.qmm_last_error()
+    st = qmm.lib.qmm_unrepack(FAKE, 1, 4096, 4096, 32, 4, 2, FAKE, FAKE, None, None)
+    assert st == -1 and "zero_points" in qmm.qmm_last_error()
+
+
+def test_compint8_rejects_tiled_layout(qmm):
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, FAKE, 4, 4096, 4096, 128,
+                                   4, 4, FAKE, 1 << 30, None)
+    assert st == -2 and "tiled" in qmm.qmm_last_error()
