@@ -485,9 +485,9 @@ static hipError_t launch_gemv_x(const GemvArgs& a) {
 }
 
 hipError_t launch_gemv(const GemvArgs& a) {
-  // The tiled layout has no dedicated M = 1 kernel yet: the row kernel of
-  // the GEMM reads it.
-  if (a.tiled) return launch_gemm(a);
+  // The tiled layout: its own split-K kernel, or for f32 activations and
+  // blocks shorter than a 16-byte unit of codes, the row kernel of the GEMM.
+  if (a.tiled) return gemv_tiled_supported(a) ? launch_gemv_tiled(a) : launch_gemm(a);
   switch (a.bits) {
     case 2: return launch_gemv_x<2>(a);
     case 4: return launch_gemv_x<4>(a);

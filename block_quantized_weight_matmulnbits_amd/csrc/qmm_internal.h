@@ -31,6 +31,9 @@ struct MatArgs {
 using GemvArgs = MatArgs;
 
 hipError_t launch_gemv(const MatArgs& a);
+// M = 1 on the tiled layout (gemv_tiled.hip).
+bool gemv_tiled_supported(const MatArgs& a);
+hipError_t launch_gemv_tiled(const MatArgs& a);
 
 // Batched / prefill matmul (M > 1): bf16/f16 MFMA kernel, or the fp32
 // multi-row fallback.

@@ -2,7 +2,9 @@
 
 Element-wise within tol * S at small ragged shapes for every (bits, block
 size, dtype, zero point, bias) combination, at the full Llama-3-8B layer
-shapes of the decode workload, and on the degenerate cases.
+shapes of the decode workload, and on the degenerate cases.  Every test runs
+on the operator's layout and on the tiled layout written by qmm_repack (the
+weights repacked on the device before the call).
 """
 import numpy as np
 import pytest
@@ -13,20 +15,32 @@ from tests.util import TOL, assert_within, oracle_matmul
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+LAYOUT = {"v": "ort"}
+
+
+@pytest.fixture(params=["ort", "tiled"], autouse=True)
+def layout(request):
+    LAYOUT["v"] = request.param
+    yield request.param
 
 
 def run_gemv(case):
     from block_quantized_weight_matmulnbits_amd import qmm
     c = case.to(DEV)
     Y = torch.empty(case.N, dtype=c.A.dtype, device=DEV)
-    qmm.qmm_gemv(c.A.reshape(-1), c.B, c.scales, c.zero_points, c.bias, Y, case.K, case.N,
-                 case.block_size, case.bits)
+    B, S, Z = c.B, c.scales, c.zero_points
+    if LAYOUT["v"] == "tiled":
+        B = qmm.qmm_repack(c.B, c.scales, c.zero_points, case.K, case.N, case.block_size,
+                           case.bits)
+        S = Z = None
+    qmm.qmm_gemv(c.A.reshape(-1), B, S, Z, c.bias, Y, case.K, case.N, case.block_size,
+                 case.bits)
     torch.cuda.synchronize()
     return Y
 
 
 def check(case, what=""):
-    print(f"[gemv] {what} M=1 K={case.K} N={case.N} bs={case.block_size} bits={case.bits} "
+    print(f"[gemv {LAYOUT['v']}] {what} M=1 K={case.K} N={case.N} bs={case.block_size} bits={case.bits} "
           f"a={case.a_dtype} s={case.s_dtype} zp={case.zero_points is not None} "
           f"bias={case.bias is not None}", flush=True)
     Y, S = oracle_matmul(case)
