@@ -1,33 +1,35 @@
 // gemv_tiled.hip -- M = 1 decode GEMV on the tiled weight layout (qmm_layout.h)
-// for gfx950: split-K over the waves of a workgroup, one coalesced 1 KiB load
-// of packed codes per wave instruction, a DPP / LDS reduction at the end.
+// for gfx950.
 //
 // Computes y[n] = sum_k x[k] * (code(n,k) - zp(n, k/bs)) * scale[n, k/bs]
 // (+ bias[n]) (onnx-runtime-ep-cpu matmul_nbits.rs: module documentation and
 // dequantize_nbits_value) from the buffer written by qmm_repack.
 //
-// Work split.  A workgroup owns CW columns of one 32-column group (CW = 32, 16
-// or 8) over the whole of K; its 4 waves split K into 4 contiguous ranges of
-// 64-code chunks.  In the tiled layout the CW columns' bytes of one chunk are
-// contiguous (CW * 8 * BITS bytes), so a wave-wide 16-byte-per-lane load reads
-// 1 KiB covering 64 / (CW * BITS / 2) consecutive chunks.  Lane l keeps one
-// column for the whole kernel and one fp32 partial sum; lanes of a column are
-// combined with cross-lane shuffles, and the 4 waves through LDS.
+// Work split.  A wave owns an octet of 8 columns of one 32-column group and
+// a contiguous share of K; a workgroup holds O octets times S shares of K
+// (O * S waves), sized so that the grid covers the 256 compute units about
+// once.  In the tiled layout the 8 columns' bytes of one 64-code chunk are
+// contiguous (8 * 8 * BITS bytes), so one 16-byte-per-lane wave load reads
+// 64 / (8 * BITS / 2) consecutive chunks in runs of 256 (4-bit) bytes; the
+// byte offset of load j is a per-lane base plus 4096 * j.  Lane l keeps one
+// column and one fp32 partial sum; lanes of a column are combined with
+// cross-lane shuffles and the S shares of K through LDS.
 //
-// Activations.  Each wave stages its own K range of x into LDS (no workgroup
-// barrier): as fp16 for f16 x; for bf16 x re-encoded exactly as fp16 after a
-// power-of-two shift per 16-byte unit of codes (the largest magnitude lands
-// in [2^14, 2^15), so every value within 2^28 of it keeps all of its 8
-// significant bits).  A range with inf/nan, bf16 subnormals or a wider
-// dynamic range takes an exact fp32 path instead.
+// Activations are staged once per workgroup into LDS (pieces of at most
+// 16384): as they are for f16 x; for bf16 x re-encoded exactly as fp16
+// after a power-of-two shift per 16-byte unit of codes (the largest
+// magnitude lands in [2^14, 2^15), so every value within 2^28 of it keeps
+// all of its 8 significant bits).  A piece with inf/nan, bf16 subnormals or
+// a wider dynamic range takes an exact fp32 path instead.
 //
 // Arithmetic.  A 16-bit half of a code word holds 16 / BITS codes at bit
-// offsets 0, BITS, ...; the codes at offsets p <= 8 - BITS of the word and of
-// the word shifted right by 8 are masked in place and OR-ed with fp16 1024.0,
-// giving 1024 + 2^p * code exactly.  Adding the fp16 pair -(1024 + 2^p * zp)
-// leaves 2^p * (code - zp) exactly, and v_dot2_f32_f16 multiplies that by two
-// activations (exact products) and accumulates in fp32, one accumulator per p,
-// scaled back by 2^-p at the end of the unit.
+// offsets 0, BITS, ...; the codes at offsets p <= 8 - BITS of the word and
+// of the word shifted right by 8 are masked in place and OR-ed with fp16
+// 1024.0 (one v_and_or_b32 per pair), giving 1024 + 2^p * code exactly.
+// Adding the fp16 pair -(1024 + 2^p * zp) leaves 2^p * (code - zp) exactly,
+// and v_dot2_f32_f16 multiplies that by two activations (exact products)
+// and accumulates in fp32, one accumulator per p, scaled back by 2^-p at the
+// end of each 16-byte unit.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 #include "qmm_layout.h"
@@ -38,26 +40,23 @@ namespace qmm {
 
 namespace {
 
-constexpr int TGV_THREADS = 256;
-constexpr int TGV_WAVES = 4;
-// Chunks of 64 codes staged at once per wave (4096 activations, 8 KiB).
-constexpr int TGV_PIECE = 64;
+constexpr int OCT = 8;            // columns per wave
+constexpr int PIECE_CHUNKS = 256; // 64-code chunks staged at once (16384 activations)
 constexpr int RSRC_WORD3 = 0x00020000;
-// Byte offset used for lanes without work: past every extent, reads zeros.
-constexpr int OFF_NONE = 0x7FFFFFF0;
+constexpr int MAX_WAVES = 16;
 
-// Geometry of one (BITS, CW) variant.
-template <int BITS, int CW>
+// Geometry of one code width.
+template <int BITS>
 struct TGeom {
   static constexpr int P = 32 / BITS;          // codes per 32-bit word
   static constexpr int E = 4 * P;              // codes per 16-byte unit
   static constexpr int CB = TKC * BITS / 8;    // bytes per column chunk
   static constexpr int UPC = CB / 16;          // units per column chunk
-  static constexpr int LPC = CW * UPC;         // lanes per chunk in a load
+  static constexpr int LPC = OCT * UPC;        // lanes per chunk in a load
   static constexpr int CPL = 64 / LPC;         // chunks per wave load
   static constexpr int NPOS = 8 / BITS;        // bit offsets p per half word
   static constexpr int LPU = E / 16;           // staging lanes per unit
-  static_assert(LPC <= 64 && 64 % LPC == 0, "a chunk's columns must fit one wave load");
+  static_assert(CPL * TG * CB == 4096, "a wave load steps 4096 bytes through the codes");
 };
 
 // One in-flight load of a wave: the lane's 16 bytes of codes and the aligned
@@ -70,9 +69,31 @@ struct TSlot {
   uint32_t zw;
 };
 
-// Staging of 16 activations per lane into fp16 pairs (pair word w*P/2 + i of
-// a code word w holds activations (wP + i, wP + i + P/2)), the per-unit
-// factor pw undoing the shift, and whether every unit was exact.
+// 16 activations x[k, k + 16) as raw 16-bit values; positions past K read
+// zero (buffer range checking).  vec: K % 8 == 0 and x 16-byte aligned, so a
+// 16-byte load is wholly inside or wholly past the end.
+__device__ __forceinline__ void load_x16(__amdgpu_buffer_rsrc_t rx, int k, bool vec,
+                                         u32x4 (&raw)[2]) {
+  if (vec) {
+    raw[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, k * 2, 0, 0);
+    raw[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, k * 2 + 16, 0, 0);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rx, (k + 2 * j) * 2, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rx, (k + 2 * j + 1) * 2, 0, 0);
+      w[j] = lo | (hi << 16);
+    }
+    raw[0] = u32x4{w[0], w[1], w[2], w[3]};
+    raw[1] = u32x4{w[4], w[5], w[6], w[7]};
+  }
+}
+
+// Staging of 16 activations (starting at a multiple of 16) into fp16 pairs:
+// pair word w*P/2 + i of code word w holds activations (wP + i, wP + i + P/2).
+// pw[unit] undoes the unit's shift.  Returns whether a unit is not exact.
+// The LPU lanes of a unit are adjacent and all take part (whole units).
 template <int BITS, int XDT>
 __device__ __forceinline__ bool stage16(const u32x4 (&raw)[2], int a, uint32_t* __restrict__ xs,
                                         float* __restrict__ pw) {
@@ -126,10 +147,6 @@ __device__ __forceinline__ bool stage16(const u32x4 (&raw)[2], int a, uint32_t* 
       pairs[w * (P / 2) + i] = as_u32(h);
     }
   }
-  // 16 activations of a 2-bit word span a whole word (P = 16) but only when
-  // the lane holds the full word; a lane always holds 16 consecutive
-  // activations starting at a multiple of 16, which is a whole number of
-  // code words for BITS >= 4 and one full word for BITS = 2.
   u32x4* dst = reinterpret_cast<u32x4*>(xs + a / 2);
   dst[0] = u32x4{pairs[0], pairs[1], pairs[2], pairs[3]};
   dst[1] = u32x4{pairs[4], pairs[5], pairs[6], pairs[7]};
@@ -137,188 +154,236 @@ __device__ __forceinline__ bool stage16(const u32x4 (&raw)[2], int a, uint32_t* 
   return bad;
 }
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int CW, int D>
-__global__ __launch_bounds__(TGV_THREADS) void gemv_tiled_kernel(
+// LDS layout, in 32-bit words, for a piece of pc chunks: the fp16 pairs
+// (pc + CPL chunks, the last CPL zero or unused), the unit factors, then the
+// S-share partial sums.
+template <int BITS>
+struct TLds {
+  int xs_words, pw_words, total;
+  __host__ __device__ TLds(int pc, int waves) {
+    constexpr int CPL = TGeom<BITS>::CPL, E = TGeom<BITS>::E;
+    xs_words = (pc + CPL) * 32;
+    pw_words = ((pc + CPL) * 64 / E + 3) / 4 * 4;
+    total = xs_words + pw_words + waves * OCT;
+  }
+};
+
+// LINB: blocks no longer than one wave load (bs <= 64 * CPL), so the scale
+// and zero-point offsets of load j are a per-lane base plus j times a step.
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int D, bool LINB>
+__global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
-    const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zps,
+    const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int K, int N, int kb,
-    int chunks, int log2_bs, int per_wave, int pc) {
-  using G = TGeom<BITS, CW>;
+    int chunks, int log2_bs, int n_oct, int O, int S, int pc) {
+  using G = TGeom<BITS>;
   using ST = typename dt<SDT>::T;
   constexpr int P = G::P, E = G::E, CB = G::CB, UPC = G::UPC, LPC = G::LPC, CPL = G::CPL;
+  constexpr int SZ = (int)sizeof(ST);
   constexpr uint32_t m = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
 
   extern __shared__ u32x4 smem_tv[];
+  const int W = O * S;
+  const TLds<BITS> L(pc, W);
+  uint32_t* xs = reinterpret_cast<uint32_t*>(smem_tv);
+  float* pw = reinterpret_cast<float*>(xs + L.xs_words);
+  float* red = pw + L.pw_words;
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Per-wave LDS region: pc * 32 pair words, then pc * 64 / E unit factors,
-  // rounded up to 16 bytes.
-  const int region = pc * 32 + (pc * (64 / E) + 3) / 4 * 4;
-  uint32_t* xs = reinterpret_cast<uint32_t*>(smem_tv) + wave * region;
-  float* pw = reinterpret_cast<float*>(xs + pc * 32);
-  float* red = reinterpret_cast<float*>(smem_tv) + TGV_WAVES * region;
-
-  const int slices = 32 / CW;
-  const int g = blockIdx.x / slices;
-  const int col0 = (blockIdx.x % slices) * CW;     // first column within the group
-  const int cl = lane / LPC;                        // chunk within a wave load
+  const int ol = wave % O, s = wave / O;             // octet in the workgroup, share of K
+  const int oct = blockIdx.x * O + ol;
+  const bool has_oct = oct < n_oct;
+  const int g = oct >> 2;                            // group
+  const int cl = lane / LPC;                         // chunk within a wave load
   const int rem = lane % LPC;
-  const int col = rem / UPC;                        // column within the slice
-  const int u = rem % UPC;                          // unit within the column chunk
-  const int gcol = col0 + col;                      // column within the group
+  const int col = rem / UPC;                         // column within the octet
+  const int u = rem % UPC;                           // unit within the column chunk
+  const int gcol = (oct & 3) * OCT + col;            // column within the group
+  const int ue = cl * TKC + u * E;                   // unit start within a wave load
 
   const int groups = (N + TG - 1) / TG;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)codes, 0, groups * chunks * TG * CB, RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)scales, 0, groups * kb * TG * (int)sizeof(ST), RSRC_WORD3);
+      (void*)scales, 0, groups * kb * TG * SZ, RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
       (void*)zps, 0, HAS_ZP ? groups * kb * TG * BITS / 8 : 0, RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, 0, K * 2, RSRC_WORD3);
   const bool x_vec = (K % 8) == 0 && (((uintptr_t)x) & 15) == 0;
 
-  const int w_lo = wave * per_wave;
-  const int w_hi = min(chunks, w_lo + per_wave);
+  // Block of a unit: chunk bases are multiples of CPL, so when a block spans
+  // at most one wave load (bs <= 64 * CPL) the block is the base's block plus
+  // a per-lane part, and otherwise the base's block alone.
+  const int lane_db = (TKC * CPL >= (1 << log2_bs)) ? (ue >> log2_bs) : 0;
+  const int lane_si = lane_db * TG + gcol;           // scale index minus the uniform part
+  const int lane_soff = (lane_si * SZ) & ~3;
+  const int lane_shalf = (SZ == 2) ? (lane_si & 1) * 16 : 0;
+  const int lane_zoff = ((lane_si * BITS) >> 3) & ~3;
+  const int lane_zbit = (lane_si * BITS) & 31;
+  // fp16 1024.0 twice, held in a register the compiler cannot see through:
+  // (code & mask) | magic then selects one v_and_or_b32 with the mask in a
+  // scalar register (gfx9 VOP3 takes no literal constants, so with both
+  // constants literal it would emit an AND and an OR).
+  uint32_t magic;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
   float acc = 0.0f;
+  const int nthreads = W * 64;
 
-  for (int p_lo = w_lo; p_lo < w_hi; p_lo += pc) {
-    const int p_hi = min(w_hi, p_lo + pc);
-    const int nloads = (p_hi - p_lo + CPL - 1) / CPL;
+  for (int P0 = 0; P0 < chunks; P0 += pc) {
+    const int pn = min(pc, chunks - P0);
+    // This wave's share of the piece: whole wave loads.
+    const int cs = (pn + S * CPL - 1) / (S * CPL) * CPL;
+    const int c_lo = P0 + s * cs;
+    const int c_hi = has_oct ? min(P0 + pn, c_lo + cs) : c_lo;
+    const int nloads = c_hi > c_lo ? (c_hi - c_lo + CPL - 1) / CPL : 0;
+    const int lane_code = ((g * chunks + c_lo + cl) * TG + gcol) * CB + u * 16;
+    const int lane_kr = (c_lo - P0) * TKC + ue;      // unit start within the staged piece
 
-    // Load j of the piece: chunk p_lo + j*CPL + cl; lanes past the piece
-    // read zeros from past the extents.
-    auto chunk_of = [&](int j) { return p_lo + j * CPL + cl; };
-    // A lane is live when its chunk is in the piece and its unit starts
-    // inside the blocks (chunk padding past kb * bs has no scale).
-    auto live_of = [&](int c) { return c < p_hi && ((c * TKC + u * E) >> log2_bs) < kb; };
-    auto issue = [&](TSlot& s, int j) {
-      const int c = chunk_of(j);
-      const bool live = live_of(c);
-      const int off = live ? ((g * chunks + c) * TG + gcol) * CB + u * 16 : OFF_NONE;
-      s.cw = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
-      const int b = (c * TKC + u * E) >> log2_bs;
-      const int si = (g * kb + b) * TG + gcol;
-      // Region sizes are multiples of 4 bytes, so aligned words are wholly
-      // inside or wholly past them.
-      s.sw = __builtin_amdgcn_raw_buffer_load_b32(
-          rs, live ? (si * (int)sizeof(ST)) & ~3 : OFF_NONE, 0, 0);
+    // x of the first two staging passes, loaded before the weights: loads
+    // return in order, so x loaded after them would wait for them.
+    const int n_act = (pn + CPL) * TKC;              // with CPL chunks of padding
+    const int a0 = threadIdx.x * 16, a1 = a0 + nthreads * 16;
+    u32x4 xr0[2], xr1[2];
+    load_x16(rx, P0 * TKC + a0, x_vec, xr0);
+    load_x16(rx, P0 * TKC + a1, x_vec, xr1);
+
+    // Uniform scale-index base of load 0 and, for LINB, the step per load.
+    const int ub0 = (g * kb + ((c_lo * TKC) >> log2_bs)) * TG;
+    const int ubs = ((CPL * TKC) >> log2_bs) * TG;
+    auto issue = [&](TSlot& sl, int j) {
+      sl.cw = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, 0);
+      const int ub = LINB ? ub0 + j * ubs
+                          : (g * kb + (((c_lo + j * CPL) * TKC) >> log2_bs)) * TG;
+      sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, ub * SZ + lane_soff, 0, 0);
       if constexpr (HAS_ZP)
-        s.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((si * BITS) >> 3) & ~3 : OFF_NONE,
-                                                    0, 0);
+        sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, ub * BITS / 8 + lane_zoff, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
-
     TSlot sl[D];
 #pragma unroll
     for (int q = 0; q < D; ++q) issue(sl[q], q);
 
-    // Stage this piece's activations (wave-local: the same wave reads them).
-    const int n_act = (p_hi - p_lo) * TKC;
+    // Stage the piece (all waves), then agree on the path.
     bool bad = false;
-    for (int a = lane * 16; a < n_act; a += 64 * 16) {
-      const int k = p_lo * TKC + a;
+    if (a0 < n_act) bad |= stage16<BITS, XDT>(xr0, a0, xs, pw);
+    if (a1 < n_act) bad |= stage16<BITS, XDT>(xr1, a1, xs, pw);
+    for (int a = a1 + nthreads * 16; a < n_act; a += nthreads * 16) {
       u32x4 raw[2];
-      if (x_vec) {
-        raw[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, k * 2, 0, 0);
-        raw[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, k * 2 + 16, 0, 0);
-      } else {
-        uint32_t w[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rx, (k + 2 * j) * 2, 0, 0);
-          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rx, (k + 2 * j + 1) * 2, 0, 0);
-          w[j] = lo | (hi << 16);
-        }
-        raw[0] = u32x4{w[0], w[1], w[2], w[3]};
-        raw[1] = u32x4{w[4], w[5], w[6], w[7]};
-      }
+      load_x16(rx, P0 * TKC + a, x_vec, raw);
       bad |= stage16<BITS, XDT>(raw, a, xs, pw);
     }
-    // Make the staged values visible to the other lanes of this wave.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const bool exact = __builtin_amdgcn_ballot_w64(bad) != 0;
+    const bool exact = __syncthreads_or(bad) != 0;
 
     if (!exact) {
-      for (int j0 = 0; j0 < nloads; j0 += D) {
+      // The activations of load j (read from LDS one load ahead of their use,
+      // so that the LDS latency hides behind the previous load's arithmetic).
+      // Loads past the share may point past the staged piece: clamped.
+      struct XV { uint32_t w[E / 2]; float f; };
+      auto fetch = [&](XV& xv, int j) {
+        const int kr = min(lane_kr + j * (CPL * TKC), 2 * L.xs_words - E);
+        const u32x4* p = reinterpret_cast<const u32x4*>(xs + kr / 2);
 #pragma unroll
-        for (int q = 0; q < D; ++q) {
-          const int j = j0 + q;
-          TSlot& s = sl[q];
-          const int c = chunk_of(j);
-          const bool live = live_of(c);
-          // Unit start relative to the piece; dead lanes read a staged spot.
-          const int kr = live ? (c - p_lo) * TKC + u * E : 0;
-          const u32x4* xv = reinterpret_cast<const u32x4*>(xs + kr / 2);
-          uint32_t xw[E / 2];
+        for (int t = 0; t < E / 8; ++t) {
+          const u32x4 v = p[t];
+          xv.w[4 * t + 0] = v.x; xv.w[4 * t + 1] = v.y; xv.w[4 * t + 2] = v.z; xv.w[4 * t + 3] = v.w;
+        }
+        xv.f = pw[kr / E];
+      };
+      // acc += scale * (codes . activations) for load j from slot sl.
+      // masked: the load may hold lanes past the share or past the blocks.
+      auto compute = [&](const TSlot& sl, const XV& xv, int j, bool masked) {
+        uint32_t z = 1u << (BITS - 1);
+        if constexpr (HAS_ZP) z = (sl.zw >> lane_zbit) & m;
+        float sc;
+        if constexpr (SZ == 4) sc = __uint_as_float(sl.sw);
+        else sc = bits16_to_f32<SDT>((uint16_t)(sl.sw >> lane_shalf));
+        float dp[G::NPOS];
+        half2_t nz[G::NPOS];
 #pragma unroll
-          for (int t = 0; t < E / 8; ++t) {
-            const u32x4 v = xv[t];
-            xw[4 * t + 0] = v.x; xw[4 * t + 1] = v.y; xw[4 * t + 2] = v.z; xw[4 * t + 3] = v.w;
-          }
-          const float f = pw[kr / E];
-          const int b = (c * TKC + u * E) >> log2_bs;
-          const int si = (g * kb + b) * TG + gcol;
-          uint32_t z = 1u << (BITS - 1);
-          if constexpr (HAS_ZP) z = (s.zw >> ((si * BITS) & 31)) & m;
-          float sc;
-          if constexpr (sizeof(ST) == 4) sc = __uint_as_float(s.sw);
-          else sc = bits16_to_f32<SDT>((uint16_t)(s.sw >> ((si & 1) * 16)));
-          float dp[G::NPOS];
-          half2_t nz[G::NPOS];
+        for (int pi = 0; pi < G::NPOS; ++pi) {
+          dp[pi] = 0.0f;
+          const uint32_t h = 0xE400u | (z << (pi * BITS));   // -(1024 + 2^p z)
+          nz[pi] = as_half2(h | (h << 16));
+        }
+        const uint32_t cw[4] = {sl.cw.x, sl.cw.y, sl.cw.z, sl.cw.w};
 #pragma unroll
-          for (int pi = 0; pi < G::NPOS; ++pi) {
-            dp[pi] = 0.0f;
-            const uint32_t h = 0xE400u | (z << (pi * BITS));   // -(1024 + 2^p z)
-            nz[pi] = as_half2(h | (h << 16));
-          }
-          const uint32_t cw[4] = {s.cw.x, s.cw.y, s.cw.z, s.cw.w};
+        for (int wi = 0; wi < 4; ++wi) {
 #pragma unroll
-          for (int wi = 0; wi < 4; ++wi) {
+          for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t src = hf ? (cw[wi] >> 8) : cw[wi];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const uint32_t src = hf ? (cw[wi] >> 8) : cw[wi];
-#pragma unroll
-              for (int pi = 0; pi < G::NPOS; ++pi) {
-                const int p = pi * BITS;
-                const uint32_t mask = (m << p) | (m << (p + 16));
-                const half2_t cv = as_half2((src & mask) | 0x64006400u) + nz[pi];
-                const int ci = (hf * 8 + p) / BITS;            // code index in the word
-                dp[pi] = __builtin_amdgcn_fdot2(cv, as_half2(xw[wi * (P / 2) + ci]), dp[pi],
-                                                false);
-              }
+            for (int pi = 0; pi < G::NPOS; ++pi) {
+              const int p = pi * BITS;
+              const uint32_t mask = (m << p) | (m << (p + 16));
+              const half2_t cv = as_half2((src & mask) | magic) + nz[pi];
+              const int ci = (hf * 8 + p) / BITS;            // code index in the word
+              dp[pi] = __builtin_amdgcn_fdot2(cv, as_half2(xv.w[wi * (P / 2) + ci]), dp[pi],
+                                              false);
             }
           }
-          float d = dp[0];
-#pragma unroll
-          for (int pi = 1; pi < G::NPOS; ++pi) d = fmaf(dp[pi], ldexpf(1.0f, -pi * BITS), d);
-          const float t = fmaf(d, f * sc, acc);
-          acc = live ? t : acc;
-          issue(s, j + D);
         }
+        float d = dp[0];
+#pragma unroll
+        for (int pi = 1; pi < G::NPOS; ++pi) d = fmaf(dp[pi], ldexpf(1.0f, -pi * BITS), d);
+        const float t = fmaf(d, xv.f * sc, acc);
+        if (masked) {
+          const int c = c_lo + j * CPL + cl;
+          const int b = (((c_lo + j * CPL) * TKC) >> log2_bs) + lane_db;
+          acc = (c < c_hi && b < kb) ? t : acc;
+        } else {
+          acc = t;
+        }
+      };
+      // Steady state: each consumed slot is refilled with the load D ahead.
+      // Only the last load of a share can hold dead lanes, and it is always
+      // among the last D, which are consumed masked and without refills (a
+      // dead load would still cost an address-unit pass).
+      // 2-bit units hold 64 activations: without the look-ahead, to stay
+      // within 128 registers.
+      constexpr bool AHEAD = BITS != 2;
+      XV xa, xb;
+      if constexpr (AHEAD) fetch(xa, 0);
+      int j0 = 0;
+      for (; j0 + D < nloads; j0 += D) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+          XV& cur = (q & 1) ? xb : xa;
+          XV& nxt = (q & 1) ? xa : xb;
+          if constexpr (AHEAD) fetch(nxt, j0 + q + 1);
+          else fetch(cur, j0 + q);
+          compute(sl[q], cur, j0 + q, false);
+          issue(sl[q], j0 + q + D);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < D; ++q) {
+        XV& cur = (q & 1) ? xb : xa;
+        XV& nxt = (q & 1) ? xa : xb;
+        if constexpr (AHEAD) {
+          if (q + 1 < D) fetch(nxt, j0 + q + 1);
+        } else {
+          fetch(cur, j0 + q);
+        }
+        compute(sl[q], cur, j0 + q, true);
       }
     } else {
       // Exact fp32 path: every code times the activation read from memory.
       for (int j = 0; j < nloads; ++j) {
-        const int c = chunk_of(j);
-        const bool live = live_of(c);
-        const int off = live ? ((g * chunks + c) * TG + gcol) * CB + u * 16 : OFF_NONE;
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
-        const int b = (c * TKC + u * E) >> log2_bs;
-        const int si = (g * kb + b) * TG + gcol;
-        const int soff = live ? si * (int)sizeof(ST) : OFF_NONE;
-        float s;
-        if constexpr (sizeof(ST) == 4)
-          s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
-        else
-          s = bits16_to_f32<SDT>(__builtin_amdgcn_raw_buffer_load_b16(rs, soff, 0, 0));
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, 0);
+        const int ub = (g * kb + (((c_lo + j * CPL) * TKC) >> log2_bs)) * TG;
+        const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(rs, ub * SZ + lane_soff, 0, 0);
+        float sc;
+        if constexpr (SZ == 4) sc = __uint_as_float(sw);
+        else sc = bits16_to_f32<SDT>((uint16_t)(sw >> lane_shalf));
         int z = 1 << (BITS - 1);
         if constexpr (HAS_ZP)
-          z = (int)((__builtin_amdgcn_raw_buffer_load_b8(rz, live ? (si * BITS) >> 3 : OFF_NONE,
-                                                         0, 0) >> ((si * BITS) & 7)) & m);
+          z = (int)((__builtin_amdgcn_raw_buffer_load_b32(rz, ub * BITS / 8 + lane_zoff, 0, 0) >>
+                     lane_zbit) & m);
         const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
+        const int c = c_lo + j * CPL + cl;
         const int k0 = c * TKC + u * E;
         float d = 0.0f;
 #pragma unroll
@@ -331,10 +396,13 @@ __global__ __launch_bounds__(TGV_THREADS) void gemv_tiled_kernel(
             d = fmaf(xk, (float)(q - z), d);
           }
         }
-        const float t = fmaf(d, s, acc);
-        acc = live ? t : acc;
+        const int b = (((c_lo + j * CPL) * TKC) >> log2_bs) + lane_db;
+        const float t = fmaf(d, sc, acc);
+        acc = (c < c_hi && b < kb) ? t : acc;
       }
     }
+    // The next piece overwrites the staged activations.
+    if (P0 + pc < chunks) __syncthreads();
   }
 
   // Lanes of one column: the UPC units of a chunk, then the CPL chunks.
@@ -342,49 +410,52 @@ __global__ __launch_bounds__(TGV_THREADS) void gemv_tiled_kernel(
   if constexpr (UPC >= 4) acc += __shfl_xor(acc, 2);
 #pragma unroll
   for (int st = LPC; st < 64; st *= 2) acc += __shfl_xor(acc, st);
-  if (lane < LPC && u == 0) red[wave * CW + col] = acc;
-  __syncthreads();
-  if (threadIdx.x < CW) {
-    const int n = g * TG + col0 + threadIdx.x;
-    if (n < N) {
-      float o = red[threadIdx.x];
-#pragma unroll
-      for (int w = 1; w < TGV_WAVES; ++w) o += red[w * CW + threadIdx.x];
+  const bool writer = lane < LPC && u == 0;
+  const int n = g * TG + gcol;
+  if (S == 1) {
+    if (writer && has_oct && n < N) {
+      float o = acc;
+      if (bias) o += bits16_to_f32<XDT>(bias[n]);
+      y[n] = __builtin_bit_cast(uint16_t, dt<XDT>::from_f32(o));
+    }
+  } else {
+    if (writer) red[wave * OCT + col] = acc;
+    __syncthreads();
+    if (s == 0 && writer && has_oct && n < N) {
+      float o = red[ol * OCT + col];
+      for (int t = 1; t < S; ++t) o += red[(t * O + ol) * OCT + col];
       if (bias) o += bits16_to_f32<XDT>(bias[n]);
       y[n] = __builtin_bit_cast(uint16_t, dt<XDT>::from_f32(o));
     }
   }
 }
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int CW>
-hipError_t launch_cw(const MatArgs& a, const TiledGeom& tg) {
-  using G = TGeom<BITS, CW>;
-  constexpr int D = (BITS == 8) ? 8 : 8;
-  const int chunks = (int)tg.chunks;
-  // Chunks per wave: a whole number of wave loads.
-  const int per_wave = (chunks + TGV_WAVES * G::CPL - 1) / (TGV_WAVES * G::CPL) * G::CPL;
-  const int pc = std::min(per_wave, TGV_PIECE);
-  const int region = pc * 32 + (pc * (64 / G::E) + 3) / 4 * 4;
-  const size_t lds = (size_t)(TGV_WAVES * region + TGV_WAVES * CW) * 4;
-  const int grid = (int)tg.groups * (32 / CW);
-  const uint8_t* codes = a.B + tg.codes_off;
-  hipLaunchKernelGGL((gemv_tiled_kernel<BITS, XDT, SDT, HAS_ZP, CW, D>), dim3(grid),
-                     dim3(TGV_THREADS), lds, a.stream, (const uint16_t*)a.A, codes,
-                     (const typename dt<SDT>::T*)a.scales, a.zp, (const uint16_t*)a.bias,
-                     (uint16_t*)a.Y, (int)a.K, (int)a.N, (int)a.kb, chunks,
-                     __builtin_ctz((unsigned)a.block_size), per_wave, pc);
-  return hipGetLastError();
-}
-
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 hipError_t launch_z(const MatArgs& a, const TiledGeom& tg) {
-  // Columns per workgroup: enough workgroups to cover the 256 compute units
-  // about twice.
-  const int64_t groups = tg.groups;
-  if constexpr (BITS != 8)
-    if (groups >= 256) return launch_cw<BITS, XDT, SDT, HAS_ZP, 32>(a, tg);
-  if (groups >= 128) return launch_cw<BITS, XDT, SDT, HAS_ZP, 16>(a, tg);
-  return launch_cw<BITS, XDT, SDT, HAS_ZP, 8>(a, tg);
+  using G = TGeom<BITS>;
+  // Loads in flight per wave (2-bit units hold 64 activations: fewer slots
+  // keep the kernel within 128 registers).
+  constexpr int D = (BITS == 2) ? 2 : 4;
+  const int chunks = (int)tg.chunks;
+  const int n_oct = (int)tg.groups * (TG / OCT);
+  // Octets per workgroup: one workgroup per compute unit where there are
+  // enough octets; then shares of K until a workgroup has 8 waves (two per
+  // SIMD), keeping at least two wave loads per share.
+  const int O = std::min(MAX_WAVES, std::max(1, (n_oct + 255) / 256));
+  int S = 1;
+  while (O * S * 2 <= MAX_WAVES && O * S < 4 && chunks >= 2 * (2 * S) * G::CPL) S *= 2;
+  const int pc = std::min(chunks, PIECE_CHUNKS);
+  const TLds<BITS> L(pc, O * S);
+  const size_t lds = (size_t)L.total * 4;
+  const int grid = (n_oct + O - 1) / O;
+  const bool linb = a.block_size <= TKC * G::CPL;
+  auto kern = linb ? gemv_tiled_kernel<BITS, XDT, SDT, HAS_ZP, D, true>
+                   : gemv_tiled_kernel<BITS, XDT, SDT, HAS_ZP, D, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(O * S * 64), lds, a.stream, (const uint16_t*)a.A,
+                     a.B + tg.codes_off, (const uint8_t*)a.scales, a.zp, (const uint16_t*)a.bias,
+                     (uint16_t*)a.Y, (int)a.K, (int)a.N, (int)a.kb, chunks,
+                     __builtin_ctz((unsigned)a.block_size), n_oct, O, S, pc);
+  return hipGetLastError();
 }
 
 template <int BITS, int XDT, int SDT>
@@ -410,12 +481,13 @@ hipError_t launch_b(const MatArgs& a, const TiledGeom& tg) {
 
 bool gemv_tiled_supported(const MatArgs& a) {
   // 16-bit activations, and blocks no shorter than a 16-byte unit of codes
-  // (one scale per unit); 32-bit offsets.
+  // (one scale per unit); 32-bit offsets with room for a few wave loads past
+  // the end.
   const int E = 128 / a.bits;
   if (a.a_dtype == DT_F32 || a.block_size < E) return false;
   const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
                                   a.zp != nullptr);
-  return tg.total < 0x7FFFFF00LL && a.K < (1 << 28);
+  return tg.total + 16 * 4096 < 0x7FFFFF00LL && a.K < (1 << 28);
 }
 
 hipError_t launch_gemv_tiled(const MatArgs& a) {
