@@ -27,6 +27,26 @@ import torch
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 POOL_BYTES = 640 << 20         # rotating weight pool, > 2x the Infinity Cache
+COPY_CAL_BYTES = 256 << 20     # plain copy used to scale the HBM byte counters
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "gemv_tiled_K4096_N14336_traffic.txt")
+KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                             "block_quantized_weight_matmulnbits_amd", "csrc", "gemv_tiled.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when the kernel source has changed since it was taken."""
+    import hashlib
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
+                      if ":" in line and not line.startswith("#"))
+        src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != src_hash:
+            return None
+        return int(float(fields["hbm_bytes_per_launch"].strip()))
+    except (OSError, KeyError, ValueError):
+        return None
 
 METRIC = "int4 GEMV weight GB/s (% HBM peak) at M=1; GEMM TFLOPS (% MFMA) at M=2048"
 
@@ -38,6 +58,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run a plain 256 MiB device copy (the reference kernel for "
+                        "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
     return p.parse_args()
@@ -61,6 +84,13 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cases = decode_layer()
     step_bytes = sum(layer_bytes(c) for c in cases)
     n_copies = max(2, -(-POOL_BYTES // step_bytes))
@@ -155,7 +185,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(dom_avg_ms * 1e3, 3),
             "bytes_per_launch": dom_bytes,
         },
