@@ -1,0 +1,329 @@
+// compint8_tiled.hip -- CompInt8 (accuracy_level 4) on the tiled weight
+// layout (qmm_layout.h) with the int8 matrix cores of gfx950.
+//
+// Definition (onnx-runtime-ep-cpu matmul_nbits.rs: quantize_activation_signed,
+// int4_dot_row_scalar, int8_row): with qa / sa the int8 activations and their
+// per-block scales written by quantize_a_kernel,
+//   dot[m, n, b] = sum_{k in b} qa[m, k] * (code(n, k) - zp(n, b))   (int32)
+//   y[m, n]      = sum_b float(dot) * (sa[m, b] * scale[n, b]) (+ bias[n]).
+//
+// One v_mfma_i32_16x16x64_i8 multiplies 16 activation rows (M padded with
+// zero rows) by 16 weight columns over one 64-code chunk: lane l holds 16
+// int8 of row / column l % 16 for reduction indices 16 * (l / 16) + [0, 16).
+// The codes enter raw (0 <= code < 2^bits; 8-bit codes as code - 128) and the
+// zero point is applied per block through the identity
+//   sum qa * (code - zp) = sum qa * code' - (zp - off) * sum qa,
+// off = 0 (2/4-bit) or 128 (8-bit, code' = code - 128), with sum qa taken by a
+// second MFMA against an all-ones operand; all of it is exact int32.  The
+// codes' unpacking leaves them in a fixed order inside each lane's 16 bytes
+// (nibble or crumb planes); the activation bytes are permuted the same way
+// with v_perm_b32, so products pair correctly.
+//
+// Work split: a wave owns a slice of 16 columns (half a 32-column group) and
+// a share of the blocks of K; a workgroup holds CS slices x S shares and adds
+// the shares through LDS.  Each chunk costs the wave one load of its codes
+// (the 16 columns' bytes of a chunk are 8 * BITS * 16 contiguous bytes) and
+// one 16-byte load of activations per lane (rows past M read zeros from past
+// the buffer's extent), then two MFMAs.
+#include "qmm_device.h"
+#include "qmm_internal.h"
+#include "qmm_layout.h"
+
+#include <algorithm>
+
+namespace qmm {
+
+namespace {
+
+constexpr int RSRC3 = 0x00020000;
+constexpr int CT_D = 4;            // chunks in flight per wave
+constexpr int CT_MAXW = 16;
+
+template <int BITS>
+struct CtGeom {
+  static constexpr int CB = TKC * BITS / 8;     // bytes per column chunk
+  static constexpr int LB = CB / 4;             // code bytes per lane per chunk (16 codes)
+};
+
+// The lane's 16 codes as four words of int8, in plane order (see unpack).
+template <int BITS>
+__device__ __forceinline__ i32x4 unpack_codes(const u32x4& raw) {
+  if constexpr (BITS == 4) {
+    // 8 bytes, code 2j in the low nibble of byte j: planes of even and odd
+    // codes of each 4-byte word.
+    const uint32_t w0 = raw.x, w1 = raw.y;
+    return i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                 (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+  } else if constexpr (BITS == 2) {
+    // 4 bytes, code 4j + i at bits 2i of byte j: plane i holds codes i, 4 + i,
+    // 8 + i, 12 + i.
+    const uint32_t w = raw.x;
+    return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                 (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+  } else {
+    // 16 bytes in order, as code - 128.
+    return i32x4{(int)(raw.x ^ 0x80808080u), (int)(raw.y ^ 0x80808080u),
+                 (int)(raw.z ^ 0x80808080u), (int)(raw.w ^ 0x80808080u)};
+  }
+}
+
+// The lane's 16 activation bytes (natural order) permuted into the codes'
+// plane order.  __builtin_amdgcn_perm(hi, lo, sel): selector byte values 0-3
+// pick bytes of lo, 4-7 bytes of hi.
+template <int BITS>
+__device__ __forceinline__ i32x4 permute_acts(const u32x4& a) {
+  if constexpr (BITS == 4) {
+    return i32x4{(int)__builtin_amdgcn_perm(a.y, a.x, 0x06040200u),
+                 (int)__builtin_amdgcn_perm(a.y, a.x, 0x07050301u),
+                 (int)__builtin_amdgcn_perm(a.w, a.z, 0x06040200u),
+                 (int)__builtin_amdgcn_perm(a.w, a.z, 0x07050301u)};
+  } else if constexpr (BITS == 2) {
+    // Plane i = bytes (i, 4 + i, 8 + i, 12 + i): byte i of each word.
+    const uint32_t p01[2] = {__builtin_amdgcn_perm(a.y, a.x, 0x05010400u),   // x0 y0 x1 y1
+                             __builtin_amdgcn_perm(a.y, a.x, 0x07030602u)};  // x2 y2 x3 y3
+    const uint32_t p23[2] = {__builtin_amdgcn_perm(a.w, a.z, 0x05010400u),
+                             __builtin_amdgcn_perm(a.w, a.z, 0x07030602u)};
+    return i32x4{(int)__builtin_amdgcn_perm(p23[0], p01[0], 0x05040100u),   // x0 y0 z0 w0
+                 (int)__builtin_amdgcn_perm(p23[0], p01[0], 0x07060302u),   // x1 y1 z1 w1
+                 (int)__builtin_amdgcn_perm(p23[1], p01[1], 0x05040100u),
+                 (int)__builtin_amdgcn_perm(p23[1], p01[1], 0x07060302u)};
+  } else {
+    return i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  }
+}
+
+// One chunk in flight: the lane's code bytes (LB of them used), its 16
+// activation bytes, and the aligned 32-bit words holding the scale and zero
+// point of the chunk's block (loaded with every chunk so that no load sits
+// inside the block-end branch).
+struct CtSlot {
+  u32x4 code;
+  u32x4 act;
+  uint32_t sw, zw;
+};
+
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS>
+__global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
+    const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
+    const typename dt<YDT>::T* __restrict__ bias, typename dt<YDT>::T* __restrict__ Y,
+    int32_t* __restrict__ dots, int Mp, int N, int kb, int Kp, int chunks, int log2_cpb,
+    int n_slices, int CS, int S) {
+  using G = CtGeom<BITS>;
+  using ST = typename dt<SDT>::T;
+  constexpr int CB = G::CB, LB = G::LB;
+  constexpr int SZ = (int)sizeof(ST);
+  constexpr uint32_t m = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+  constexpr int OFF = (BITS == 8) ? 128 : 0;
+
+  extern __shared__ float smem_ct[];
+  float* saT = smem_ct;                         // [kb][16]: sa of row r, block b (0 past Mp)
+  float* red = smem_ct + kb * 16;               // [W][16 x 16] partial sums
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = CS * S;
+  const int cs = wave % CS, s = wave / CS;
+  const int slice = blockIdx.x * CS + cs;
+  const bool has_slice = slice < n_slices;
+  const int grp = slice >> 1;
+  const int col = (slice & 1) * 16 + (lane & 15);   // column within the group
+  const int n = grp * TG + col;
+  const int g = lane >> 4;                          // 16 reduction indices of the 64
+  const int rowA = lane & 15;                       // activation row of this lane (A)
+
+  for (int i = threadIdx.x; i < kb * 16; i += blockDim.x) {
+    const int b = i >> 4, r = i & 15;
+    saT[i] = r < Mp ? sa[r * kb + b] : 0.0f;
+  }
+
+  const int groups = (N + TG - 1) / TG;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)codes, 0, groups * chunks * TG * CB, RSRC3);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)qa, 0, Mp * Kp, RSRC3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)scales, 0, groups * kb * TG * SZ, RSRC3);
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)zps, 0, HAS_ZP ? groups * kb * TG * BITS / 8 : 0, RSRC3);
+  // Blocks of this wave's share (whole blocks, so no block is split).
+  const int bps = (kb + S - 1) / S;
+  const int b_lo = s * bps;
+  const int b_hi = has_slice ? min(kb, b_lo + bps) : b_lo;
+  const int cpb = 1 << log2_cpb;                    // chunks per block
+  const int c_lo = b_lo * cpb;
+  const int nch = max(0, (b_hi - b_lo) * cpb);
+
+  const int lane_code = (grp * chunks * TG + col) * CB + g * LB;
+  const int lane_act = rowA * Kp + g * 16;
+  auto issue = [&](CtSlot& sl, int j) {
+    const int c = c_lo + j;
+    if constexpr (LB == 16)
+      sl.code = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + c * (TG * CB), 0, 0);
+    else if constexpr (LB == 8) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane_code + c * (TG * CB), 0, 0);
+      sl.code = u32x4{v.x, v.y, 0u, 0u};
+    } else {
+      sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * (TG * CB), 0, 0),
+                      0u, 0u, 0u};
+    }
+    sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);
+    const int si = (grp * kb + (c >> log2_cpb)) * TG + col;
+    sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (si * SZ) & ~3, 0, 0);
+    if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, ((si * BITS) >> 5) * 4, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  CtSlot sl[CT_D];
+#pragma unroll
+  for (int q = 0; q < CT_D; ++q) issue(sl[q], q);
+  __syncthreads();   // saT staged
+
+  const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+  i32x4 acc = {0, 0, 0, 0}, asum = {0, 0, 0, 0};
+  // Chunk j: two MFMAs; at the block's last chunk the epilogue scales it.
+  auto consume = [&](const CtSlot& sl, int j) {
+    const i32x4 bv = unpack_codes<BITS>(sl.code);
+    const i32x4 av = permute_acts<BITS>(sl.act);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+    asum = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones, asum, 0, 0, 0);
+    if (((j + 1) & (cpb - 1)) == 0) {
+      const int b = b_lo + (j >> log2_cpb);
+      const int si = (grp * kb + b) * TG + col;
+      float sc;
+      if constexpr (SZ == 4) sc = __uint_as_float(sl.sw);
+      else sc = bits16_to_f32<SDT>((uint16_t)(sl.sw >> ((si & 1) * 16)));
+      int z = 1 << (BITS - 1);
+      if constexpr (HAS_ZP) z = (int)((sl.zw >> ((si * BITS) & 31)) & m);
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(saT + b * 16 + 4 * g);
+      const int zo = z - OFF;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = acc[e] - zo * asum[e];
+        if constexpr (DOTS) {
+          const int r = 4 * g + e;
+          if (r < Mp && n < N) dots[((int64_t)r * N + n) * kb + b] = d;
+        }
+        y[e] = fmaf((float)d, s4[e] * sc, y[e]);
+      }
+      acc = i32x4{0, 0, 0, 0};
+      asum = i32x4{0, 0, 0, 0};
+    }
+  };
+  int j0 = 0;
+  for (; j0 + CT_D < nch; j0 += CT_D) {
+#pragma unroll
+    for (int q = 0; q < CT_D; ++q) {
+      consume(sl[q], j0 + q);
+      issue(sl[q], j0 + q + CT_D);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < CT_D; ++q)
+    if (j0 + q < nch) consume(sl[q], j0 + q);
+
+  if constexpr (!DOTS) {
+    // Lane l holds rows 4 * (l / 16) + e of column l % 16.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave * 256 + (4 * g + e) * 16 + (lane & 15)] = y[e];
+    __syncthreads();
+    if (s == 0 && has_slice) {
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float o = red[cs * 256 + r * 16 + (lane & 15)];
+        for (int t = 1; t < S; ++t) o += red[(t * CS + cs) * 256 + r * 16 + (lane & 15)];
+        if (r < Mp && n < N) {
+          if (bias) o += dt<YDT>::to_f32(bias[n]);
+          Y[(int64_t)r * N + n] = dt<YDT>::from_f32(o);
+        }
+      }
+    }
+  }
+  (void)W;
+}
+
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS>
+hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
+  const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
+                                  a.zp != nullptr);
+  const int chunks = (int)tg.chunks;
+  const int log2_cpb = __builtin_ctz((unsigned)(a.block_size / TKC));
+  const int n_slices = (int)tg.groups * 2;
+  const int Kp = (int)(a.kb * a.block_size);
+  // Two slices (one group) per workgroup, shares of K until a workgroup has
+  // 8 waves, keeping at least two blocks per share.
+  const int CS = 2;
+  int S = 1;
+  while (CS * S < 8 && (a.kb + 2 * S - 1) / (2 * S) >= 2) S *= 2;
+  const size_t lds = (size_t)(a.kb * 16 + CS * S * 256) * 4;
+  const int grid = (n_slices + CS - 1) / CS;
+  using YT = typename dt<YDT>::T;
+  for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+    const int Mp = (int)std::min<int64_t>(16, a.M - m0);
+    hipLaunchKernelGGL((compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS>), dim3(grid),
+                       dim3(CS * S * 64), lds, a.stream, qa + m0 * Kp, sa + m0 * a.kb,
+                       a.B + tg.codes_off, (const uint8_t*)a.scales, a.zp, (const YT*)a.bias,
+                       DOTS ? nullptr : (YT*)a.Y + m0 * a.N,
+                       DOTS ? dots + m0 * a.N * a.kb : nullptr, Mp, (int)a.N, (int)a.kb, Kp,
+                       chunks, log2_cpb, n_slices, CS, S);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int BITS, int SDT, int YDT, bool DOTS>
+hipError_t launch_z(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
+  return a.zp ? launch_t<BITS, SDT, YDT, true, DOTS>(a, qa, sa, dots)
+              : launch_t<BITS, SDT, YDT, false, DOTS>(a, qa, sa, dots);
+}
+
+template <int BITS, int SDT, bool DOTS>
+hipError_t launch_y(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
+  switch (a.a_dtype) {
+    case DT_F32: return launch_z<BITS, SDT, DT_F32, DOTS>(a, qa, sa, dots);
+    case DT_F16: return launch_z<BITS, SDT, DT_F16, DOTS>(a, qa, sa, dots);
+    default: return launch_z<BITS, SDT, DT_BF16, DOTS>(a, qa, sa, dots);
+  }
+}
+
+template <int BITS, bool DOTS>
+hipError_t launch_s(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
+  switch (a.s_dtype) {
+    case DT_F32: return launch_y<BITS, DT_F32, DOTS>(a, qa, sa, dots);
+    case DT_F16: return launch_y<BITS, DT_F16, DOTS>(a, qa, sa, dots);
+    default: return launch_y<BITS, DT_BF16, DOTS>(a, qa, sa, dots);
+  }
+}
+
+template <bool DOTS>
+hipError_t launch_b(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
+  switch (a.bits) {
+    case 2: return launch_s<2, DOTS>(a, qa, sa, dots);
+    case 4: return launch_s<4, DOTS>(a, qa, sa, dots);
+    default: return launch_s<8, DOTS>(a, qa, sa, dots);
+  }
+}
+
+}  // namespace
+
+bool compint8_tiled_supported(const MatArgs& a) {
+  // Whole blocks of 64-code chunks; LDS for the activation scales; 32-bit
+  // offsets.
+  const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
+                                  a.zp != nullptr);
+  return a.block_size >= TKC && (a.kb * 16 + 8 * 256) * 4 <= 64 * 1024 &&
+         tg.total < 0x7FFFFF00LL && 16 * a.kb * a.block_size < 0x7FFFFF00LL;
+}
+
+hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa) {
+  return launch_b<false>(a, qa, sa, nullptr);
+}
+
+hipError_t launch_compint8_tiled_dots(const MatArgs& a, const int8_t* qa, const float* sa,
+                                      int32_t* dots) {
+  return launch_b<true>(a, qa, sa, dots);
+}
+
+}  // namespace qmm

@@ -219,9 +219,11 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
                            s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
                            accuracy_level, &a);
   if (st != QMM_OK) return st;
-  if (a.tiled)
-    return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8: the tiled layout is not supported by "
-                "the CompInt8 kernels. How to fix: pass the operator's layout (QMM_LAYOUT_ORT).");
+  if (a.tiled && !qmm::compint8_tiled_supported(a))
+    return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8: on the tiled layout CompInt8 needs "
+                "block_size >= 64 (whole 64-code chunks per block) and at most 896 blocks per "
+                "row (got block_size=%d, %lld blocks). How to fix: pass the operator's layout "
+                "(QMM_LAYOUT_ORT) for this weight.", block_size, (long long)a.kb);
   if (M == 0) return QMM_OK;
   st = check_workspace("qmm_gemm_compint8", a, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
@@ -229,7 +231,8 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
   int8_t* qa = (int8_t*)workspace;
   float* sa = (float*)((char*)workspace + qmm::ws_qa_bytes(a.M, a.kb, a.block_size));
   hipError_t e = qmm::launch_quantize_a(a, qa, sa);
-  if (e == hipSuccess) e = qmm::launch_compint8(a, qa, sa);
+  if (e == hipSuccess)
+    e = a.tiled ? qmm::launch_compint8_tiled(a, qa, sa) : qmm::launch_compint8(a, qa, sa);
   return hip_status(e, "qmm_gemm_compint8");
 }
 
@@ -360,20 +363,24 @@ int qmm_debug_quantize_a(const void* A, int a_dtype, int64_t M, int64_t K, int b
 }
 
 int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, int b_layout,
-                                  const uint8_t* zero_points, int64_t M, int64_t K, int64_t N,
-                                  int block_size, int bits, int32_t* dots, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  int s_dtype, const uint8_t* zero_points, int64_t M, int64_t K,
+                                  int64_t N, int block_size, int bits, int32_t* dots,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (dots == nullptr)
     return fail(QMM_ERR_INVALID_ARG, "qmm_debug_compint8_block_dots: dots must be non-null.");
   MatArgs a;
+  const bool tiled = b_layout == QMM_LAYOUT_TILED || b_layout == QMM_LAYOUT_TILED_ZP;
   int st = validate_matmul("qmm_debug_compint8_block_dots", Route::CompInt8, A, a_dtype, B,
-                           b_layout, B, QMM_F32, zero_points, nullptr, (void*)dots, M, K, N,
-                           block_size, bits, 4, &a);
+                           b_layout, tiled ? nullptr : B, tiled ? s_dtype : QMM_F32, zero_points,
+                           nullptr, (void*)dots, M, K, N, block_size, bits, 4, &a);
   if (st != QMM_OK) return st;
+  if (a.tiled && !qmm::compint8_tiled_supported(a))
+    return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_compint8_block_dots: on the tiled layout "
+                "CompInt8 needs block_size >= 64. How to fix: pass the operator's layout.");
   if (M == 0) return QMM_OK;
   st = check_workspace("qmm_debug_compint8_block_dots", a, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
-  a.scales = nullptr;   // the block dots need no scales
+  if (!a.tiled) a.scales = nullptr;   // the block dots need no scales
   a.Y = nullptr;
   a.stream = (hipStream_t)stream;
   int8_t* qa = (int8_t*)workspace;
@@ -381,7 +388,9 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
   hipError_t e = qmm::launch_quantize_a(a, qa, sa);
   if (e == hipSuccess)
     e = hipMemsetAsync(dots, 0, (size_t)(a.M * a.N * a.kb) * sizeof(int32_t), a.stream);
-  if (e == hipSuccess) e = qmm::launch_compint8_dots(a, qa, sa, dots);
+  if (e == hipSuccess)
+    e = a.tiled ? qmm::launch_compint8_tiled_dots(a, qa, sa, dots)
+                : qmm::launch_compint8_dots(a, qa, sa, dots);
   return hip_status(e, "qmm_debug_compint8_block_dots");
 }
 

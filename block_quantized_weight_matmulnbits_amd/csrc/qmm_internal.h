@@ -45,6 +45,11 @@ hipError_t launch_gemm(const MatArgs& a);
 hipError_t launch_quantize_a(const MatArgs& a, int8_t* qa, float* sa);
 hipError_t launch_compint8(const MatArgs& a, const int8_t* qa, const float* sa);
 hipError_t launch_compint8_dots(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots);
+// CompInt8 on the tiled layout with int8 MFMA (compint8_tiled.hip).
+bool compint8_tiled_supported(const MatArgs& a);
+hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa);
+hipError_t launch_compint8_tiled_dots(const MatArgs& a, const int8_t* qa, const float* sa,
+                                      int32_t* dots);
 
 // int8 convolution (validated NHWC / OHWI problem).
 struct ConvArgs {

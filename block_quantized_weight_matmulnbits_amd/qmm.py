@@ -44,8 +44,8 @@ _SIGS = {
     "qmm_unrepack": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "qmm_debug_unpack": ([_vp, _i32, _vp, _i32, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "qmm_debug_quantize_a": ([_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp], _i32),
-    "qmm_debug_compint8_block_dots": ([_vp, _i32, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
-                                       _sz, _vp], _i32),
+    "qmm_debug_compint8_block_dots": ([_vp, _i32, _vp, _i32, _i32, _vp, _i64, _i64, _i64, _i32, _i32,
+                                       _vp, _vp, _sz, _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -146,10 +146,11 @@ def qmm_compint8_workspace_size(M, K, block_size) -> int:
 
 def qmm_gemm_compint8(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, workspace,
                       accuracy_level=4, stream=None):
-    _check(lib.qmm_gemm_compint8(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales),
-                                 _dt(scales), _ptr(zero_points), _ptr(bias), _ptr(Y), M, K, N,
-                                 block_size, bits, accuracy_level, _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    b, layout, s, sdt = _weights(B, scales)
+    _check(lib.qmm_gemm_compint8(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
+                                 _ptr(Y), M, K, N, block_size, bits, accuracy_level,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
 
 
 def qconv_int8(X, W, bias, w_scale, in_scale, out_scale, in_zp, out_zp, clamp_min, clamp_max,
@@ -175,8 +176,12 @@ def qmm_debug_quantize_a(A, M, K, block_size, qa, sa, stream=None):
 
 def qmm_debug_compint8_block_dots(A, B, zero_points, M, K, N, block_size, bits, dots, workspace,
                                   stream=None):
-    _check(lib.qmm_debug_compint8_block_dots(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT,
-                                             _ptr(zero_points), M, K, N, block_size, bits,
-                                             _ptr(dots), _ptr(workspace),
+    if isinstance(B, Repacked):
+        b, layout, sdt = B.buf.data_ptr(), B.layout, B.s_dtype
+    else:
+        b, layout, sdt = _ptr(B), QMM_LAYOUT_ORT, QMM_F32
+    _check(lib.qmm_debug_compint8_block_dots(_ptr(A), _dt(A), b, layout, sdt, _ptr(zero_points),
+                                             M, K, N, block_size, bits, _ptr(dots),
+                                             _ptr(workspace),
                                              workspace.numel() * workspace.element_size(),
                                              _stream(stream)))

@@ -109,7 +109,9 @@ int qmm_gemm(const void *A, int a_dtype, const uint8_t *B, int b_layout,
  * (+ bias[n]) in fp32.
  * workspace: device memory of at least qmm_compint8_workspace_size(M, K,
  * block_size) bytes, 256-byte aligned, owned by the caller, overwritten.
- * accuracy_level must be 4.  Arguments otherwise as for qmm_gemm.
+ * accuracy_level must be 4.  Arguments otherwise as for qmm_gemm.  B may be
+ * the tiled buffer of qmm_repack when block_size >= 64 (the block dots then
+ * run on the int8 matrix cores); otherwise QMM_ERR_UNSUPPORTED.
  */
 size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size);
 
@@ -177,7 +179,8 @@ int qmm_unrepack(const void *tiled, int has_zero_points, int64_t K, int64_t N, i
  *  qmm_debug_quantize_a: qa [M, kb*block_size] int8 (zero past K), sa [M, kb]
  *    float32, exactly as the first step of qmm_gemm_compint8.
  *  qmm_debug_compint8_block_dots: dots [M, N, kb] int32 as computed inside
- *    qmm_gemm_compint8 (same workspace contract).
+ *    qmm_gemm_compint8 (same workspace contract).  s_dtype matters only for
+ *    a tiled B (it locates the zero-point region); scales are not read.
  */
 int qmm_debug_unpack(const uint8_t *B, int b_layout, const void *scales,
                      int s_dtype, const uint8_t *zero_points, int64_t K,
@@ -188,7 +191,8 @@ int qmm_debug_quantize_a(const void *A, int a_dtype, int64_t M, int64_t K,
                          int block_size, int8_t *qa, float *sa, void *stream);
 
 int qmm_debug_compint8_block_dots(const void *A, int a_dtype, const uint8_t *B,
-                                  int b_layout, const uint8_t *zero_points,
+                                  int b_layout, int s_dtype,
+                                  const uint8_t *zero_points,
                                   int64_t M, int64_t K, int64_t N,
                                   int block_size, int bits, int32_t *dots,
                                   void *workspace, size_t workspace_bytes,

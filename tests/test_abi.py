@@ -149,7 +149,7 @@ def test_repack_rejects_bad_arguments(qmm):
     assert st == -1 and "zero_points" in qmm.qmm_last_error()
 
 
-def test_compint8_rejects_tiled_layout(qmm):
-    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, FAKE, 4, 4096, 4096, 128,
+def test_compint8_tiled_layout_needs_whole_chunks_per_block(qmm):
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, FAKE, 4, 4096, 4096, 32,
                                    4, 4, FAKE, 1 << 30, None)
-    assert st == -2 and "tiled" in qmm.qmm_last_error()
+    assert st == -2 and "block_size >= 64" in qmm.qmm_last_error()

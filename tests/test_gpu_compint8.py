@@ -6,7 +6,9 @@ and the int32 block dots computed by the production kernel
 against the oracle's CompInt8 value.  Shapes: small ragged ones for every
 (bits, block size, dtype, zero point) and the full batched-decode workload
 (M in {1, 4, 16}, K = 4096, N = 14336; bits 4 / bs 128 symmetric, bits 8 /
-bs 64 and bits 2 / bs 64 asymmetric).
+bs 64 and bits 2 / bs 64 asymmetric).  Every test runs on the operator's
+layout and on the tiled layout of qmm_repack (int8 matrix-core kernel);
+on the tiled layout blocks shorter than 64 codes must be rejected.
 """
 import numpy as np
 import pytest
@@ -17,6 +19,22 @@ from tests.util import TOL, assert_within, f64, u8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+LAYOUT = {"v": "ort"}
+
+
+@pytest.fixture(params=["ort", "tiled"], autouse=True)
+def layout(request):
+    LAYOUT["v"] = request.param
+    yield request.param
+
+
+def weights(case, c):
+    """(B, scales, zero_points) of the case on the current layout."""
+    if LAYOUT["v"] == "tiled":
+        t = qmm().qmm_repack(c.B, c.scales, c.zero_points, case.K, case.N, case.block_size,
+                             case.bits)
+        return t, None, None
+    return c.B, c.scales, c.zero_points
 
 
 def qmm():
@@ -46,7 +64,8 @@ def gpu_quant(case):
 def gpu_dots(case):
     c = case.to(DEV)
     dots = torch.empty(case.M, case.N, case.k_blocks, dtype=torch.int32, device=DEV)
-    qmm().qmm_debug_compint8_block_dots(c.A, c.B, c.zero_points, case.M, case.K, case.N,
+    B, _, Z = weights(case, c)
+    qmm().qmm_debug_compint8_block_dots(c.A, B, Z, case.M, case.K, case.N,
                                         case.block_size, case.bits, dots,
                                         workspace(case.M, case.K, case.block_size))
     torch.cuda.synchronize()
@@ -56,19 +75,25 @@ def gpu_dots(case):
 def gpu_matmul(case):
     c = case.to(DEV)
     Y = torch.empty(case.M, case.N, dtype=c.A.dtype, device=DEV)
-    qmm().qmm_gemm_compint8(c.A, c.B, c.scales, c.zero_points, c.bias, Y, case.M, case.K, case.N,
+    B, S, Z = weights(case, c)
+    qmm().qmm_gemm_compint8(c.A, B, S, Z, c.bias, Y, case.M, case.K, case.N,
                             case.block_size, case.bits, workspace(case.M, case.K, case.block_size))
     torch.cuda.synchronize()
     return Y
 
 
 def check_all(case, what):
-    print(f"[compint8] {what} M={case.M} K={case.K} N={case.N} bs={case.block_size} "
+    print(f"[compint8 {LAYOUT['v']}] {what} M={case.M} K={case.K} N={case.N} bs={case.block_size} "
           f"bits={case.bits} a={case.a_dtype} zp={case.zero_points is not None}", flush=True)
     qa, sa = oracle_quant(case)
     gqa, gsa = gpu_quant(case)
     assert np.array_equal(gsa, sa), f"{what}: activation scales differ"
     assert np.array_equal(gqa, qa), f"{what}: int8 activations differ"
+    if LAYOUT["v"] == "tiled" and case.block_size < 64:
+        with pytest.raises(qmm().QmmError) as err:
+            gpu_matmul(case)
+        assert err.value.status == qmm().QMM_ERR_UNSUPPORTED
+        return 0.0
     dots = oracle.compint8_block_dots(qa, u8(case.B), u8(case.zero_points), case.N, case.K,
                                       case.block_size, case.bits)
     assert np.array_equal(gpu_dots(case), dots), f"{what}: int32 block dots differ"
