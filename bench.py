@@ -209,6 +209,12 @@ def main():
 
 
 def _time_launches(fn, n, stream):
+    """Average ms per launch of fn(i), i = 0..n-1, after one untimed pass of
+    the same n launches (so clocks have ramped up and every buffer of a
+    rotating pool has been touched before the timed region)."""
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)

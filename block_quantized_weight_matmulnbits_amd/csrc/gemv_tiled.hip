@@ -94,58 +94,74 @@ __device__ __forceinline__ void load_x16(__amdgpu_buffer_rsrc_t rx, int k, bool 
 // pair word w*P/2 + i of code word w holds activations (wP + i, wP + i + P/2).
 // pw[unit] undoes the unit's shift.  Returns whether a unit is not exact.
 // The LPU lanes of a unit are adjacent and all take part (whole units).
+//
+// bf16: the magnitude bits of a bf16 value order like the value, so the
+// largest magnitude of the unit (packed 16-bit max) gives the largest
+// exponent, and the smallest nonzero one (packed 16-bit min after
+// subtracting 1, which sends zeros to 0xFFFF) the smallest.  Every value is
+// then scaled by 2^sh (exact) and packed to fp16 with round-toward-zero,
+// which is exact as well because the scaled values are fp16 normals with at
+// most 8 significant bits.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 template <int BITS, int XDT>
 __device__ __forceinline__ bool stage16(const u32x4 (&raw)[2], int a, uint32_t* __restrict__ xs,
                                         float* __restrict__ pw) {
   constexpr int P = 32 / BITS, E = 4 * P, LPU = E / 16;
-  float v[16];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * q + 2 * j] = bits16_to_f32<XDT>((uint16_t)(w[j] & 0xFFFFu));
-      v[8 * q + 2 * j + 1] = bits16_to_f32<XDT>((uint16_t)(w[j] >> 16));
-    }
-  }
+  const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w,
+                         raw[1].x, raw[1].y, raw[1].z, raw[1].w};
   bool bad = false;
   int sh = 0;
+  uint32_t pairs[8];
   if constexpr (XDT == DT_BF16) {
-    int emax = 0, emin = 255;
+    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t u = __float_as_uint(v[j]) & 0x7FFFFFFFu;
-      const int e = (int)(u >> 23);
-      emax = (u != 0) ? max(emax, e) : emax;
-      emin = (u != 0) ? min(emin, e) : emin;
+    for (int j = 0; j < 8; ++j) {
+      const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
+      mx = __builtin_elementwise_max(mx, m);
+      mn = __builtin_elementwise_min(mn, m - u16x2{1, 1});
     }
+    uint32_t umax = max((uint32_t)mx.x, (uint32_t)mx.y);
+    uint32_t umin = min((uint32_t)mn.x, (uint32_t)mn.y);
     if constexpr (LPU >= 2) {
-      emax = max(emax, __builtin_amdgcn_update_dpp(0, emax, 0xB1, 0xF, 0xF, false));
-      emin = min(emin, __builtin_amdgcn_update_dpp(0, emin, 0xB1, 0xF, 0xF, false));
+      umax = max(umax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)umax, 0xB1, 0xF, 0xF, false));
+      umin = min(umin, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)umin, 0xB1, 0xF, 0xF, false));
     }
     if constexpr (LPU >= 4) {
-      emax = max(emax, __builtin_amdgcn_update_dpp(0, emax, 0x4E, 0xF, 0xF, false));
-      emin = min(emin, __builtin_amdgcn_update_dpp(0, emin, 0x4E, 0xF, 0xF, false));
+      umax = max(umax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)umax, 0x4E, 0xF, 0xF, false));
+      umin = min(umin, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)umin, 0x4E, 0xF, 0xF, false));
     }
-    if (emax != 0) {
+    if (umax != 0) {
+      const int emax = (int)(umax >> 7);          // 255: inf or nan
+      const int emin = (int)((umin + 1) >> 7);    // 0: a subnormal
       bad = (emax == 255) || (emin == 0) || (emin < emax - 28);
       sh = 141 - emax;   // 14 - (emax - 127)
     }
+    // Value j of the unit's 16 as fp32 (bf16 is the upper half of fp32).
+    auto val = [&](int j) {
+      const uint32_t u = w[j >> 1];
+      return __uint_as_float((j & 1) ? (u & 0xFFFF0000u) : (u << 16));
+    };
+#pragma unroll
+    for (int c = 0; c < 16 / P; ++c) {
+#pragma unroll
+      for (int i = 0; i < P / 2; ++i) {
+        const float lo = ldexpf(val(c * P + i), sh);
+        const float hi = ldexpf(val(c * P + i + P / 2), sh);
+        pairs[c * (P / 2) + i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      }
+    }
   } else {
     // fp16 activations are used as they are; only inf / nan are not exact.
+    // Pairs are regrouped with byte permutes.
 #pragma unroll
-    for (int j = 0; j < 16; ++j) bad |= !__builtin_isfinite(v[j]);
-  }
-  uint32_t pairs[8];
+    for (int j = 0; j < 8; ++j) bad |= ((w[j] & 0x7C00u) == 0x7C00u) || ((w[j] & 0x7C000000u) == 0x7C000000u);
+    auto half_of = [&](int j) { return (w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu; };
 #pragma unroll
-  for (int w = 0; w < 16 / P; ++w) {
+    for (int c = 0; c < 16 / P; ++c)
 #pragma unroll
-    for (int i = 0; i < P / 2; ++i) {
-      const _Float16 lo = (_Float16)ldexpf(v[w * P + i], sh);
-      const _Float16 hi = (_Float16)ldexpf(v[w * P + i + P / 2], sh);
-      half2_t h = {lo, hi};
-      pairs[w * (P / 2) + i] = as_u32(h);
-    }
+      for (int i = 0; i < P / 2; ++i)
+        pairs[c * (P / 2) + i] = half_of(c * P + i) | (half_of(c * P + i + P / 2) << 16);
   }
   u32x4* dst = reinterpret_cast<u32x4*>(xs + a / 2);
   dst[0] = u32x4{pairs[0], pairs[1], pairs[2], pairs[3]};
@@ -154,17 +170,30 @@ __device__ __forceinline__ bool stage16(const u32x4 (&raw)[2], int a, uint32_t* 
   return bad;
 }
 
-// LDS layout, in 32-bit words, for a piece of pc chunks: the fp16 pairs
-// (pc + CPL chunks, the last CPL zero or unused), the unit factors, then the
-// S-share partial sums.
+// a.lo * b.lo + a.hi * b.hi + 0 in fp32, as __builtin_amdgcn_fdot2(a, b, 0.0f,
+// false); written as the three-operand form with an inline zero so that a
+// chain's first product needs no register cleared beforehand.
+__device__ __forceinline__ float dot2_first(half2_t a, half2_t b) {
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// LDS layout, in 32-bit words, for a piece of pc chunks and S shares of D
+// loads in flight: the fp16 pairs, the unit factors, then the S-share
+// partial sums.  The first pc + CPL chunks are staged; the pairs and factors
+// extend (S + D) * CPL chunks past pc so that every activation read of a
+// load past the end of its share (whose result is discarded) stays inside
+// the allocation: such reads reach at most chunk pn + (S + D) * CPL - 1.
 template <int BITS>
 struct TLds {
   int xs_words, pw_words, total;
-  __host__ __device__ TLds(int pc, int waves) {
+  __host__ __device__ TLds(int pc, int O, int S, int D) {
     constexpr int CPL = TGeom<BITS>::CPL, E = TGeom<BITS>::E;
-    xs_words = (pc + CPL) * 32;
-    pw_words = ((pc + CPL) * 64 / E + 3) / 4 * 4;
-    total = xs_words + pw_words + waves * OCT;
+    const int span = pc + (S + D) * CPL;
+    xs_words = span * 32;
+    pw_words = (span * 64 / E + 3) / 4 * 4;
+    total = xs_words + pw_words + O * S * OCT;
   }
 };
 
@@ -184,7 +213,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
 
   extern __shared__ u32x4 smem_tv[];
   const int W = O * S;
-  const TLds<BITS> L(pc, W);
+  const TLds<BITS> L(pc, O, S, D);
   uint32_t* xs = reinterpret_cast<uint32_t*>(smem_tv);
   float* pw = reinterpret_cast<float*>(xs + L.xs_words);
   float* red = pw + L.pw_words;
@@ -280,17 +309,20 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
     if (!exact) {
       // The activations of load j (read from LDS one load ahead of their use,
       // so that the LDS latency hides behind the previous load's arithmetic).
-      // Loads past the share may point past the staged piece: clamped.
+      // Loads past the share read the padding past the staged piece.
       struct XV { uint32_t w[E / 2]; float f; };
+      // This lane's unit in the staged piece (lane_kr is a multiple of E);
+      // load j reads CPL chunks further on.
+      const u32x4* x_lane = reinterpret_cast<const u32x4*>(xs) + lane_kr / 8;
+      const float* pw_lane = pw + lane_kr / E;
       auto fetch = [&](XV& xv, int j) {
-        const int kr = min(lane_kr + j * (CPL * TKC), 2 * L.xs_words - E);
-        const u32x4* p = reinterpret_cast<const u32x4*>(xs + kr / 2);
+        const u32x4* p = x_lane + j * (CPL * TKC / 8);
 #pragma unroll
         for (int t = 0; t < E / 8; ++t) {
           const u32x4 v = p[t];
           xv.w[4 * t + 0] = v.x; xv.w[4 * t + 1] = v.y; xv.w[4 * t + 2] = v.z; xv.w[4 * t + 3] = v.w;
         }
-        xv.f = pw[kr / E];
+        xv.f = pw_lane[j * (CPL * TKC / E)];
       };
       // acc += scale * (codes . activations) for load j from slot sl.
       // masked: the load may hold lanes past the share or past the blocks.
@@ -304,7 +336,6 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
         half2_t nz[G::NPOS];
 #pragma unroll
         for (int pi = 0; pi < G::NPOS; ++pi) {
-          dp[pi] = 0.0f;
           const uint32_t h = 0xE400u | (z << (pi * BITS));   // -(1024 + 2^p z)
           nz[pi] = as_half2(h | (h << 16));
         }
@@ -320,8 +351,11 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
               const uint32_t mask = (m << p) | (m << (p + 16));
               const half2_t cv = as_half2((src & mask) | magic) + nz[pi];
               const int ci = (hf * 8 + p) / BITS;            // code index in the word
-              dp[pi] = __builtin_amdgcn_fdot2(cv, as_half2(xv.w[wi * (P / 2) + ci]), dp[pi],
-                                              false);
+              const half2_t xh = as_half2(xv.w[wi * (P / 2) + ci]);
+              if (wi == 0 && hf == 0)
+                dp[pi] = dot2_first(cv, xh);
+              else
+                dp[pi] = __builtin_amdgcn_fdot2(cv, xh, dp[pi], false);
             }
           }
         }
@@ -444,8 +478,11 @@ hipError_t launch_z(const MatArgs& a, const TiledGeom& tg) {
   const int O = std::min(MAX_WAVES, std::max(1, (n_oct + 255) / 256));
   int S = 1;
   while (O * S * 2 <= MAX_WAVES && O * S < 4 && chunks >= 2 * (2 * S) * G::CPL) S *= 2;
+  // More shares while the workgroup's threads cannot stage the activations
+  // in their two first passes (every further pass is a dependent load).
   const int pc = std::min(chunks, PIECE_CHUNKS);
-  const TLds<BITS> L(pc, O * S);
+  while (O * S * 2 <= MAX_WAVES && O * S * 64 * 32 < (pc + G::CPL) * TKC) S *= 2;
+  const TLds<BITS> L(pc, O, S, D);
   const size_t lds = (size_t)L.total * 4;
   const int grid = (n_oct + O - 1) / O;
   const bool linb = a.block_size <= TKC * G::CPL;
