@@ -129,6 +129,7 @@ def main():
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
+        _queue_ahead(len(cases) * args.steps)
         t_start.record(stream)
         for s in range(args.steps):
             step(s)
@@ -142,6 +143,7 @@ def main():
         n_dom = max(20, args.steps)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        _queue_ahead(n_dom)
         e0.record(stream)
         for s in range(n_dom):
             launch(dom[s % len(dom)], s % n_copies)
@@ -208,6 +210,28 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _queue_ahead(n_launches):
+    """Hold the current stream with a device-side spin long enough for the
+    host to queue n_launches calls (10 us each, about twice what the Python
+    binding takes per call), so that the HIP events which follow time the
+    device executing the launches back to back rather than the host issuing
+    them: the smallest projections run for about as long as one Python
+    call takes."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * max(1.0, 0.01 * n_launches)))
+
+
 def _time_launches(fn, n, stream):
     """Average ms per launch of fn(i), i = 0..n-1, after one untimed pass of
     the same n launches (so clocks have ramped up and every buffer of a
@@ -217,6 +241,7 @@ def _time_launches(fn, n, stream):
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    _queue_ahead(n)
     e0.record(stream)
     for i in range(n):
         fn(i)

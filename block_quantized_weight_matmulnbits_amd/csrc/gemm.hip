@@ -68,6 +68,15 @@ template <> struct MfmaOp<DT_F16> {
   }
 };
 
+// w & m through an instruction the compiler cannot look into, so that the
+// byte conversions below stay v_cvt_f32_ubyte{0..3} of the masked word
+// instead of becoming one bit-field extract per code.
+__device__ __forceinline__ uint32_t opaque_and(uint32_t w, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %2, %1" : "=v"(r) : "v"(w), "s"(m));
+  return r;
+}
+
 // Codes of one 32-bit word as fp32 values, in element order.
 template <int BITS>
 __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
@@ -75,15 +84,15 @@ __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
     q[0] = (float)(w & 0xFF); q[1] = (float)((w >> 8) & 0xFF);
     q[2] = (float)((w >> 16) & 0xFF); q[3] = (float)(w >> 24);
   } else if constexpr (BITS == 4) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo = opaque_and(w, 0x0F0F0F0Fu), hi = opaque_and(w >> 4, 0x0F0F0F0Fu);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       q[2 * j] = (float)((lo >> (8 * j)) & 0xFF);
       q[2 * j + 1] = (float)((hi >> (8 * j)) & 0xFF);
     }
   } else {
-    const uint32_t f[4] = {w & 0x03030303u, (w >> 2) & 0x03030303u, (w >> 4) & 0x03030303u,
-                           (w >> 6) & 0x03030303u};
+    const uint32_t f[4] = {opaque_and(w, 0x03030303u), opaque_and(w >> 2, 0x03030303u),
+                           opaque_and(w >> 4, 0x03030303u), opaque_and(w >> 6, 0x03030303u)};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -260,18 +269,27 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
       zs[i] = (float)z * sf[i];
     }
     uint32_t pk[HK / 2];
-#pragma unroll
-    for (int w = 0; w < WPT; ++w) {
-      // Block of this word relative to the thread's first block (0 or 1).
-      const bool second = min((kt + w * P) >> log2_bs, kb - 1) != blk0;
-      const float s = second ? sf[1] : sf[0];
-      const float z = second ? zs[1] : zs[0];
+    // (q - z) * s = q * s - z * s: for 16-bit scales both products are
+    // exact and so is the difference; one rounding to the activation dtype.
+    auto dequant_word = [&](int w, float s, float z) {
       float q[P];
       word_codes_f32<BITS>(cw[st][w], q);
-      // (q - z) * s = q * s - z * s: both products exact, the difference
-      // exact, one rounding to the activation dtype.
 #pragma unroll
       for (int j = 0; j < P; j += 2) pk[(w * P + j) / 2] = Op::pack(fmaf(q[j], s, -z), fmaf(q[j + 1], s, -z));
+    };
+    // The thread's HK codes start on a block boundary (kt is a multiple of
+    // HK, and bs >= 16 divides it or is a multiple of it).
+    if ((1 << log2_bs) >= HK) {
+      // All in one block.
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) dequant_word(w, sf[0], zs[0]);
+    } else {
+      // bs = 16: word w lies in the second block when w * P >= bs.
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        const bool second = w * P >= (1 << log2_bs);
+        dequant_word(w, second ? sf[1] : sf[0], second ? zs[1] : zs[0]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < HK / 8; ++j)
