@@ -378,6 +378,9 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
       // 2-bit units hold 64 activations: without the look-ahead, to stay
       // within 128 registers.
       constexpr bool AHEAD = BITS != 2;
+      // The look-ahead alternates two activation buffers by the parity of q,
+      // which restarts at every D loads: D must be even.
+      static_assert(!AHEAD || D % 2 == 0, "the activation look-ahead needs an even D");
       XV xa, xb;
       if constexpr (AHEAD) fetch(xa, 0);
       int j0 = 0;
