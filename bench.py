@@ -1,18 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the block-quantized-weight matmul hot path on one MI355X.
 
-A step is one M = 1 decode pass over a Llama-3-8B-shaped layer: the seven
-projections (q, k, v, o, gate, up, down; 4-bit asymmetric, block 32, bf16
-activations and scales) run back to back through ``qmm_gemv``.  ``value`` is
-the layer's algorithmic bytes (packed codes + scales + zero points +
-activations + outputs) divided by the measured time per step, in GB/s.
-Weights rotate through enough copies (> 512 MB) that each step streams them
-from HBM instead of the 256 MB Infinity Cache.
+A step is one M = 1 decode pass over a Llama-3-8B-shaped layer (4-bit
+asymmetric, block 32, bf16 activations and scales).  The projections that
+read the same activations are stored stacked along N, as one weight matrix
+each, so a step is four ``qmm_gemv`` launches in dependency order: q|k|v
+(K 4096, N 6144), o, gate|up (K 4096, N 28672), down.  ``value`` is the
+step's algorithmic bytes (packed codes + scales + zero points + activations
++ outputs) divided by the measured time per step, in GB/s.  Weights rotate
+through enough copies (> 512 MB) that each step streams them from HBM
+instead of the 256 MB Infinity Cache.  The same layer as seven separate
+launches is reported beside it (``unfused``).
 
 The JSON line also carries the roofline of the dominant kernel (the GEMV on
-the 4096 x 14336 gate/up shape, timed by HIP events around a run of its own
-back-to-back launches on the same stream) and the CPU oracle timed on the
-host cores.
+the gate|up matrix, timed by HIP events around a run of its own
+back-to-back launches on the same stream), the same for one 4096 x 14336
+projection, the prefill GEMM, CompInt8 and conv figures, and the CPU oracle
+timed on the host cores.
 """
 from __future__ import annotations
 
@@ -28,18 +32,18 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 POOL_BYTES = 640 << 20         # rotating weight pool, > 2x the Infinity Cache
 COPY_CAL_BYTES = 256 << 20     # plain copy used to scale the HBM byte counters
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "gemv_tiled_K4096_N14336_traffic.txt")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                              "block_quantized_weight_matmulnbits_amd", "csrc", "gemv_tiled.hip")
 
 
-def measured_traffic():
+def measured_traffic(name):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when the kernel source has changed since it was taken."""
+    summary profiles/<name>, or None when it is missing or the kernel source
+    has changed since it was taken."""
     import hashlib
     try:
-        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
+        fields = dict(line.split(":", 1) for line in open(os.path.join(PROFILES, name))
                       if ":" in line and not line.startswith("#"))
         src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256", "").strip() != src_hash:
@@ -80,7 +84,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     from block_quantized_weight_matmulnbits_amd import qmm
-    from block_quantized_weight_matmulnbits_amd.workloads import decode_layer
+    from block_quantized_weight_matmulnbits_amd.workloads import decode_layer, decode_layer_fused
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -91,37 +95,55 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cases = decode_layer()
+    cases = decode_layer()                 # the seven projections
+    fcases = decode_layer_fused()          # q|k|v and gate|up stacked: four launches
     step_bytes = sum(layer_bytes(c) for c in cases)
+    fstep_bytes = sum(layer_bytes(c) for c in fcases)
     n_copies = max(2, -(-POOL_BYTES // step_bytes))
-    # Copy 0 is the seeded weights; the others are byte-identical copies at
-    # different addresses (only the addresses matter for cache behaviour).
-    pools = []
-    for c in cases:
-        d = c.to(dev)
-        pools.append([(d.B, d.scales, d.zero_points)] +
-                     [(d.B.clone(), d.scales.clone(), d.zero_points.clone())
-                      for _ in range(n_copies - 1)])
-    # The same weights repacked once into the tiled layout (qmm_repack), as an
-    # inference session does when it loads constant weights; not timed.
-    tiled = [[(qmm.qmm_repack(B, sc, zp, c.K, c.N, c.block_size, c.bits), None, None)
-              for (B, sc, zp) in pool] for c, pool in zip(cases, pools)]
-    xs = [c.to(dev).A.reshape(-1) for c in cases]
-    ys = [torch.empty(c.N, dtype=torch.bfloat16, device=dev) for c in cases]
+
+    def pool_of(clist):
+        """Per case: n_copies (B, scales, zero points) on the device. Copy 0 is
+        the seeded weights; the others are byte-identical copies at other
+        addresses (only the addresses matter for cache behaviour)."""
+        pools = []
+        for c in clist:
+            d = c.to(dev)
+            pools.append([(d.B, d.scales, d.zero_points)] +
+                         [(d.B.clone(), d.scales.clone(), d.zero_points.clone())
+                          for _ in range(n_copies - 1)])
+        return pools
+
+    def repacked(clist, pools):
+        """The same weights repacked once into the tiled layout (qmm_repack), as
+        an inference session does when it loads constant weights; not timed."""
+        return [[(qmm.qmm_repack(B, sc, zp, c.K, c.N, c.block_size, c.bits), None, None)
+                 for (B, sc, zp) in pool] for c, pool in zip(clist, pools)]
+
+    pools = pool_of(cases)
+    tiled = repacked(cases, pools)
+    fpools = pool_of(fcases)
+    ftiled = repacked(fcases, fpools)
+    del fpools
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
-    dom = [i for i, c in enumerate(cases) if (c.K, c.N) == (4096, 14336)]
-    dom_bytes = layer_bytes(cases[dom[0]])
 
-    def measure(weights):
+    def series(clist, weights):
+        xs = [c.to(dev).A.reshape(-1) for c in clist]
+        ys = [torch.empty(c.N, dtype=torch.bfloat16, device=dev) for c in clist]
+
         def launch(i, j):
-            c = cases[i]
+            c = clist[i]
             B, sc, zp = weights[i][j]
             qmm.qmm_gemv(xs[i], B, sc, zp, None, ys[i], c.K, c.N, c.block_size, c.bits, 0,
                          stream)
+        return launch
+
+    def time_steps(clist, weights):
+        """ms per layer step: every launch of clist in order, weight copy s."""
+        launch = series(clist, weights)
 
         def step(s):
-            for i in range(len(cases)):
+            for i in range(len(clist)):
                 launch(i, s % n_copies)
 
         for s in range(args.warmup):
@@ -129,33 +151,48 @@ def main():
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
-        _queue_ahead(len(cases) * args.steps)
+        _queue_ahead(len(clist) * args.steps)
         t_start.record(stream)
         for s in range(args.steps):
             step(s)
         t_end.record(stream)
         torch.cuda.synchronize()
-        ms_per_step = t_start.elapsed_time(t_end) / args.steps
-        # Dominant kernel: the GEMV on the 4096 x 14336 gate/up shape,
-        # launched back to back (rotating weight copies) between one pair of
-        # HIP events on the launch stream; per-launch events would add their
-        # own overhead.
-        n_dom = max(20, args.steps)
+        return t_start.elapsed_time(t_end) / args.steps
+
+    def time_kernel(clist, weights, idx):
+        """ms per launch of the GEMVs clist[i], i in idx, launched back to back
+        (rotating weight copies) between one pair of HIP events on the launch
+        stream; per-launch events would add their own overhead."""
+        launch = series(clist, weights)
+        n = max(20, args.steps)
+        for s in range(n):
+            launch(idx[s % len(idx)], s % n_copies)
+        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        _queue_ahead(n_dom)
+        _queue_ahead(n)
         e0.record(stream)
-        for s in range(n_dom):
-            launch(dom[s % len(dom)], s % n_copies)
+        for s in range(n):
+            launch(idx[s % len(idx)], s % n_copies)
         e1.record(stream)
         torch.cuda.synchronize()
-        return ms_per_step, e0.elapsed_time(e1) / n_dom
+        return e0.elapsed_time(e1) / n
 
-    ms_t, dom_t = measure(tiled)
-    ms_o, dom_o = measure(pools)
-    ms_per_step, dom_avg_ms = ms_t, dom_t
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
+    ms_f = time_steps(fcases, ftiled)
+    ms_t = time_steps(cases, tiled)
+    ms_o = time_steps(cases, pools)
+    # Dominant kernel of the step: the gate|up launch (K = 4096, N = 28672).
+    fdom = [i for i, c in enumerate(fcases) if c.meta["name"] == "gate_up"]
+    fdom_bytes = layer_bytes(fcases[fdom[0]])
+    fdom_ms = time_kernel(fcases, ftiled, fdom)
+    # The single 4096 x 14336 projection (gate or up alone).
+    dom = [i for i, c in enumerate(cases) if (c.K, c.N) == (4096, 14336)]
+    dom_bytes = layer_bytes(cases[dom[0]])
+    dom_t = time_kernel(cases, tiled, dom)
+    dom_o = time_kernel(cases, pools, dom)
+    value = fstep_bytes / (ms_f * 1e-3) / 1e9
+    achieved = fdom_bytes / (fdom_ms * 1e-3) / 1e9
+    achieved_1 = dom_bytes / (dom_t * 1e-3) / 1e9
 
     out = {
         "metric": METRIC,
@@ -164,7 +201,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(ms_f, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -174,25 +211,41 @@ def main():
         "config": {
             "workload": "decode GEMV, one Llama-3-8B-shaped layer (q,k,v,o,gate,up,down), M=1, "
                         "bf16 activations, 4-bit asymmetric block 32, bf16 scales, packed zero points",
+            "projections": "q|k|v stacked along N (K=4096, N=6144), o, gate|up stacked "
+                           "(K=4096, N=28672), down: four launches per step",
             "weight_layout": "tiled (qmm_repack once at load, not timed)",
             "M": 1,
-            "shapes_KxN": [[c.K, c.N] for c in cases],
-            "bytes_per_step": step_bytes,
+            "shapes_KxN": [[c.K, c.N] for c in fcases],
+            "bytes_per_step": fstep_bytes,
             "weight_copies_rotated": n_copies,
         },
         "roofline": {
-            "kernel": "gemv_tiled_kernel (4-bit, bf16, zero points) on K=4096 N=14336",
+            "kernel": "gemv_tiled_kernel (4-bit, bf16, zero points) on K=4096 N=28672 (gate|up)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "avg_launch_us": round(dom_avg_ms * 1e3, 3),
+            "traffic": measured_traffic("gemv_tiled_K4096_N28672_traffic.txt"),
+            "avg_launch_us": round(fdom_ms * 1e3, 3),
+            "bytes_per_launch": fdom_bytes,
+        },
+        "unfused": {
+            "what": "the seven projections as seven launches, tiled layout",
+            "value": round(step_bytes / (ms_t * 1e-3) / 1e9, 2),
+            "ms_per_step": round(ms_t, 5),
+            "bytes_per_step": step_bytes,
+        },
+        "roofline_K4096_N14336": {
+            "kernel": "gemv_tiled_kernel on K=4096 N=14336 (gate or up alone)",
+            "achieved": round(achieved_1, 2),
+            "frac": round(achieved_1 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("gemv_tiled_K4096_N14336_traffic.txt"),
+            "avg_launch_us": round(dom_t * 1e3, 3),
             "bytes_per_launch": dom_bytes,
         },
         "operator_layout": {
-            "kernel": "gemv_kernel on the operator's [N, kb, blob] layout",
+            "kernel": "gemv_kernel on the operator's [N, kb, blob] layout, seven launches",
             "value": round(step_bytes / (ms_o * 1e-3) / 1e9, 2),
             "ms_per_step": round(ms_o, 5),
             "dominant_avg_launch_us": round(dom_o * 1e3, 3),

@@ -118,6 +118,43 @@ def decode_layer(seed: int = 2) -> list[MatmulCase]:
     return out
 
 
+# Projections of the layer that read the same activations, stored as one
+# weight matrix (their rows of B, scales and zero points stacked along N).
+FUSED_GROUPS = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+                ("down", ("down",))]
+
+
+def concat_along_n(cases: list[MatmulCase], name: str) -> MatmulCase:
+    """One MatMulNBits problem whose weights are the given problems' weights
+    stacked along N (same K, block size, bits and dtypes); the activations are
+    the first problem's.  Output column n of the result is output column n' of
+    the problem that row came from, so the layer's projections that share an
+    input run as one launch.  Pure concatenation of the operator's layout."""
+    c0 = cases[0]
+    for c in cases[1:]:
+        assert (c.M, c.K, c.block_size, c.bits, c.a_dtype, c.s_dtype) == \
+            (c0.M, c0.K, c0.block_size, c0.bits, c0.a_dtype, c0.s_dtype)
+        assert (c.zero_points is None) == (c0.zero_points is None)
+        assert (c.bias is None) == (c0.bias is None)
+    cat = lambda ts: None if ts[0] is None else torch.cat(ts, dim=0)
+    out = MatmulCase(c0.M, c0.K, sum(c.N for c in cases), c0.block_size, c0.bits, c0.a_dtype,
+                     c0.A, cat([c.B for c in cases]), cat([c.scales for c in cases]),
+                     cat([c.zero_points for c in cases]), cat([c.bias for c in cases]),
+                     c0.s_dtype)
+    out.meta["name"] = name
+    out.meta["parts"] = [(c.meta.get("name"), c.N) for c in cases]
+    return out
+
+
+def decode_layer_fused(seed: int = 2) -> list[MatmulCase]:
+    """The decode layer as it runs with fused projections: q|k|v and gate|up
+    each as one matrix (stacked along N), o and down alone -- four launches
+    in the order the layer's data dependencies allow (qkv, o, gate_up, down).
+    The weights are those of decode_layer(seed)."""
+    by_name = {c.meta["name"]: c for c in decode_layer(seed)}
+    return [concat_along_n([by_name[p] for p in parts], name) for name, parts in FUSED_GROUPS]
+
+
 # (bits, block_size, asymmetric) of the batched-decode CompInt8 workload.
 COMPINT8_VARIANTS = [(4, 128, False), (8, 64, True), (2, 64, True)]
 

@@ -80,6 +80,15 @@ def test_decode_layer_full_shapes():
         print(f"  max |err|/S = {r:.3e}")
 
 
+def test_decode_layer_fused_shapes():
+    """The layer with q|k|v and gate|up stacked along N (N = 6144 and 28672),
+    as the benchmark runs it: all outputs."""
+    from block_quantized_weight_matmulnbits_amd.workloads import decode_layer_fused
+    for case in decode_layer_fused():
+        r = check(case, f"decode fused {case.meta['name']}")
+        print(f"  max |err|/S = {r:.3e}")
+
+
 def test_long_k_spans_several_lds_chunks():
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
     for bits in (2, 4, 8):
