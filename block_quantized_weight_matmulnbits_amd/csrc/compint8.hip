@@ -40,14 +40,27 @@ __global__ __launch_bounds__(256) void quantize_a_kernel(const typename dt<XDT>:
                                                          int8_t* __restrict__ qa,
                                                          float* __restrict__ sa, int M, int K,
                                                          int bs, int kb) {
+  // Blocks of up to QA_REG * 64 activations are read once and kept in
+  // registers between the maximum and the quantization (one global round
+  // trip); longer blocks read their activations a second time.
+  constexpr int QA_REG = 4;
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw >= M * kb) return;
   const int m = gw / kb, b = gw % kb;
   const int k0 = b * bs;
   const int64_t padded = (int64_t)kb * bs;
+  const bool in_regs = bs <= QA_REG * 64;
+  float xv[QA_REG];
+#pragma unroll
+  for (int i = 0; i < QA_REG; ++i) {
+    const int k = k0 + lane + 64 * i;
+    xv[i] = (lane + 64 * i < bs && k < K) ? dt<XDT>::to_f32(A[(int64_t)m * K + k]) : 0.0f;
+  }
   float amax = 0.0f;
-  for (int e = lane; e < bs; e += 64) {
+#pragma unroll
+  for (int i = 0; i < QA_REG; ++i) amax = fmaxf(amax, fabsf(xv[i]));
+  for (int e = lane + 64 * QA_REG; e < bs; e += 64) {
     const int k = k0 + e;
     if (k < K) amax = fmaxf(amax, fabsf(dt<XDT>::to_f32(A[(int64_t)m * K + k])));
   }
@@ -56,16 +69,26 @@ __global__ __launch_bounds__(256) void quantize_a_kernel(const typename dt<XDT>:
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const float scale = amax / 127.0f;   // IEEE binary32 division
   if (lane == 0) sa[(int64_t)m * kb + b] = scale;
-  for (int e = lane; e < bs; e += 64) {
-    const int k = k0 + e;
-    int8_t v = 0;
-    if (k < K && scale != 0.0f) {
-      const float x = dt<XDT>::to_f32(A[(int64_t)m * K + k]);
-      float r = rintf(x / scale);      // IEEE division, ties to even
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      v = (int8_t)r;
+  auto quant = [&](float x) {
+    float r = rintf(x / scale);        // IEEE division, ties to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)r;
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < QA_REG; ++i) {
+      const int e = lane + 64 * i;
+      // Positions past K (the padding of the last block) are zero; so is
+      // every position of a block whose scale is 0.
+      if (e < bs) qa[(int64_t)m * padded + k0 + e] = (k0 + e < K && scale != 0.0f) ? quant(xv[i]) : 0;
     }
-    qa[(int64_t)m * padded + k] = v;
+  } else {
+    for (int e = lane; e < bs; e += 64) {
+      const int k = k0 + e;
+      int8_t v = 0;
+      if (k < K && scale != 0.0f) v = quant(dt<XDT>::to_f32(A[(int64_t)m * K + k]));
+      qa[(int64_t)m * padded + k] = v;
+    }
   }
 }
 

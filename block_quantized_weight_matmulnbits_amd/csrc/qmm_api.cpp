@@ -219,7 +219,8 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
                            s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
                            accuracy_level, &a);
   if (st != QMM_OK) return st;
-  if (a.tiled && !qmm::compint8_tiled_supported(a))
+  const bool small = M > 0 && qmm::compint8_small_supported(a);
+  if (a.tiled && !small && !qmm::compint8_tiled_supported(a))
     return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8: on the tiled layout CompInt8 needs "
                 "block_size >= 64 (whole 64-code chunks per block) and at most 896 blocks per "
                 "row (got block_size=%d, %lld blocks). How to fix: pass the operator's layout "
@@ -228,6 +229,9 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
   st = check_workspace("qmm_gemm_compint8", a, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
   a.stream = (hipStream_t)stream;
+  // M = 1 on the tiled layout: one launch that quantizes the activations in
+  // LDS (the workspace is not touched).
+  if (small) return hip_status(qmm::launch_compint8_small(a), "qmm_gemm_compint8");
   int8_t* qa = (int8_t*)workspace;
   float* sa = (float*)((char*)workspace + qmm::ws_qa_bytes(a.M, a.kb, a.block_size));
   hipError_t e = qmm::launch_quantize_a(a, qa, sa);

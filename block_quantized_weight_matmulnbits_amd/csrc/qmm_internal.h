@@ -45,6 +45,10 @@ hipError_t launch_gemm(const MatArgs& a);
 hipError_t launch_quantize_a(const MatArgs& a, int8_t* qa, float* sa);
 hipError_t launch_compint8(const MatArgs& a, const int8_t* qa, const float* sa);
 hipError_t launch_compint8_dots(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots);
+// CompInt8 for M = 1 on the tiled layout, quantization fused
+// (compint8_small.hip); it needs no workspace.
+bool compint8_small_supported(const MatArgs& a);
+hipError_t launch_compint8_small(const MatArgs& a);
 // CompInt8 on the tiled layout with int8 MFMA (compint8_tiled.hip).
 bool compint8_tiled_supported(const MatArgs& a);
 hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa);

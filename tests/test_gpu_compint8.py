@@ -7,8 +7,11 @@ against the oracle's CompInt8 value.  Shapes: small ragged ones for every
 (bits, block size, dtype, zero point) and the full batched-decode workload
 (M in {1, 4, 16}, K = 4096, N = 14336; bits 4 / bs 128 symmetric, bits 8 /
 bs 64 and bits 2 / bs 64 asymmetric).  Every test runs on the operator's
-layout and on the tiled layout of qmm_repack (int8 matrix-core kernel);
-on the tiled layout blocks shorter than 64 codes must be rejected.
+layout and on the tiled layout of qmm_repack.  On the tiled layout M = 1
+runs the fused single-launch kernel (v_dot4 block dots, activations
+quantized in LDS; any block of at least one 16-byte unit of codes) and
+larger M the int8 matrix-core kernel, which, like the block-dot export,
+rejects blocks shorter than 64 codes.
 """
 import numpy as np
 import pytest
@@ -89,14 +92,22 @@ def check_all(case, what):
     gqa, gsa = gpu_quant(case)
     assert np.array_equal(gsa, sa), f"{what}: activation scales differ"
     assert np.array_equal(gqa, qa), f"{what}: int8 activations differ"
-    if LAYOUT["v"] == "tiled" and case.block_size < 64:
+    tiled = LAYOUT["v"] == "tiled"
+    mfma_ok = not tiled or case.block_size >= 64
+    small_ok = tiled and case.M == 1 and 128 // case.bits <= case.block_size <= 1024
+    if mfma_ok:
+        dots = oracle.compint8_block_dots(qa, u8(case.B), u8(case.zero_points), case.N, case.K,
+                                          case.block_size, case.bits)
+        assert np.array_equal(gpu_dots(case), dots), f"{what}: int32 block dots differ"
+    else:
+        with pytest.raises(qmm().QmmError) as err:
+            gpu_dots(case)
+        assert err.value.status == qmm().QMM_ERR_UNSUPPORTED
+    if not (mfma_ok or small_ok):
         with pytest.raises(qmm().QmmError) as err:
             gpu_matmul(case)
         assert err.value.status == qmm().QMM_ERR_UNSUPPORTED
         return 0.0
-    dots = oracle.compint8_block_dots(qa, u8(case.B), u8(case.zero_points), case.N, case.K,
-                                      case.block_size, case.bits)
-    assert np.array_equal(gpu_dots(case), dots), f"{what}: int32 block dots differ"
     Y, S = oracle.compint8_matmul(qa, sa, u8(case.B), f64(case.scales), u8(case.zero_points),
                                   f64(case.bias), case.N, case.K, case.block_size, case.bits)
     return assert_within(gpu_matmul(case), Y, S, TOL[case.A.dtype], what)
@@ -113,6 +124,21 @@ def test_small_ragged_shapes(bits, bs, a_dtype):
             case = make_matmul_case(M, K, N, bs, bits, a_dtype=a_dtype, has_zp=has_zp,
                                     has_bias=has_bias, seed=100 * bits + bs + i)
             check_all(case, f"small b{bits} bs{bs} {a_dtype}")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_few_rows_long_k_and_lds_limit(bits):
+    """M = 2 and 3 with K long enough for several wave loads per share, an
+    M = 1 row whose quantized activations nearly fill the fused kernel's LDS
+    budget, and one past it (which takes the quantize-then-matrix-core route
+    on the tiled layout)."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    for i, (M, K, N, bs) in enumerate([(2, 4096, 300, 64), (3, 4104, 96, 128),
+                                       (1, 40000, 65, 64), (1, 60000, 64, 128)]):
+        case = make_matmul_case(M, K, N, bs, bits, a_dtype="bf16", has_zp=True, has_bias=True,
+                                seed=500 + 10 * bits + i)
+        r = check_all(case, f"rows/long K b{bits}")
+        print(f"  max |err|/S = {r:.3e}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])

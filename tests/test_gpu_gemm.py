@@ -32,6 +32,18 @@ def run_gemm(case):
     return Y
 
 
+def run_gemm_tiled(case):
+    """The same product on the weights repacked by qmm_repack."""
+    from block_quantized_weight_matmulnbits_amd import qmm
+    c = case.to(DEV)
+    Y = torch.empty(case.M, case.N, dtype=c.A.dtype, device=DEV)
+    t = qmm.qmm_repack(c.B, c.scales, c.zero_points, case.K, case.N, case.block_size, case.bits)
+    qmm.qmm_gemm(c.A, t, None, None, c.bias, Y, case.M, case.K, case.N, case.block_size,
+                 case.bits)
+    torch.cuda.synchronize()
+    return Y
+
+
 def exact_case(M, K, N, bs, bits, a_dtype, seed):
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
     case = make_matmul_case(M, K, N, bs, bits, a_dtype=a_dtype, has_zp=True, has_bias=True,
@@ -71,6 +83,29 @@ def test_random_data_within_tolerance(a_dtype, bits):
         Y, S = oracle_matmul(case)
         r = assert_within(run_gemm(case), Y, S, TOL[case.A.dtype], "gemm random")
         print(f"  max |err|/S = {r:.3e}")
+
+
+def test_224_column_tiles_ragged():
+    """N a multiple of 224 (the 224-column tile kernels) with ragged M and K:
+    exact data bit for bit, random data within tolerance, on both layouts."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    for i, (M, K, N) in enumerate([(17, 64, 224), (300, 264, 448), (520, 1000, 672),
+                                   (257, 72, 224)]):
+        case = exact_case(M, K, N, 32, 4, "bf16", seed=77 + i)
+        print(f"[gemm 224 exact] M={M} K={K} N={N}", flush=True)
+        Y, _ = oracle_matmul(case)
+        expect = torch.from_numpy(Y).to(case.A.dtype)
+        assert torch.equal(run_gemm(case).cpu(), expect), (M, K, N)
+        assert torch.equal(run_gemm_tiled(case).cpu(), expect), ("tiled", M, K, N)
+    for i, (M, K, N) in enumerate([(257, 4096, 448), (600, 1032, 224)]):
+        case = make_matmul_case(M, K, N, 32, 4, a_dtype="bf16", has_zp=True, has_bias=True,
+                                seed=90 + i)
+        print(f"[gemm 224 random] M={M} K={K} N={N}", flush=True)
+        Y, S = oracle_matmul(case)
+        y = run_gemm(case)
+        r = assert_within(y, Y, S, TOL[case.A.dtype], "gemm 224 random")
+        print(f"  max |err|/S = {r:.3e}")
+        assert torch.equal(run_gemm_tiled(case), y), ("tiled", M, K, N)
 
 
 def test_prefill_workload_sampled_rows():
