@@ -253,6 +253,7 @@ def main():
         },
     }
 
+    out["roofline"]["read_ceiling"] = read_ceiling(dev, stream, fdom_bytes, fdom_ms)
     out["prefill_gemm"] = bench_prefill(qmm, dev, stream, args)
     out["compint8"] = bench_compint8(qmm, dev, stream, args)
     out["conv_int8"] = bench_conv(qmm, dev, stream, args)
@@ -301,6 +302,45 @@ def _time_launches(fn, n, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def read_ceiling(dev, stream, nbytes, kernel_ms):
+    """Time a plain streaming read of nbytes (the probe library's kernel:
+    non-temporal 16-byte loads, grid-stride, nothing else) over rotating
+    buffers, as the dominant kernel's launches are timed: what one launch
+    needs just to read that many bytes here.  None if the probe library was
+    not built."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "block_quantized_weight_matmulnbits_amd", "probe", "libqmm_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.qmm_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    nb = nbytes // 16 * 16
+    copies = max(2, -(-POOL_BYTES // nb))
+    bufs = [torch.full((nb,), i, dtype=torch.uint8, device=dev) for i in range(copies)]
+    best = None
+    for grid in (1024, 2048):
+        out = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+
+        def run(i, grid=grid, out=out):
+            rc = lib.qmm_probe_stream_read(bufs[i % copies].data_ptr(), nb, out.data_ptr(), grid,
+                                           ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"stream read probe failed: {rc}")
+
+        ms = _time_launches(run, 100, stream)
+        if best is None or ms < best[0]:
+            best = (ms, grid)
+    del bufs
+    gbps = nb / (best[0] * 1e-3) / 1e9
+    return {"what": "plain streaming read of the same bytes (non-temporal 16-byte loads, "
+                    f"{best[1]} x 256 threads), one launch per buffer, rotating buffers",
+            "bytes": nb, "us": round(best[0] * 1e3, 3), "GBps": round(gbps, 2),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
+            "kernel_frac_of_read": round(best[0] / kernel_ms, 4)}
 
 
 def bench_prefill(qmm, dev, stream, args):
