@@ -102,7 +102,13 @@ struct CtSlot {
   uint32_t sw, zw;
 };
 
-template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS>
+// STAGE: the workgroup first copies the 16 activation rows (rows past M as
+// zeros) into LDS, padded by 16 bytes per row so that the 16 rows of a
+// fragment read fall in distinct banks, and its waves read them there;
+// otherwise every wave loads its rows from memory with each chunk.  With
+// CS = 4 column slices per workgroup the staged rows serve 4 waves each,
+// cutting the activation reads from L2 fourfold at M = 16.
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE>
 __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
@@ -119,6 +125,8 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   extern __shared__ float smem_ct[];
   float* saT = smem_ct;                         // [kb][16]: sa of row r, block b (0 past Mp)
   float* red = smem_ct + kb * 16;               // [W][16 x 16] partial sums
+  const int qrow = Kp + 16;                     // STAGE: bytes per staged row
+  int8_t* qs = reinterpret_cast<int8_t*>(red + CS * S * 256);   // STAGE: [16][qrow]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
       sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * (TG * CB), 0, 0),
                       0u, 0u, 0u};
     }
-    sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);
+    if constexpr (!STAGE) sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);
     const int si = (grp * kb + (c >> log2_cpb)) * TG + col;
     sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (si * SZ) & ~3, 0, 0);
     if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, ((si * BITS) >> 5) * 4, 0, 0);
@@ -177,7 +185,16 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   CtSlot sl[CT_D];
 #pragma unroll
   for (int q = 0; q < CT_D; ++q) issue(sl[q], q);
-  __syncthreads();   // saT staged
+  if constexpr (STAGE) {
+    // 16-byte pieces of the 16 rows (rows past Mp read zeros).
+    const int ppr = Kp / 16;
+    for (int i = threadIdx.x; i < 16 * ppr; i += blockDim.x) {
+      const int r = i / ppr, c16 = i - r * ppr;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, r < Mp ? r * Kp + c16 * 16 : 0x7FFFFFF0, 0, 0);
+      *reinterpret_cast<u32x4*>(qs + r * qrow + c16 * 16) = v;
+    }
+  }
+  __syncthreads();   // saT (and the activation rows) staged
 
   const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
   f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -185,7 +202,12 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   // Chunk j: two MFMAs; at the block's last chunk the epilogue scales it.
   auto consume = [&](const CtSlot& sl, int j) {
     const i32x4 bv = unpack_codes<BITS>(sl.code);
-    const i32x4 av = permute_acts<BITS>(sl.act);
+    u32x4 raw_act;
+    if constexpr (STAGE)
+      raw_act = *reinterpret_cast<const u32x4*>(qs + rowA * qrow + (c_lo + j) * TKC + g * 16);
+    else
+      raw_act = sl.act;
+    const i32x4 av = permute_acts<BITS>(raw_act);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
     asum = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones, asum, 0, 0, 0);
     if (((j + 1) & (cpb - 1)) == 0) {
@@ -243,7 +265,14 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   (void)W;
 }
 
-template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS>
+// LDS bytes of a launch: sa [kb][16], the share sums [CS * S][256], and for
+// STAGE the 16 padded activation rows.
+static size_t ct_lds(int64_t kb, int64_t Kp, int CS, int S, bool stage) {
+  return (size_t)(kb * 16 + CS * S * 256) * 4 + (stage ? (size_t)16 * (Kp + 16) : 0);
+}
+constexpr size_t CT_STAGE_LDS_MAX = 128 * 1024;
+
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE>
 hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
   const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
                                   a.zp != nullptr);
@@ -251,17 +280,30 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   const int log2_cpb = __builtin_ctz((unsigned)(a.block_size / TKC));
   const int n_slices = (int)tg.groups * 2;
   const int Kp = (int)(a.kb * a.block_size);
-  // Two slices (one group) per workgroup, shares of K until a workgroup has
-  // 8 waves, keeping at least two blocks per share.
-  const int CS = 2;
+  // Unstaged: two slices (one group) per workgroup, shares of K until a
+  // workgroup has 8 waves.  Staged: four slices sharing the staged rows,
+  // shares until 16 waves.  Both keep at least two blocks per share.
+  const int CS = STAGE ? 4 : 2;
+  const int maxw = STAGE ? 16 : 8;
   int S = 1;
-  while (CS * S < 8 && (a.kb + 2 * S - 1) / (2 * S) >= 2) S *= 2;
-  const size_t lds = (size_t)(a.kb * 16 + CS * S * 256) * 4;
+  while (CS * S < maxw && (a.kb + 2 * S - 1) / (2 * S) >= 2) S *= 2;
+  const size_t lds = ct_lds(a.kb, Kp, CS, S, STAGE);
+  auto kern = compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE>;
+  if (lds > 64 * 1024) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)CT_STAGE_LDS_MAX);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
   const int grid = (n_slices + CS - 1) / CS;
   using YT = typename dt<YDT>::T;
   for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
     const int Mp = (int)std::min<int64_t>(16, a.M - m0);
-    hipLaunchKernelGGL((compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS>), dim3(grid),
+    hipLaunchKernelGGL(kern, dim3(grid),
                        dim3(CS * S * 64), lds, a.stream, qa + m0 * Kp, sa + m0 * a.kb,
                        a.B + tg.codes_off, (const uint8_t*)a.scales, a.zp, (const YT*)a.bias,
                        DOTS ? nullptr : (YT*)a.Y + m0 * a.N,
@@ -275,8 +317,21 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
 
 template <int BITS, int SDT, int YDT, bool DOTS>
 hipError_t launch_z(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
-  return a.zp ? launch_t<BITS, SDT, YDT, true, DOTS>(a, qa, sa, dots)
-              : launch_t<BITS, SDT, YDT, false, DOTS>(a, qa, sa, dots);
+  // Staged rows above 4 rows, when they fit (the block-dot export keeps the
+  // plain form).  At 4 rows the activation reads are small next to the
+  // codes, and the 4-slice workgroups leave compute units idle (224 for
+  // N = 14336): measured at K = 4096, N = 14336, M = 16 staging takes
+  // 17.2 -> 13.5 us (4-bit), 20.7 -> 18.5 (8-bit), 19.0 -> 15.0 (2-bit); at
+  // M = 4 it gains 0.3 us for 2/4-bit and loses 1.0 us for 8-bit.
+  const int64_t Kp = a.kb * a.block_size;
+  const bool stage = !DOTS && a.M > 4 && ct_lds(a.kb, Kp, 4, 4, true) <= CT_STAGE_LDS_MAX;
+  if constexpr (!DOTS) {
+    if (stage)
+      return a.zp ? launch_t<BITS, SDT, YDT, true, false, true>(a, qa, sa, dots)
+                  : launch_t<BITS, SDT, YDT, false, false, true>(a, qa, sa, dots);
+  }
+  return a.zp ? launch_t<BITS, SDT, YDT, true, DOTS, false>(a, qa, sa, dots)
+              : launch_t<BITS, SDT, YDT, false, DOTS, false>(a, qa, sa, dots);
 }
 
 template <int BITS, int SDT, bool DOTS>

@@ -131,10 +131,13 @@ def test_few_rows_long_k_and_lds_limit(bits):
     """M = 2 and 3 with K long enough for several wave loads per share, an
     M = 1 row whose quantized activations nearly fill the fused kernel's LDS
     budget, and one past it (which takes the quantize-then-matrix-core route
-    on the tiled layout)."""
+    on the tiled layout); M > 4 with the activation rows staged in LDS (33
+    rows: three launches of 16, 16 and 1 rows) and with rows too long to
+    stage."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
     for i, (M, K, N, bs) in enumerate([(2, 4096, 300, 64), (3, 4104, 96, 128),
-                                       (1, 40000, 65, 64), (1, 60000, 64, 128)]):
+                                       (1, 40000, 65, 64), (1, 60000, 64, 128),
+                                       (33, 4096, 100, 128), (20, 10000, 64, 64)]):
         case = make_matmul_case(M, K, N, bs, bits, a_dtype="bf16", has_zp=True, has_bias=True,
                                 seed=500 + 10 * bits + i)
         r = check_all(case, f"rows/long K b{bits}")
