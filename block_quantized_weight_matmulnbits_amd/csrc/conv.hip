@@ -44,6 +44,11 @@ __device__ __forceinline__ void divmod_small(int n, int d, float inv_d, int& q, 
 // any of them, from addresses that are always valid (out-of-image taps and
 // the tail past K read element 0 and are replaced afterwards), so the loads
 // stay free of branches and their latency is paid once per batch.
+// V16: C % 16 == 0 and 16-byte aligned tensors, so a lane's 16 reduction
+// indices of a step lie in one tap and are 16 contiguous bytes of both the
+// input pixel and the weight row: one 16-byte load each instead of four
+// 4-byte loads.
+template <bool V16>
 __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wt, const int32_t* __restrict__ bias,
     const float* __restrict__ w_scale, float in_scale, float out_scale, int in_zp, int out_zp,
@@ -78,11 +83,47 @@ __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
   }
   const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
+  // The epilogue's per-channel bias and requantization multiplier, loaded
+  // before the reduction so their latency hides under it.
+  int bias_t[CONV_NT];
+  float mult_t[CONV_NT];
+#pragma unroll
+  for (int t = 0; t < CONV_NT; ++t) {
+    const int oc = oc0 + t * 16 + li;
+    const int occ = oc < Co ? oc : 0;
+    bias_t[t] = bias ? bias[occ] : 0;
+    mult_t[t] = (in_scale * w_scale[occ]) / out_scale;   // binary32, IEEE division
+  }
+
   for (int ks0 = ks_lo; ks0 < ks_hi; ks0 += CONV_BATCH) {
     uint32_t av[CONV_BATCH][4], bv[CONV_BATCH][CONV_NT][4];
     uint32_t ain = 0, kin = 0;       // bit 4 s + j: inside the image / k < K
 #pragma unroll
     for (int s = 0; s < CONV_BATCH; ++s) {
+      if constexpr (V16) {
+        // The lane's 16 indices: one tap, channels c .. c + 15 (K % 16 == 0,
+        // so the group is all in or all out).
+        const int k = (ks0 + s) * 64 + g * 16;
+        const bool k_ok = k < K;
+        int tap, c, kh, kw;
+        divmod_small(k_ok ? k : 0, C, inv_c, tap, c);
+        divmod_small(tap, KW, inv_kw, kh, kw);
+        const int ih = oh * sh - ph + kh, iw = ow * sw - pw + kw;
+        const bool inside = p_ok && k_ok && ih >= 0 && ih < H && iw >= 0 && iw < W;
+        const int64_t xoff = inside ? (((int64_t)nb * H + ih) * W + iw) * C + c : 0;
+        const u32x4 xa = *reinterpret_cast<const u32x4*>(X + xoff);
+        av[s][0] = xa.x; av[s][1] = xa.y; av[s][2] = xa.z; av[s][3] = xa.w;
+        ain |= (inside ? 0xFu : 0u) << (4 * s);
+        kin |= (k_ok ? 0xFu : 0u) << (4 * s);
+#pragma unroll
+        for (int t = 0; t < CONV_NT; ++t) {
+          const int oc = oc0 + t * 16 + li;
+          const bool w_ok = oc < Co && k_ok;
+          const u32x4 wb = *reinterpret_cast<const u32x4*>(Wt + (w_ok ? (int64_t)oc * K + k : 0));
+          bv[s][t][0] = wb.x; bv[s][t][1] = wb.y; bv[s][t][2] = wb.z; bv[s][t][3] = wb.w;
+        }
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // A group of 4 channels (C % 4 == 0, so a group stays in one tap).
@@ -152,8 +193,8 @@ __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
   for (int t = 0; t < CONV_NT; ++t) {
     const int oc = oc0 + t * 16 + li;
     if (oc >= Co) continue;
-    const float mult = (in_scale * w_scale[oc]) / out_scale;   // binary32, IEEE division
-    const int b0 = bias ? bias[oc] : 0;
+    const float mult = mult_t[t];
+    const int b0 = bias_t[t];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int pe = p0 + g * 4 + e;
@@ -172,7 +213,9 @@ hipError_t launch_conv_int8(const ConvArgs& c) {
   const int OW = (c.W + 2 * c.pad_w - c.KW) / c.stride_w + 1;
   const int P = c.Nb * OH * OW;
   dim3 grid((P + 15) / 16, (c.Co + 16 * CONV_NT - 1) / (16 * CONV_NT));
-  hipLaunchKernelGGL(conv_int8_kernel, grid, dim3(64 * CONV_WAVES), 0, c.stream, c.X, c.Wt,
+  const bool v16 = (c.C % 16) == 0 && (((uintptr_t)c.X | (uintptr_t)c.Wt) & 15) == 0;
+  auto kern = v16 ? conv_int8_kernel<true> : conv_int8_kernel<false>;
+  hipLaunchKernelGGL(kern, grid, dim3(64 * CONV_WAVES), 0, c.stream, c.X, c.Wt,
                      c.bias, c.w_scale, c.in_scale, c.out_scale, c.in_zp, c.out_zp, c.clamp_min,
                      c.clamp_max, c.H, c.W, c.C, c.Co, c.KH, c.KW, c.stride_h, c.stride_w,
                      c.pad_h, c.pad_w, OH, OW, P, 1.0f / (float)c.C, 1.0f / (float)c.KW, c.Y);

@@ -48,6 +48,8 @@ def test_conv_workload_bit_exact():
     ((1, 6, 6, 16), (70, 1, 1), (1, 1), (0, 0)),
     ((2, 11, 13, 68), (130, 3, 3), (2, 2), (1, 1)),
     ((1, 4, 20, 64), (64, 3, 3), (1, 3), (0, 2)),
+    ((1, 10, 9, 32), (7, 3, 3), (1, 2), (1, 1)),
+    ((2, 5, 8, 48), (100, 3, 2), (2, 1), (1, 0)),
 ])
 @pytest.mark.parametrize("zps", [(0, 0, -128, 127), (3, -5, -128, 127), (-7, 10, 10, 127),
                                  (120, 0, -20, 90)])
