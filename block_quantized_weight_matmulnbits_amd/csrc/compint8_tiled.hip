@@ -102,12 +102,11 @@ struct CtSlot {
   uint32_t sw, zw;
 };
 
-// STAGE: the workgroup first copies the 16 activation rows (rows past M as
-// zeros) into LDS, padded by 16 bytes per row so that the 16 rows of a
-// fragment read fall in distinct banks, and its waves read them there;
-// otherwise every wave loads its rows from memory with each chunk.  With
-// CS = 4 column slices per workgroup the staged rows serve 4 waves each,
-// cutting the activation reads from L2 fourfold at M = 16.
+// STAGE: the workgroup first copies its Mp activation rows into LDS, padded
+// by 16 bytes per row so that the rows of a fragment read fall in distinct
+// banks, and its waves read them there (rows past Mp as zeros, by a select);
+// otherwise every wave loads its rows from memory with each chunk.  The CS
+// column slices of the workgroup share the staged rows.
 template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE>
 __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ codes,
@@ -188,9 +187,9 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   if constexpr (STAGE) {
     // 16-byte pieces of the 16 rows (rows past Mp read zeros).
     const int ppr = Kp / 16;
-    for (int i = threadIdx.x; i < 16 * ppr; i += blockDim.x) {
+    for (int i = threadIdx.x; i < Mp * ppr; i += blockDim.x) {
       const int r = i / ppr, c16 = i - r * ppr;
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, r < Mp ? r * Kp + c16 * 16 : 0x7FFFFFF0, 0, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, r * Kp + c16 * 16, 0, 0);
       *reinterpret_cast<u32x4*>(qs + r * qrow + c16 * 16) = v;
     }
   }
@@ -203,9 +202,12 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   auto consume = [&](const CtSlot& sl, int j) {
     const i32x4 bv = unpack_codes<BITS>(sl.code);
     u32x4 raw_act;
-    if constexpr (STAGE)
-      raw_act = *reinterpret_cast<const u32x4*>(qs + rowA * qrow + (c_lo + j) * TKC + g * 16);
-    else
+    if constexpr (STAGE) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qs + min(rowA, Mp - 1) * qrow +
+                                                      (c_lo + j) * TKC + g * 16);
+      raw_act = rowA < Mp ? v : u32x4{0u, 0u, 0u, 0u};
+    } else
+
       raw_act = sl.act;
     const i32x4 av = permute_acts<BITS>(raw_act);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
@@ -266,9 +268,9 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
 }
 
 // LDS bytes of a launch: sa [kb][16], the share sums [CS * S][256], and for
-// STAGE the 16 padded activation rows.
-static size_t ct_lds(int64_t kb, int64_t Kp, int CS, int S, bool stage) {
-  return (size_t)(kb * 16 + CS * S * 256) * 4 + (stage ? (size_t)16 * (Kp + 16) : 0);
+// STAGE the rows padded activation rows.
+static size_t ct_lds(int64_t kb, int64_t Kp, int CS, int S, bool stage, int rows) {
+  return (size_t)(kb * 16 + CS * S * 256) * 4 + (stage ? (size_t)rows * (Kp + 16) : 0);
 }
 constexpr size_t CT_STAGE_LDS_MAX = 128 * 1024;
 
@@ -280,14 +282,16 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   const int log2_cpb = __builtin_ctz((unsigned)(a.block_size / TKC));
   const int n_slices = (int)tg.groups * 2;
   const int Kp = (int)(a.kb * a.block_size);
-  // Unstaged: two slices (one group) per workgroup, shares of K until a
-  // workgroup has 8 waves.  Staged: four slices sharing the staged rows,
-  // shares until 16 waves.  Both keep at least two blocks per share.
-  const int CS = STAGE ? 4 : 2;
-  const int maxw = STAGE ? 16 : 8;
+  // Two slices (one group) per workgroup, shares of K until a workgroup has
+  // 8 waves; staged above 4 rows, four slices sharing the rows and shares
+  // until 16 waves.  Both keep at least two blocks per share.
+  const bool wide = STAGE && a.M > 4;
+  const int CS = wide ? 4 : 2;
+  const int maxw = wide ? 16 : 8;
   int S = 1;
   while (CS * S < maxw && (a.kb + 2 * S - 1) / (2 * S) >= 2) S *= 2;
-  const size_t lds = ct_lds(a.kb, Kp, CS, S, STAGE);
+  const int rows = (int)std::min<int64_t>(16, a.M);
+  const size_t lds = ct_lds(a.kb, Kp, CS, S, STAGE, rows);
   auto kern = compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE>;
   if (lds > 64 * 1024) {
     static bool attr_set = false;
@@ -317,14 +321,13 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
 
 template <int BITS, int SDT, int YDT, bool DOTS>
 hipError_t launch_z(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
-  // Staged rows above 4 rows, when they fit (the block-dot export keeps the
-  // plain form).  At 4 rows the activation reads are small next to the
-  // codes, and the 4-slice workgroups leave compute units idle (224 for
-  // N = 14336): measured at K = 4096, N = 14336, M = 16 staging takes
-  // 17.2 -> 13.5 us (4-bit), 20.7 -> 18.5 (8-bit), 19.0 -> 15.0 (2-bit); at
-  // M = 4 it gains 0.3 us for 2/4-bit and loses 1.0 us for 8-bit.
+  // Staged rows when they fit (the block-dot export keeps the plain form).
+  // Above 4 rows four slices share them (unstaged, every wave re-read its
+  // 16 rows from L2 with each chunk: 59 MB per call at M = 16, K = 4096,
+  // N = 14336); at up to 4 rows two slices do, which keeps 448 workgroups
+  // for N = 14336 (four would leave 32 compute units idle).
   const int64_t Kp = a.kb * a.block_size;
-  const bool stage = !DOTS && a.M > 4 && ct_lds(a.kb, Kp, 4, 4, true) <= CT_STAGE_LDS_MAX;
+  const bool stage = !DOTS && ct_lds(a.kb, Kp, 4, 4, true, 16) <= CT_STAGE_LDS_MAX;
   if constexpr (!DOTS) {
     if (stage)
       return a.zp ? launch_t<BITS, SDT, YDT, true, false, true>(a, qa, sa, dots)
