@@ -108,10 +108,15 @@ int qmm_gemm(const void *A, int a_dtype, const uint8_t *B, int b_layout,
  * exactly in int32 and Y[m, n] = sum_b float(dot) * (sa[m, b] * scale[n, b])
  * (+ bias[n]) in fp32.
  * workspace: device memory of at least qmm_compint8_workspace_size(M, K,
- * block_size) bytes, 256-byte aligned, owned by the caller, overwritten.
+ * block_size) bytes, 256-byte aligned, owned by the caller, overwritten (it
+ * holds qa and sa between the two launches of the computation; for M = 1 on
+ * the tiled layout the quantization runs inside the one launch and the
+ * workspace is checked but not written).
  * accuracy_level must be 4.  Arguments otherwise as for qmm_gemm.  B may be
  * the tiled buffer of qmm_repack when block_size >= 64 (the block dots then
- * run on the int8 matrix cores); otherwise QMM_ERR_UNSUPPORTED.
+ * run on the int8 matrix cores), and for M = 1 also when block_size is at
+ * least one 16-byte unit of codes (32, 64 or 16 codes for 4, 2 or 8 bits)
+ * and at most 1024; otherwise QMM_ERR_UNSUPPORTED.
  */
 size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size);
 
