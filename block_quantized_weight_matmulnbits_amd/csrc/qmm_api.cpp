@@ -223,8 +223,10 @@ int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout
   if (a.tiled && !small && !qmm::compint8_tiled_supported(a))
     return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8: on the tiled layout CompInt8 needs "
                 "block_size >= 64 (whole 64-code chunks per block) and at most 896 blocks per "
-                "row (got block_size=%d, %lld blocks). How to fix: pass the operator's layout "
-                "(QMM_LAYOUT_ORT) for this weight.", block_size, (long long)a.kb);
+                "row, or M = 1 with a block of at least one 16-byte unit of codes and at most "
+                "1024 codes (got M=%lld, block_size=%d, %lld blocks). How to fix: pass the "
+                "operator's layout (QMM_LAYOUT_ORT) for this weight.", (long long)M, block_size,
+                (long long)a.kb);
   if (M == 0) return QMM_OK;
   st = check_workspace("qmm_gemm_compint8", a, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
