@@ -158,3 +158,17 @@ def test_compint8_tiled_layout_needs_whole_chunks_per_block(qmm):
     st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, FAKE, 1, 4096, 4096, 16,
                                    4, 4, FAKE, 1 << 30, None)
     assert st == -2 and "M = 1" in qmm.qmm_last_error()
+
+
+def test_benchmark_probe_library_exports_its_read_kernel():
+    """bench.py's reference read (libqmm_probe.so, not part of libqmm.so)
+    loads and rejects bad arguments on the host."""
+    path = os.path.join(ROOT, "block_quantized_weight_matmulnbits_amd", "probe", "libqmm_probe.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.qmm_probe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert fn(None, 16, None, 1, None) != 0        # null pointers
+    assert fn(1 << 20, 15, 1 << 20, 1, None) != 0  # not a multiple of 16 bytes
+    assert fn(1 << 20, 16, 1 << 20, 0, None) != 0  # empty grid
+    assert "qmm_probe_stream_read" not in open(
+        os.path.join(ROOT, "include", "qmm.h")).read()   # not part of the matmul ABI
