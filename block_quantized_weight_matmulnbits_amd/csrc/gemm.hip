@@ -159,13 +159,8 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   // make the compiler loop over the lanes for every load).  This thread's
   // column is addressed by offset; a column past N (or a thread with no
   // column) gets an offset past the extent, which reads zeros.
-  // Which thread dequantizes which 32 codes.  Tiled layout: half t / BN of
-  // column t % BN, so adjacent lanes take adjacent columns (their 16-byte
-  // pieces are 32 bytes apart in the group's chunk; measured 0.263 -> 0.244
-  // ms at M=2048, K=4096, N=14336 against half t & 1 of column t >> 1).
-  // Operator layout: half t & 1 of column t >> 1, so adjacent lanes read the
-  // two halves of one column's contiguous 32 bytes (adjacent columns are a
-  // whole row of codes apart there: 0.266 -> 0.315 ms the other way).
+  // Thread t dequantizes half t & 1 (32 codes) of column t >> 1 of the tile,
+  // so adjacent lanes read adjacent 16-byte pieces.
   //   operator layout: codes at n * row_bytes + k * bits / 8; scale (n, b) at
   //     n * kb + b; zero point (n, b) at bit n * zp_row_bytes * 8 + b * bits.
   //   tiled layout (qmm_layout.h): codes at ((g * chunks + c) * 32 + i) *
@@ -174,9 +169,9 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   const int row_bytes = kb << log2_blob;
   constexpr int CHUNK_BYTES = TKC * BITS / 8;
   const bool dq = tid < 2 * BN;                // this thread dequantizes
-  const int bcol = TL ? tid % BN : tid >> 1;
+  const int bcol = tid >> 1;
   const int ncol = n0 + bcol;
-  const int khalf = (TL ? tid / BN : tid & 1) * HK;   // which half of the K-step
+  const int khalf = (tid & 1) * HK;            // which half of the K-step
   const bool ncol_ok = dq && ncol < N;
   const int ngroups = (N + TG - 1) / TG;
   const int code_extent = TL ? ngroups * chunks * TG * CHUNK_BYTES : N * row_bytes;
@@ -208,19 +203,11 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   ST scr[2][2];                      // scales of the (at most 2) blocks of 32 codes
   uint32_t zbr[2][2];                // zero-point bytes of those blocks
 
-  // A tile row of 16-byte chunk c (8 chunks per row).  Tiled layout: the two
-  // 8-lane halves of a 16-lane pass take rows r and r + 8, whose padded LDS
-  // rows start 32 banks apart (a bijection of the 256 rows); operator
-  // layout: rows in order.
-  auto a_row = [](int c) {
-    const int g = c >> 3;
-    return TL ? (g & ~15) | ((g & 1) << 3) | ((g >> 1) & 7) : g;
-  };
   auto load_a = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + i * GEMM_TPB;
-      const int r = a_row(c), kc = (c & 7) * 8;
+      const int r = c >> 3, kc = (c & 7) * 8;
       const int row = m0 + r, k = k0 + kc;
       const bool ok = row < M && k < K;    // K % 8 == 0: a chunk is all in or all out
       av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (row * K + k) * 2 : OOB, 0, 0);
@@ -261,7 +248,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + i * GEMM_TPB;
-      const int r = a_row(c), kc = (c & 7) * 8;
+      const int r = c >> 3, kc = (c & 7) * 8;
       *reinterpret_cast<u32x4*>(&as[r * LDS_ROW + kc]) = av[i];
     }
   };
