@@ -5,16 +5,17 @@
 // weight is dequantized tile by tile inside the kernel and never written to
 // memory).
 //
-// gemm_mfma_kernel (bf16 / f16 activations): a workgroup of 4 waves computes a
-// BM x BN = 256 x 256 tile of Y, each wave 128 x 128 as 8 x 8
+// gemm_mfma_kernel (bf16 / f16 activations): a workgroup of 8 waves computes a
+// 256 x BN tile of Y (BN = 224 or 256), each wave 64 x BN/2 as 4 x BN/32
 // v_mfma_f32_16x16x32_{bf16,f16} tiles accumulated in fp32.  Per K-step of
-// BK = 32: the A tile is copied to LDS, the B tile is dequantized once for
-// the whole workgroup (each thread one output column: unpack codes, subtract
-// the zero point, multiply by the block scale in fp32, round to the activation
+// 64: the A tile is copied to LDS, the B tile is dequantized once for the
+// whole workgroup (each thread 32 codes of one column: unpack, subtract the
+// zero point, multiply by the block scale in fp32, round to the activation
 // dtype) and stored to LDS; then every wave reads its operand fragments from
-// LDS.  LDS rows are padded by 16 bytes so the fragment reads of 16 rows fall
-// in distinct banks.  Loads of A and of the codes go through buffer
-// descriptors whose extents end at M, K and N, so ragged edges read zeros.
+// LDS.  LDS rows are 128 bytes with their 16-byte pieces XOR-permuted by the
+// row (lds_at), so the 16 rows of a fragment read fall in distinct bank
+// groups.  Loads of A and of the codes go through buffer descriptors whose
+// extents end at M, K and N, so ragged edges read zeros.
 //
 // gemm_rows_kernel (fallback: f32 activations, small M, unaligned operands):
 // fp32 throughout -- each wave owns R output columns, stages MT rows of A in
@@ -31,8 +32,19 @@ namespace qmm {
 
 constexpr int GEMM_THREADS = 256;
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int LDS_ROW = GBK + 8;             // padded LDS row, in 16-bit elements
+constexpr int LDS_ROW = GBK;                 // LDS row (128 bytes), in 16-bit elements
 constexpr int STAGE = GBM * LDS_ROW;         // one operand tile, in 16-bit elements
+
+// Element offset of 16-byte piece p (8 elements) of row r of an LDS tile.
+// The 8 pieces of a row are permuted by an XOR with a function of the row's
+// low four bits, so that the 16 rows of a fragment read (same piece) fall in
+// distinct 16-byte bank groups whether a pass serves 8 lanes from 32 banks
+// or 16 lanes from 64 banks; so do the 8 pieces of one row written by 8
+// adjacent lanes.
+__device__ __forceinline__ int lds_at(int r, int p) {
+  const int f = ((r >> 1) & 7) ^ ((r & 1) << 2);
+  return r * LDS_ROW + ((p ^ f) << 3);
+}
 constexpr int BUF_WORD3 = 0x00020000;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -139,8 +151,8 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   constexpr int WPT = HK / P;                  // code words per thread per K-step
   constexpr int TM = 4;                        // MFMA row tiles per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_g[];
-  uint16_t* As = lds_g;                        // [2][GBM][LDS_ROW]
-  uint16_t* Bs = lds_g + 2 * STAGE;            // [2][BN][LDS_ROW]
+  uint16_t* As = lds_g;                        // [2][GBM][LDS_ROW], pieces per lds_at
+  uint16_t* Bs = lds_g + 2 * STAGE;            // [2][BN][LDS_ROW], pieces per lds_at
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -249,7 +261,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     for (int i = 0; i < 4; ++i) {
       const int c = tid + i * GEMM_TPB;
       const int r = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&as[r * LDS_ROW + kc]) = av[i];
+      *reinterpret_cast<u32x4*>(&as[lds_at(r, kc >> 3)]) = av[i];
     }
   };
   // Dequantize register stage `st` (step starting at k0) into LDS buffer buf.
@@ -295,7 +307,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     }
 #pragma unroll
     for (int j = 0; j < HK / 8; ++j)
-      *reinterpret_cast<u32x4*>(&bs[bcol * LDS_ROW + khalf + 8 * j]) =
+      *reinterpret_cast<u32x4*>(&bs[lds_at(bcol, (khalf >> 3) + j)]) =
           u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
   };
 
@@ -315,11 +327,11 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         af[i] = __builtin_bit_cast(typename Op::V,
-                                   *reinterpret_cast<const u32x4*>(&as[(wm + i * 16 + fr) * LDS_ROW + kk + fk]));
+                                   *reinterpret_cast<const u32x4*>(&as[lds_at(wm + i * 16 + fr, (kk + fk) >> 3)]));
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const typename Op::V bf = __builtin_bit_cast(
-            typename Op::V, *reinterpret_cast<const u32x4*>(&bs[(wn + j * 16 + fr) * LDS_ROW + kk + fk]));
+            typename Op::V, *reinterpret_cast<const u32x4*>(&bs[lds_at(wn + j * 16 + fr, (kk + fk) >> 3)]));
 #pragma unroll
         for (int i = 0; i < TM; ++i) acc[i][j] = Op::run(af[i], bf, acc[i][j]);
       }
