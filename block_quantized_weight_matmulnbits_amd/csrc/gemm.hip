@@ -122,8 +122,8 @@ __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
 // rounds of 256 workgroups).  8 waves, two per SIMD so one wave's waits hide
 // under the other's MFMAs, arranged 4 (M) x 2 (N); each wave owns 64 x 16*TN
 // outputs as 4 x TN v_mfma_f32_16x16x32 tiles.
-// Per K-step of GBK = 64: thread t dequantizes 32 codes of column t % BN
-// (half t / BN of the step); threads t >= 2 * BN only copy A.
+// Per K-step of GBK = 64: thread t dequantizes 32 codes of column t >> 1
+// (half t & 1 of the step); threads t >= 2 * BN only copy A.
 // Pipeline: A chunks are prefetched into registers one step ahead, the codes,
 // scales and zero points two steps ahead (register stage = step parity, fixed
 // at compile time by unrolling the loop by two); the next step is written to
