@@ -172,3 +172,14 @@ def test_benchmark_probe_library_exports_its_read_kernel():
     assert fn(1 << 20, 16, 1 << 20, 0, None) != 0  # empty grid
     assert "qmm_probe_stream_read" not in open(
         os.path.join(ROOT, "include", "qmm.h")).read()   # not part of the matmul ABI
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus 2 exits with status 2 and says so,
+    before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
