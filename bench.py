@@ -67,6 +67,9 @@ def parse():
                         "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
+    p.add_argument("--read-sweep", action="store_true",
+                   help="only sweep the plain streaming read (bench_probe/) over launch shapes "
+                        "and sizes and print a markdown table")
     return p.parse_args()
 
 
@@ -88,6 +91,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.read_sweep:
+        read_sweep(dev, torch.cuda.current_stream(dev))
+        return
     if args.copy_calibration:
         src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -304,43 +310,128 @@ def _time_launches(fn, n, stream):
     return e0.elapsed_time(e1) / n
 
 
-def read_ceiling(dev, stream, nbytes, kernel_ms):
-    """Time a plain streaming read of nbytes (the probe library's kernel:
-    non-temporal 16-byte loads, grid-stride, nothing else) over rotating
-    buffers, as the dominant kernel's launches are timed: what one launch
-    needs just to read that many bytes here.  None if the probe library was
-    not built."""
-    import ctypes
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                        "block_quantized_weight_matmulnbits_amd", "probe", "libqmm_probe.so")
-    if not os.path.exists(path):
-        return None
-    lib = ctypes.CDLL(path)
-    lib.qmm_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                          ctypes.c_int, ctypes.c_void_p]
-    nb = nbytes // 16 * 16
-    copies = max(2, -(-POOL_BYTES // nb))
-    bufs = [torch.full((nb,), i, dtype=torch.uint8, device=dev) for i in range(copies)]
-    best = None
-    for grid in (1024, 2048):
-        out = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+READ_SWEEP = [(grid, block, unroll, nt, slab)
+              for grid in (256, 512, 1024, 2048)
+              for block in (256, 512, 1024)
+              for unroll in (2, 4, 8, 16)
+              for nt in (1, 0)
+              for slab in (1, 0)]
 
-        def run(i, grid=grid, out=out):
-            rc = lib.qmm_probe_stream_read(bufs[i % copies].data_ptr(), nb, out.data_ptr(), grid,
-                                           ctypes.c_void_p(stream.cuda_stream))
+
+class ReadProbe:
+    """The plain streaming read of bench_probe/ (its own library): times one
+    launch reading n bytes over rotating buffers (> 2x the Infinity Cache),
+    as the matmul kernels' launches are timed."""
+
+    def __init__(self, dev, stream):
+        import ctypes
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bench_probe",
+                            "libqmm_probe.so")
+        if not os.path.exists(path):
+            raise FileNotFoundError(path)
+        self.lib = ctypes.CDLL(path)
+        c = ctypes
+        self.lib.qmm_probe_stream_read.argtypes = [c.c_void_p, c.c_int64, c.c_void_p, c.c_int64,
+                                                   c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
+                                                   c.c_void_p]
+        self.dev, self.stream = dev, stream
+        self.out = torch.empty(2048 * 1024, dtype=torch.int32, device=dev)
+        self.nb = None
+
+    def _buffers(self, nbytes):
+        if self.nb != nbytes:
+            self.bufs = None
+            copies = max(2, -(-POOL_BYTES // nbytes))
+            self.bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device=self.dev)
+                         for i in range(copies)]
+            self.nb = nbytes
+        return self.bufs
+
+    def ms(self, nbytes, cfg, launches=100):
+        import ctypes
+        nbytes = nbytes // 16 * 16
+        bufs = self._buffers(nbytes)
+        grid, block, unroll, nt, slab = cfg
+
+        def run(i):
+            rc = self.lib.qmm_probe_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes,
+                                                self.out.data_ptr(), self.out.numel(), grid,
+                                                block, unroll, nt, slab,
+                                                ctypes.c_void_p(self.stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"stream read probe failed: {rc}")
 
-        ms = _time_launches(run, 100, stream)
+        return _time_launches(run, launches, self.stream)
+
+    def release(self):
+        self.bufs, self.nb = None, None
+
+
+def _cfg_name(cfg):
+    grid, block, unroll, nt, slab = cfg
+    return (f"{grid} x {block} threads, {unroll} 16-byte loads in flight per lane, "
+            f"{'non-temporal' if nt else 'plain'} loads, "
+            f"{'one contiguous slab per workgroup' if slab else 'grid-stride'}")
+
+
+def read_ceiling(dev, stream, nbytes, kernel_ms):
+    """The fastest plain streaming read of nbytes over READ_SWEEP (grid,
+    workgroup size, loads in flight per lane, non-temporal or plain loads,
+    grid-stride or slab order): what one launch needs just to read that many
+    bytes here.  None if the probe library was not built."""
+    try:
+        probe = ReadProbe(dev, stream)
+    except FileNotFoundError:
+        return None
+    best = None
+    for cfg in READ_SWEEP:
+        ms = probe.ms(nbytes, cfg, launches=50)
         if best is None or ms < best[0]:
-            best = (ms, grid)
-    del bufs
-    gbps = nb / (best[0] * 1e-3) / 1e9
-    return {"what": "plain streaming read of the same bytes (non-temporal 16-byte loads, "
-                    f"{best[1]} x 256 threads), one launch per buffer, rotating buffers",
-            "bytes": nb, "us": round(best[0] * 1e3, 3), "GBps": round(gbps, 2),
+            best = (ms, cfg)
+    # Re-time the winner with as many launches as the kernel's own series.
+    ms = probe.ms(nbytes, best[1], launches=100)
+    probe.release()
+    nb = nbytes // 16 * 16
+    gbps = nb / (ms * 1e-3) / 1e9
+    return {"what": "fastest plain streaming read of the same bytes over "
+                    f"{len(READ_SWEEP)} launch shapes: {_cfg_name(best[1])}; one launch per "
+                    "buffer, rotating buffers",
+            "bytes": nb, "us": round(ms * 1e3, 3), "GBps": round(gbps, 2),
             "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
-            "kernel_frac_of_read": round(best[0] / kernel_ms, 4)}
+            "kernel_frac_of_read": round(ms / kernel_ms, 4)}
+
+
+def read_sweep(dev, stream):
+    """--read-sweep: every READ_SWEEP shape at several read sizes; prints a
+    markdown table (the summary kept under profiles/)."""
+    probe = ReadProbe(dev, stream)
+    sizes = [(29360128, "codes of one 4096x14336 4-bit projection"),
+             (67960832, "gate|up GEMV bytes"),
+             (126255104, "decode layer bytes"),
+             (536870912, "512 MiB")]
+    print("| bytes | what | best us | best GB/s | frac of 8 TB/s | best shape | "
+          "best non-temporal | best plain | best stride | best slab |", flush=True)
+    print("|---|---|---|---|---|---|---|---|---|---|", flush=True)
+    for nb, what in sizes:
+        res = []
+        for cfg in READ_SWEEP:
+            res.append((probe.ms(nb, cfg, launches=50 if nb < (256 << 20) else 10), cfg))
+        gb = lambda ms: nb / (ms * 1e-3) / 1e9
+        best = min(res)
+        sub = lambda f: min(r for r in res if f(r[1]))
+        print(f"| {nb} | {what} | {best[0] * 1e3:.2f} | {gb(best[0]):.0f} | "
+              f"{gb(best[0]) / HBM_PEAK_GBS:.3f} | {_cfg_name(best[1])} | "
+              f"{gb(sub(lambda c: c[3] == 1)[0]):.0f} | {gb(sub(lambda c: c[3] == 0)[0]):.0f} | "
+              f"{gb(sub(lambda c: c[4] == 0)[0]):.0f} | {gb(sub(lambda c: c[4] == 1)[0]):.0f} |",
+              flush=True)
+        # Per loads-in-flight and per grid: the best over the other knobs.
+        for key, idx in (("loads in flight per lane", 2), ("workgroups", 0),
+                         ("threads per workgroup", 1)):
+            vals = sorted({c[idx] for _, c in res})
+            cells = ", ".join(f"{v}: {gb(min(r for r in res if r[1][idx] == v)[0]):.0f}"
+                              for v in vals)
+            print(f"|  | best GB/s by {key} | {cells} | | | | | | | |", flush=True)
+    probe.release()
 
 
 def bench_prefill(qmm, dev, stream, args):

@@ -16,9 +16,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmm.so")
-# The benchmark's reference kernel (a plain streaming read), its own library.
-PROBE_SRC = os.path.join(HERE, "probe", "stream_read.hip")
-PROBE_LIB = os.path.join(HERE, "probe", "libqmm_probe.so")
 ROOT = os.path.dirname(HERE)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -60,21 +57,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(sources)} sources")
-    build_probe(verbose)
     return LIB
-
-
-def build_probe(verbose: bool = False) -> str:
-    """Compile the streaming-read reference kernel into libqmm_probe.so."""
-    tmp = PROBE_LIB + ".tmp"
-    cmd = [HIPCC, *COMMON, "-shared", "-o", tmp, PROBE_SRC]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, PROBE_LIB)
-    if verbose:
-        print(f"built {PROBE_LIB}")
-    return PROBE_LIB
 
 
 if __name__ == "__main__":

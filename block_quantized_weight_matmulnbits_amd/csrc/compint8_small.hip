@@ -26,8 +26,16 @@
 // same plane order, v_dot4_i32_i8 multiplies four pairs at a time, and the
 // zero point is removed per unit with the unit's sum of activations:
 //   sum qa * (code - zp) = sum qa * code' - (zp - off) * sum qa
-// (off = 128 for 8-bit codes, else 0).  Each unit's dot is scaled by
-// sa * scale in fp32 and summed.
+// (off = 128 for 8-bit codes, else 0).  The units of one block are added in
+// int32 before any scaling, so the block dot of the definition exists as an
+// exact integer: a load holds 8 units of each column (lane bits for the unit
+// within the chunk and for the chunk), the units of a block are combined by
+// integer lane exchanges over those bits, and a block wider than one load
+// (8 units) carries its int32 sum from load to load.  The block's leading
+// lane then adds float(dot) * (sa * scale) once.  A share of K per wave is a
+// whole number of blocks, so no block is split between waves.  The DOTS
+// variant writes the int32 block dots and, from workgroup 0, the quantized
+// activations and scales it computed in LDS.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 #include "qmm_layout.h"
@@ -144,15 +152,35 @@ __device__ __forceinline__ void cs_planes(uint32_t w, int* out) {
   }
 }
 
-template <int BITS, bool HAS_ZP, int MR, int XDT>
+// v from the lane whose index differs from this lane's in bit mask MASK (an
+// integer exchange: DPP within a quad, a swizzle within 32 lanes, a
+// permute across the halves of the wave).
+template <int MASK>
+__device__ __forceinline__ int cs_xor(int v) {
+  if constexpr (MASK == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (MASK == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (MASK < 32) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (MASK << 10));
+  else return __shfl_xor(v, MASK);
+}
+
+// Lane-index bit that holds bit i of a lane's unit index q = chunk * UPC + u
+// within its column's 8 units of a load: the unit bits are the lowest lane
+// bits, the chunk bits sit above the 8 columns' lanes.
+template <int LOG_UPC>
+constexpr int cs_unit_bit_mask(int i) { return i < LOG_UPC ? (1 << i) : (1 << (i + 3)); }
+
+template <int BITS, bool HAS_ZP, int MR, int XDT, bool DOTS>
 __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
     const void* __restrict__ x, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
     const void* __restrict__ bias, void* __restrict__ Y, int Mp, int K, int N, int kb,
-    int chunks, int log2_bs, int n_oct, int O, int S, int s_dtype) {
+    int chunks, int log2_bs, int n_oct, int O, int S, int s_dtype,
+    int32_t* __restrict__ dots, int8_t* __restrict__ qa_out, float* __restrict__ sa_out) {
   using G = CsGeom<BITS>;
   constexpr int P = G::P, E = G::E, CB = G::CB, UPC = G::UPC, LPC = G::LPC, CPL = G::CPL,
                 PPU = G::PPU;
+  constexpr int LOG_UPC = UPC == 1 ? 0 : (UPC == 2 ? 1 : 2);
+  static_assert(CPL * UPC == 8, "a wave load holds 8 units of each of its 8 columns");
   constexpr uint32_t zmask = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
   constexpr int OFF = (BITS == 8) ? 128 : 0;
   constexpr int NPL = (BITS == 4) ? 2 : (BITS == 2 ? 4 : 1);   // planes per code word
@@ -194,8 +222,14 @@ __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
       (void*)x, 0, Mp * K * XB, CS_RSRC3);
   const bool x_vec = XDT != DT_F32 && (K % 8) == 0 && (((uintptr_t)x) & 15) == 0;
 
-  // This wave's share of the chunks: whole wave loads.
-  const int cs = (chunks + S * CPL - 1) / (S * CPL) * CPL;
+  // Units of a block in one load (log2, at most 8 units = 3) and whether a
+  // block spans several loads.
+  const int log2_ub = log2_bs - __builtin_ctz(E);   // block_size >= E
+  const int log2_rb = min(log2_ub, 3);
+  const bool multi_load = log2_ub > 3;
+  // This wave's share of the chunks: whole wave loads and whole blocks.
+  const int share_step = max(CPL, (1 << log2_bs) / TKC);
+  const int cs = (chunks + S * share_step - 1) / (S * share_step) * share_step;
   const int c_lo = s * cs;
   const int c_hi = has_oct ? min(chunks, c_lo + cs) : c_lo;
   const int nloads = c_hi > c_lo ? (c_hi - c_lo + CPL - 1) / CPL : 0;
@@ -263,14 +297,30 @@ __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
         // Pieces past the last block (the chunk padding of short blocks)
         // hold zeros and no scale.
         if ((p % bsp) == 0 && (k0 >> log2_bs) < kb) sa[r * kb + (k0 >> log2_bs)] = scale;
+        if constexpr (DOTS) {
+          // Workgroup 0 exports the quantization in natural order:
+          // qa_out [Mp, kb * bs], sa_out [Mp, kb].
+          const int kbbs = kb << log2_bs;
+          if (blockIdx.x == 0 && k0 < kbbs) {
+            *reinterpret_cast<u32x4*>(qa_out + r * kbbs + k0) = cs_permute<8>(q);
+            if ((p % bsp) == 0) sa_out[r * kb + (k0 >> log2_bs)] = scale;
+          }
+        }
       }
     }
   }
   __syncthreads();
 
   float acc[MR];
+  int dsum[MR];                  // int32 sum of the current block (multi-load blocks)
 #pragma unroll
-  for (int r = 0; r < MR; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < MR; ++r) {
+    acc[r] = 0.0f;
+    dsum[r] = 0;
+  }
+  // The lane that adds its block's scaled dot: unit 0 of the block in a load.
+  const int q_unit = cl * UPC + u;
+  const bool leader = (q_unit & ((1 << log2_rb) - 1)) == 0;
 
   // Load j: the lane's unit starts at k = lane_k + j * CPL * 64.
   auto compute = [&](const Slot& sl, int j, bool masked) {
@@ -292,6 +342,10 @@ __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
     for (int w = 0; w < 4; ++w) cs_planes<BITS>(cw[w], pl[w]);
     const int c = c_lo + j * CPL + cl;
     const bool live = !masked || (c < c_hi && (k >> log2_bs) < kb);
+    // A multi-load block ends after this load at the next block boundary or
+    // at the share's last load; other blocks end within the load.
+    const bool flush = !multi_load || j == nloads - 1 ||
+                       ((k + CPL * TKC) >> log2_bs) != (k >> log2_bs);
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       if (r >= Mp) break;
@@ -311,8 +365,22 @@ __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
         }
       }
       d -= zo * sq[r * su + k / E];
-      const float t = fmaf((float)d, sa[r * kb + b] * sc, acc[r]);
-      acc[r] = live ? t : acc[r];
+      d = live ? d : 0;
+      // Integer sum over the block's units of this load (the reduction
+      // conditions are uniform across the wave).
+      if (log2_rb > 0) d += cs_xor<cs_unit_bit_mask<LOG_UPC>(0)>(d);
+      if (log2_rb > 1) d += cs_xor<cs_unit_bit_mask<LOG_UPC>(1)>(d);
+      if (log2_rb > 2) d += cs_xor<cs_unit_bit_mask<LOG_UPC>(2)>(d);
+      dsum[r] += d;
+      if (flush) {
+        const bool add = leader && live;
+        const float t = fmaf((float)dsum[r], sa[r * kb + b] * sc, acc[r]);
+        acc[r] = add ? t : acc[r];
+        if constexpr (DOTS) {
+          if (add && has_oct && n < N) dots[((int64_t)r * N + n) * kb + (k >> log2_bs)] = dsum[r];
+        }
+        dsum[r] = 0;
+      }
     }
   };
 
@@ -336,6 +404,7 @@ __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
 #pragma unroll
     for (int st = LPC; st < 64; st *= 2) acc[r] += __shfl_xor(acc[r], st);
   }
+  if constexpr (DOTS) return;
   const bool writer = lane < LPC && u == 0;
   if (writer)
 #pragma unroll
@@ -369,11 +438,13 @@ bool cs_fits(const MatArgs& a, int* O_out, int* S_out, size_t* lds_out) {
   if (O_out) *O_out = O;
   if (S_out) *S_out = S;
   if (lds_out) *lds_out = (size_t)L.total;
-  return L.total <= CS_LDS_MAX && tg.total + 16 * 4096 < 0x7FFFFF00LL;
+  // 32-bit buffer offsets: shares rounded up to whole blocks may start past
+  // the last chunk (by at most 8 shares of 16 chunks), and loads run 4 ahead.
+  return L.total <= CS_LDS_MAX && tg.total + (1 << 20) < 0x7FFFFF00LL;
 }
 
-template <int BITS, bool HAS_ZP, int MR, int XDT>
-hipError_t cs_launch(const MatArgs& a) {
+template <int BITS, bool HAS_ZP, int MR, int XDT, bool DOTS>
+hipError_t cs_launch(const MatArgs& a, int32_t* dots, int8_t* qa_out, float* sa_out) {
   int O = 1, S = 1;
   size_t lds = 0;
   cs_fits<BITS>(a, &O, &S, &lds);
@@ -381,25 +452,36 @@ hipError_t cs_launch(const MatArgs& a) {
                                   a.zp != nullptr);
   const int n_oct = (int)tg.groups * (TG / CS_OCT);
   const int grid = (n_oct + O - 1) / O;
-  hipLaunchKernelGGL((compint8_small_kernel<BITS, HAS_ZP, MR, XDT>), dim3(grid), dim3(O * S * 64),
-                     lds, a.stream, a.A, a.B + tg.codes_off, (const uint8_t*)a.scales, a.zp,
-                     a.bias, a.Y, (int)a.M, (int)a.K, (int)a.N, (int)a.kb, (int)tg.chunks,
-                     __builtin_ctz((unsigned)a.block_size), n_oct, O, S, a.s_dtype);
+  hipLaunchKernelGGL((compint8_small_kernel<BITS, HAS_ZP, MR, XDT, DOTS>), dim3(grid),
+                     dim3(O * S * 64), lds, a.stream, a.A, a.B + tg.codes_off,
+                     (const uint8_t*)a.scales, a.zp, a.bias, a.Y, (int)a.M, (int)a.K, (int)a.N,
+                     (int)a.kb, (int)tg.chunks, __builtin_ctz((unsigned)a.block_size), n_oct, O,
+                     S, a.s_dtype, dots, qa_out, sa_out);
   return hipGetLastError();
 }
 
-template <int BITS, bool HAS_ZP, int MR>
-hipError_t cs_launch_x(const MatArgs& a) {
+template <int BITS, bool HAS_ZP, int MR, bool DOTS>
+hipError_t cs_launch_x(const MatArgs& a, int32_t* dots, int8_t* qa_out, float* sa_out) {
   switch (a.a_dtype) {
-    case DT_F32: return cs_launch<BITS, HAS_ZP, MR, DT_F32>(a);
-    case DT_F16: return cs_launch<BITS, HAS_ZP, MR, DT_F16>(a);
-    default: return cs_launch<BITS, HAS_ZP, MR, DT_BF16>(a);
+    case DT_F32: return cs_launch<BITS, HAS_ZP, MR, DT_F32, DOTS>(a, dots, qa_out, sa_out);
+    case DT_F16: return cs_launch<BITS, HAS_ZP, MR, DT_F16, DOTS>(a, dots, qa_out, sa_out);
+    default: return cs_launch<BITS, HAS_ZP, MR, DT_BF16, DOTS>(a, dots, qa_out, sa_out);
   }
 }
 
-template <int BITS>
-hipError_t cs_launch_z(const MatArgs& a) {
-  return a.zp ? cs_launch_x<BITS, true, 1>(a) : cs_launch_x<BITS, false, 1>(a);
+template <int BITS, bool DOTS>
+hipError_t cs_launch_z(const MatArgs& a, int32_t* dots, int8_t* qa_out, float* sa_out) {
+  return a.zp ? cs_launch_x<BITS, true, 1, DOTS>(a, dots, qa_out, sa_out)
+              : cs_launch_x<BITS, false, 1, DOTS>(a, dots, qa_out, sa_out);
+}
+
+template <bool DOTS>
+hipError_t cs_launch_b(const MatArgs& a, int32_t* dots, int8_t* qa_out, float* sa_out) {
+  switch (a.bits) {
+    case 2: return cs_launch_z<2, DOTS>(a, dots, qa_out, sa_out);
+    case 4: return cs_launch_z<4, DOTS>(a, dots, qa_out, sa_out);
+    default: return cs_launch_z<8, DOTS>(a, dots, qa_out, sa_out);
+  }
 }
 
 }  // namespace
@@ -417,11 +499,11 @@ bool compint8_small_supported(const MatArgs& a) {
 }
 
 hipError_t launch_compint8_small(const MatArgs& a) {
-  switch (a.bits) {
-    case 2: return cs_launch_z<2>(a);
-    case 4: return cs_launch_z<4>(a);
-    default: return cs_launch_z<8>(a);
-  }
+  return cs_launch_b<false>(a, nullptr, nullptr, nullptr);
+}
+
+hipError_t launch_compint8_small_dots(const MatArgs& a, int8_t* qa, float* sa, int32_t* dots) {
+  return cs_launch_b<true>(a, dots, qa, sa);
 }
 
 }  // namespace qmm

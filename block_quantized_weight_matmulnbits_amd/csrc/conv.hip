@@ -44,11 +44,14 @@ __device__ __forceinline__ void divmod_small(int n, int d, float inv_d, int& q, 
 // any of them, from addresses that are always valid (out-of-image taps and
 // the tail past K read element 0 and are replaced afterwards), so the loads
 // stay free of branches and their latency is paid once per batch.
-// V16: C % 16 == 0 and 16-byte aligned tensors, so a lane's 16 reduction
-// indices of a step lie in one tap and are 16 contiguous bytes of both the
-// input pixel and the weight row: one 16-byte load each instead of four
-// 4-byte loads.
-template <bool V16>
+// VEC = 16: C % 16 == 0 and 16-byte aligned tensors, so a lane's 16
+// reduction indices of a step lie in one tap and are 16 contiguous bytes of
+// both the input pixel and the weight row: one 16-byte load each.
+// VEC = 4: C % 4 == 0 and 4-byte aligned tensors: four 4-byte loads, each
+// group of 4 channels inside one tap.
+// VEC = 1: any C: every byte is gathered on its own (its own tap), and the
+// zero-point / zero replacement is applied per byte as it is loaded.
+template <int VEC>
 __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wt, const int32_t* __restrict__ bias,
     const float* __restrict__ w_scale, float in_scale, float out_scale, int in_zp, int out_zp,
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
     uint32_t ain = 0, kin = 0;       // bit 4 s + j: inside the image / k < K
 #pragma unroll
     for (int s = 0; s < CONV_BATCH; ++s) {
-      if constexpr (V16) {
+      if constexpr (VEC == 16) {
         // The lane's 16 indices: one tap, channels c .. c + 15 (K % 16 == 0,
         // so the group is all in or all out).
         const int k = (ks0 + s) * 64 + g * 16;
@@ -121,6 +124,41 @@ __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
           const bool w_ok = oc < Co && k_ok;
           const u32x4 wb = *reinterpret_cast<const u32x4*>(Wt + (w_ok ? (int64_t)oc * K + k : 0));
           bv[s][t][0] = wb.x; bv[s][t][1] = wb.y; bv[s][t][2] = wb.z; bv[s][t][3] = wb.w;
+        }
+        continue;
+      }
+      if constexpr (VEC == 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t xw = 0, ww[CONV_NT];
+#pragma unroll
+          for (int t = 0; t < CONV_NT; ++t) ww[t] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k = (ks0 + s) * 64 + g * 16 + j * 4 + e;
+            const bool k_ok = k < K;
+            int tap, c, kh, kw;
+            divmod_small(k_ok ? k : 0, C, inv_c, tap, c);
+            divmod_small(tap, KW, inv_kw, kh, kw);
+            const int ih = oh * sh - ph + kh, iw = ow * sw - pw + kw;
+            const bool inside = p_ok && k_ok && ih >= 0 && ih < H && iw >= 0 && iw < W;
+            const int64_t xoff = inside ? (((int64_t)nb * H + ih) * W + iw) * C + c : 0;
+            const uint32_t xb = (uint8_t)X[xoff];
+            xw |= (inside ? xb : (zp4 & 0xFFu)) << (8 * e);
+#pragma unroll
+            for (int t = 0; t < CONV_NT; ++t) {
+              const int oc = oc0 + t * 16 + li;
+              const bool w_ok = oc < Co && k_ok;
+              const uint32_t wb = (uint8_t)Wt[w_ok ? (int64_t)oc * K + k : 0];
+              ww[t] |= (w_ok ? wb : 0u) << (8 * e);
+            }
+          }
+          // Already replaced byte by byte: mark the group as taken as is.
+          av[s][j] = xw;
+          ain |= 1u << (4 * s + j);
+          kin |= 1u << (4 * s + j);
+#pragma unroll
+          for (int t = 0; t < CONV_NT; ++t) bv[s][t][j] = ww[t];
         }
         continue;
       }
@@ -199,7 +237,9 @@ __global__ __launch_bounds__(64 * CONV_WAVES) void conv_int8_kernel(
     for (int e = 0; e < 4; ++e) {
       const int pe = p0 + g * 4 + e;
       if (pe >= P) continue;
-      const int a = b0 + acc[t][e] - in_zp * wsum[t][e];
+      // The true accumulator in 64 bits (the bias is any int32); the int32
+      // partial sums are exact under the host's bound on the reduction.
+      const int64_t a = (int64_t)b0 + acc[t][e] - (int64_t)in_zp * wsum[t][e];
       const float r = rintf((float)a * mult);
       float v = r + (float)out_zp;
       v = fminf(fmaxf(v, (float)clamp_min), (float)clamp_max);
@@ -213,8 +253,10 @@ hipError_t launch_conv_int8(const ConvArgs& c) {
   const int OW = (c.W + 2 * c.pad_w - c.KW) / c.stride_w + 1;
   const int P = c.Nb * OH * OW;
   dim3 grid((P + 15) / 16, (c.Co + 16 * CONV_NT - 1) / (16 * CONV_NT));
-  const bool v16 = (c.C % 16) == 0 && (((uintptr_t)c.X | (uintptr_t)c.Wt) & 15) == 0;
-  auto kern = v16 ? conv_int8_kernel<true> : conv_int8_kernel<false>;
+  const uintptr_t align = (uintptr_t)c.X | (uintptr_t)c.Wt;
+  auto kern = ((c.C % 16) == 0 && (align & 15) == 0) ? conv_int8_kernel<16>
+              : ((c.C % 4) == 0 && (align & 3) == 0) ? conv_int8_kernel<4>
+                                                      : conv_int8_kernel<1>;
   hipLaunchKernelGGL(kern, grid, dim3(64 * CONV_WAVES), 0, c.stream, c.X, c.Wt,
                      c.bias, c.w_scale, c.in_scale, c.out_scale, c.in_zp, c.out_zp, c.clamp_min,
                      c.clamp_max, c.H, c.W, c.C, c.Co, c.KH, c.KW, c.stride_h, c.stride_w,

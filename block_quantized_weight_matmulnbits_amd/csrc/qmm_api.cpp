@@ -258,12 +258,6 @@ int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const flo
   if (H + 2 * pad_h < KH || W + 2 * pad_w < KW)
     return fail(QMM_ERR_INVALID_ARG, "%s: the padded input (%dx%d) is smaller than the kernel "
                 "(%dx%d), so there is no output pixel.", fn, H + 2 * pad_h, W + 2 * pad_w, KH, KW);
-  if (C % 4 != 0)
-    return fail(QMM_ERR_UNSUPPORTED, "%s: C=%d must be a multiple of 4. Why: the kernel reads "
-                "input channels and weight rows as 4-byte words. How to fix: pad the channels "
-                "with zero weights.", fn, C);
-  if (((uintptr_t)X & 3) || ((uintptr_t)Wt & 3))
-    return fail(QMM_ERR_INVALID_ARG, "%s: X and Wt must be 4-byte aligned.", fn);
   if (in_zp < -128 || in_zp > 127 || clamp_min < -128 || clamp_max > 127 || clamp_min > clamp_max)
     return fail(QMM_ERR_INVALID_ARG, "%s: in_zp must be an int8 value and -128 <= clamp_min <= "
                 "clamp_max <= 127 (got in_zp=%d clamp=[%d,%d]). Why: the output is int8; a ReLU "
@@ -380,9 +374,12 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
                            b_layout, tiled ? nullptr : B, tiled ? s_dtype : QMM_F32, zero_points,
                            nullptr, (void*)dots, M, K, N, block_size, bits, 4, &a);
   if (st != QMM_OK) return st;
-  if (a.tiled && !qmm::compint8_tiled_supported(a))
+  // The route qmm_gemm_compint8 takes for the same arguments.
+  const bool small = M > 0 && qmm::compint8_small_supported(a);
+  if (a.tiled && !small && !qmm::compint8_tiled_supported(a))
     return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_compint8_block_dots: on the tiled layout "
-                "CompInt8 needs block_size >= 64. How to fix: pass the operator's layout.");
+                "CompInt8 needs block_size >= 64, or M = 1 with a block of at least one 16-byte "
+                "unit of codes. How to fix: pass the operator's layout.");
   if (M == 0) return QMM_OK;
   st = check_workspace("qmm_debug_compint8_block_dots", a, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
@@ -391,9 +388,14 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
   a.stream = (hipStream_t)stream;
   int8_t* qa = (int8_t*)workspace;
   float* sa = (float*)((char*)workspace + qmm::ws_qa_bytes(a.M, a.kb, a.block_size));
-  hipError_t e = qmm::launch_quantize_a(a, qa, sa);
-  if (e == hipSuccess)
-    e = hipMemsetAsync(dots, 0, (size_t)(a.M * a.N * a.kb) * sizeof(int32_t), a.stream);
+  hipError_t e = hipMemsetAsync(dots, 0, (size_t)(a.M * a.N * a.kb) * sizeof(int32_t), a.stream);
+  if (small) {
+    // One launch: the kernel quantizes in LDS and writes its qa / sa to the
+    // workspace beside the dots.
+    if (e == hipSuccess) e = qmm::launch_compint8_small_dots(a, qa, sa, dots);
+    return hip_status(e, "qmm_debug_compint8_block_dots");
+  }
+  if (e == hipSuccess) e = qmm::launch_quantize_a(a, qa, sa);
   if (e == hipSuccess)
     e = a.tiled ? qmm::launch_compint8_tiled_dots(a, qa, sa, dots)
                 : qmm::launch_compint8_dots(a, qa, sa, dots);

@@ -49,6 +49,9 @@ hipError_t launch_compint8_dots(const MatArgs& a, const int8_t* qa, const float*
 // (compint8_small.hip); it needs no workspace.
 bool compint8_small_supported(const MatArgs& a);
 hipError_t launch_compint8_small(const MatArgs& a);
+// The same kernel, writing its exact int32 block dots [M, N, kb] and the
+// activations it quantized in LDS (qa [M, kb*bs], sa [M, kb]) instead of Y.
+hipError_t launch_compint8_small_dots(const MatArgs& a, int8_t* qa, float* sa, int32_t* dots);
 // CompInt8 on the tiled layout with int8 MFMA (compint8_tiled.hip).
 bool compint8_tiled_supported(const MatArgs& a);
 hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa);

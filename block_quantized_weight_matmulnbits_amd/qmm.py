@@ -86,33 +86,54 @@ def qmm_last_error() -> str:
 
 class Repacked:
     """A device buffer written by :func:`qmm_repack`: pass it as ``B`` (with
-    ``scales=None`` and ``zero_points=None``) to qmm_gemv / qmm_gemm."""
+    ``scales=None`` and ``zero_points=None``) to qmm_gemv / qmm_gemm /
+    qmm_gemm_compint8.  The tiled buffer itself carries no geometry (the
+    kernels derive its regions from K, N, block_size, bits and the scale
+    dtype), so the geometry it was repacked with is kept here and every call
+    that takes it must pass the same K, N, block_size and bits."""
 
-    def __init__(self, buf, s_dtype, has_zero_points):
+    def __init__(self, buf, s_dtype, has_zero_points, K, N, block_size, bits):
         self.buf = buf
         self.s_dtype = s_dtype
+        self.has_zero_points = bool(has_zero_points)
         self.layout = QMM_LAYOUT_TILED_ZP if has_zero_points else QMM_LAYOUT_TILED
+        self.K, self.N, self.block_size, self.bits = int(K), int(N), int(block_size), int(bits)
+        self.nbytes = buf.numel() * buf.element_size()
+
+    def check(self, K, N, block_size, bits):
+        """Raise ValueError unless (K, N, block_size, bits) are the repack's."""
+        got = (int(K), int(N), int(block_size), int(bits))
+        want = (self.K, self.N, self.block_size, self.bits)
+        if got != want:
+            raise ValueError(f"repacked buffer geometry mismatch: it was repacked for (K, N, "
+                             f"block_size, bits) = {want}, the call passes {got}. The tiled "
+                             "regions are located from these values: pass the repack's.")
+        need = qmm_repacked_bytes(K, N, block_size, bits, self.s_dtype, self.has_zero_points)
+        if self.nbytes < need:
+            raise ValueError(f"repacked buffer holds {self.nbytes} bytes, the geometry needs "
+                             f"{need}")
 
 
-def _weights(B, scales):
+def _weights(B, scales, K, N, block_size, bits):
     """(B pointer, layout, scales pointer, scales dtype) for either layout."""
     if isinstance(B, Repacked):
         if scales is not None:
             raise ValueError("a repacked buffer carries its scales: pass scales=None")
+        B.check(K, N, block_size, bits)
         return B.buf.data_ptr(), B.layout, None, B.s_dtype
     return B.data_ptr(), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales)
 
 
 def qmm_gemv(A, B, scales, zero_points, bias, Y, K, N, block_size, bits, accuracy_level=0,
              stream=None):
-    b, layout, s, sdt = _weights(B, scales)
+    b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
     _check(lib.qmm_gemv(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
                         _ptr(Y), K, N, block_size, bits, accuracy_level, _stream(stream)))
 
 
 def qmm_gemm(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level=0,
              stream=None):
-    b, layout, s, sdt = _weights(B, scales)
+    b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
     _check(lib.qmm_gemm(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
                         _ptr(Y), M, K, N, block_size, bits, accuracy_level, _stream(stream)))
 
@@ -130,10 +151,12 @@ def qmm_repack(B, scales, zero_points, K, N, block_size, bits, out=None, stream=
         out = torch.empty(nbytes, dtype=torch.uint8, device=B.device)
     _check(lib.qmm_repack(_ptr(B), _ptr(scales), _dt(scales), _ptr(zero_points), K, N, block_size,
                           bits, _ptr(out), out.numel() * out.element_size(), _stream(stream)))
-    return Repacked(out, _dt(scales), zero_points is not None)
+    return Repacked(out, _dt(scales), zero_points is not None, K, N, block_size, bits)
 
 
 def qmm_unrepack(tiled, K, N, block_size, bits, B, scales, zero_points, stream=None):
+    if isinstance(tiled, Repacked):
+        tiled.check(K, N, block_size, bits)
     buf = tiled.buf if isinstance(tiled, Repacked) else tiled
     _check(lib.qmm_unrepack(_ptr(buf), int(zero_points is not None), K, N, block_size, bits,
                             _dt(scales), _ptr(B), _ptr(scales), _ptr(zero_points),
@@ -146,7 +169,7 @@ def qmm_compint8_workspace_size(M, K, block_size) -> int:
 
 def qmm_gemm_compint8(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, workspace,
                       accuracy_level=4, stream=None):
-    b, layout, s, sdt = _weights(B, scales)
+    b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
     _check(lib.qmm_gemm_compint8(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
                                  _ptr(Y), M, K, N, block_size, bits, accuracy_level,
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -177,6 +200,7 @@ def qmm_debug_quantize_a(A, M, K, block_size, qa, sa, stream=None):
 def qmm_debug_compint8_block_dots(A, B, zero_points, M, K, N, block_size, bits, dots, workspace,
                                   stream=None):
     if isinstance(B, Repacked):
+        B.check(K, N, block_size, bits)
         b, layout, sdt = B.buf.data_ptr(), B.layout, B.s_dtype
     else:
         b, layout, sdt = _ptr(B), QMM_LAYOUT_ORT, QMM_F32

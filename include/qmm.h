@@ -139,8 +139,11 @@ int qmm_gemm_compint8(const void *A, int a_dtype, const uint8_t *B,
  * mult = (in_scale * w_scale[oc]) / out_scale in binary32;
  * y = clamp(round_half_even(float(acc) * mult) + out_zp, clamp_min, clamp_max).
  * A ReLU is expressed as clamp_min = out_zp.  Groups and dilation are 1.
- * Requires C % 4 == 0 (rows of 4-byte words) and KH*KW*C*2^14 < 2^31 (an
- * exact int32 accumulator); float(acc) is the round-to-nearest conversion.
+ * Any C (C % 16 == 0 with 16-byte aligned X and Wt takes 16-byte loads,
+ * C % 4 == 0 with 4-byte alignment 4-byte loads, the rest byte gathers).
+ * Requires KH*KW*C*2^14 < 2^31 (exact int32 partial sums); the accumulator
+ * with the bias is formed in 64 bits and float(acc) is the round-to-nearest
+ * conversion.
  */
 int qconv_int8(const int8_t *X, const int8_t *Wt, const int32_t *bias,
                const float *w_scale, float in_scale, float out_scale,
@@ -165,6 +168,12 @@ int qconv_int8(const int8_t *X, const int8_t *Wt, const int32_t *bias,
  * unused bits of each zero-point row's last byte are written as zero).
  * Arguments as for qmm_gemv; out / tiled are device buffers of at least
  * qmm_repacked_bytes bytes, 256-byte aligned.
+ * The tiled buffer holds no header: every call that takes it locates its
+ * regions from K, N, block_size, bits, s_dtype and the layout (with or
+ * without zero points).  The caller must pass exactly the values it was
+ * repacked with; other values read the wrong bytes (within the buffer's
+ * extent only if it is at least qmm_repacked_bytes of those values).  The
+ * Python binding records the geometry and rejects a mismatch.
  */
 size_t qmm_repacked_bytes(int64_t K, int64_t N, int block_size, int bits, int s_dtype,
                           int has_zero_points);
@@ -182,10 +191,15 @@ int qmm_unrepack(const void *tiled, int has_zero_points, int64_t K, int64_t N, i
  *  qmm_debug_unpack: codes [N, K] uint8, zps [N, kb] uint8 (defaults filled
  *    in), w [N, K] float32 = (code - zp) * scale; any output may be NULL.
  *  qmm_debug_quantize_a: qa [M, kb*block_size] int8 (zero past K), sa [M, kb]
- *    float32, exactly as the first step of qmm_gemm_compint8.
- *  qmm_debug_compint8_block_dots: dots [M, N, kb] int32 as computed inside
- *    qmm_gemm_compint8 (same workspace contract).  s_dtype matters only for
- *    a tiled B (it locates the zero-point region); scales are not read.
+ *    float32, exactly as the quantization launch of qmm_gemm_compint8's
+ *    two-launch route.
+ *  qmm_debug_compint8_block_dots: dots [M, N, kb] int32 computed by the
+ *    kernels of the route qmm_gemm_compint8 takes for the same arguments
+ *    (same workspace contract).  On return the workspace holds that route's
+ *    quantized activations: qa [M, kb*block_size] int8 at offset 0 and sa
+ *    [M, kb] float32 at the next 256-byte boundary -- for M = 1 on the tiled
+ *    layout, the ones the one-launch kernel computed in LDS.  s_dtype
+ *    matters only for a tiled B (it locates the zero-point region).
  */
 int qmm_debug_unpack(const uint8_t *B, int b_layout, const void *scales,
                      int s_dtype, const uint8_t *zero_points, int64_t K,

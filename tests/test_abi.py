@@ -106,14 +106,12 @@ def conv(qmm, **kw):
 
 
 @pytest.mark.parametrize("kw,code,needle", [
-    (dict(C=6), -2, "multiple of 4"),
     (dict(X=None), -1, "non-null"),
     (dict(sh=0), -1, "strides must be >= 1"),
     (dict(KH=9, ph=0, H=4), -1, "smaller than the kernel"),
     (dict(lo=10, hi=5), -1, "clamp_min"),
     (dict(in_zp=300), -1, "in_zp"),
     (dict(out_scale=0.0), -1, "out_scale"),
-    (dict(X=FAKE + 2), -1, "4-byte aligned"),
     (dict(C=1 << 20), -2, "too large"),
 ])
 def test_conv_rejects_bad_arguments(qmm, kw, code, needle):
@@ -161,17 +159,26 @@ def test_compint8_tiled_layout_needs_whole_chunks_per_block(qmm):
 
 
 def test_benchmark_probe_library_exports_its_read_kernel():
-    """bench.py's reference read (libqmm_probe.so, not part of libqmm.so)
-    loads and rejects bad arguments on the host."""
-    path = os.path.join(ROOT, "block_quantized_weight_matmulnbits_amd", "probe", "libqmm_probe.so")
+    """bench.py's reference read (bench_probe/libqmm_probe.so, not part of
+    libqmm.so and not built by the library's build) loads and rejects bad
+    arguments on the host."""
+    path = os.path.join(ROOT, "bench_probe", "libqmm_probe.so")
     lib = ctypes.CDLL(path)
     fn = lib.qmm_probe_stream_read
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    assert fn(None, 16, None, 1, None) != 0        # null pointers
-    assert fn(1 << 20, 15, 1 << 20, 1, None) != 0  # not a multiple of 16 bytes
-    assert fn(1 << 20, 16, 1 << 20, 0, None) != 0  # empty grid
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    big = 1 << 20
+    assert fn(None, 16, None, 256, 1, 256, 4, 1, 0, None) != 0        # null pointers
+    assert fn(big, 15, big, 256, 1, 256, 4, 1, 0, None) != 0          # not whole 16-byte words
+    assert fn(big, 16, big, 256, 0, 256, 4, 1, 0, None) != 0          # empty grid
+    assert fn(big, 16, big, 256, 2, 256, 4, 1, 0, None) != 0          # out too small for the grid
+    assert fn(big, 16, big, 4096, 1, 96, 4, 1, 0, None) != 0          # block not whole waves
+    assert fn(big, 16, big, 4096, 1, 256, 3, 1, 0, None) != 0         # unroll not offered
     assert "qmm_probe_stream_read" not in open(
         os.path.join(ROOT, "include", "qmm.h")).read()   # not part of the matmul ABI
+    import block_quantized_weight_matmulnbits_amd.build as libbuild
+    assert "stream_read" not in open(libbuild.__file__).read()
 
 
 def test_bench_refuses_more_than_one_gpu():
@@ -183,3 +190,23 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_repacked_geometry_is_checked_by_the_binding(qmm):
+    """A Repacked buffer remembers the (K, N, block_size, bits) it was
+    repacked with; the binding rejects a call that passes other values
+    before anything reaches the library."""
+    import torch
+    nbytes = qmm.qmm_repacked_bytes(4096, 1024, 32, 4, torch.bfloat16, True)
+    r = qmm.Repacked(torch.empty(nbytes, dtype=torch.uint8), qmm.QMM_BF16, True, 4096, 1024, 32, 4)
+    r.check(4096, 1024, 32, 4)
+    for bad in [(4096, 2048, 32, 4), (4097, 1024, 32, 4), (4096, 1024, 64, 4),
+                (4096, 1024, 32, 8)]:
+        with pytest.raises(ValueError, match="geometry mismatch"):
+            r.check(*bad)
+    short = qmm.Repacked(torch.empty(nbytes - 256, dtype=torch.uint8), qmm.QMM_BF16, True, 4096,
+                         1024, 32, 4)
+    with pytest.raises(ValueError, match="holds"):
+        short.check(4096, 1024, 32, 4)
+    with pytest.raises(ValueError, match="geometry mismatch"):
+        qmm.qmm_gemv(None, r, None, None, None, None, 4096, 2048, 32, 4)

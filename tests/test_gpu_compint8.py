@@ -1,9 +1,13 @@
 """GPU parity of CompInt8 (qmm_gemm_compint8 and its debug exports).
 
-Bit-exact: the quantized activations and their scales (qmm_debug_quantize_a)
-and the int32 block dots computed by the production kernel
-(qmm_debug_compint8_block_dots).  Within tol * S: the scaled float output,
-against the oracle's CompInt8 value.  Shapes: small ragged ones for every
+Bit-exact: the quantized activations and their scales of the quantization
+launch (qmm_debug_quantize_a); and the int32 block dots together with the
+quantized activations and scales left in the workspace by the kernels of the
+route qmm_gemm_compint8 takes (qmm_debug_compint8_block_dots) -- for M = 1
+on the tiled layout, the one-launch kernel's in-LDS quantization and its
+per-block int32 sums.  Within tol * S: the scaled float output, against the
+oracle's CompInt8 value (strictly, with no output-rounding allowance, on the
+seeded full-size workload).  Shapes: small ragged ones for every
 (bits, block size, dtype, zero point) and the full batched-decode workload
 (M in {1, 4, 16}, K = 4096, N = 14336; bits 4 / bs 128 symmetric, bits 8 /
 bs 64 and bits 2 / bs 64 asymmetric).  Every test runs on the operator's
@@ -65,14 +69,21 @@ def gpu_quant(case):
 
 
 def gpu_dots(case):
+    """int32 block dots [M, N, kb] and the workspace's qa [M, kb*bs] / sa
+    [M, kb] as the route's kernels left them."""
     c = case.to(DEV)
-    dots = torch.empty(case.M, case.N, case.k_blocks, dtype=torch.int32, device=DEV)
+    kb, bs, M = case.k_blocks, case.block_size, case.M
+    dots = torch.empty(M, case.N, kb, dtype=torch.int32, device=DEV)
     B, _, Z = weights(case, c)
-    qmm().qmm_debug_compint8_block_dots(c.A, B, Z, case.M, case.K, case.N,
-                                        case.block_size, case.bits, dots,
-                                        workspace(case.M, case.K, case.block_size))
+    ws = workspace(M, case.K, bs)
+    ws.fill_(0x5A)                     # stale bytes: every exported byte must be written
+    qmm().qmm_debug_compint8_block_dots(c.A, B, Z, M, case.K, case.N, bs, case.bits, dots, ws)
     torch.cuda.synchronize()
-    return dots.cpu().numpy()
+    qa_bytes = -(-(M * kb * bs) // 256) * 256
+    w = ws.cpu()
+    qa = w[:M * kb * bs].view(torch.int8).reshape(M, kb * bs).numpy()
+    sa = w[qa_bytes:qa_bytes + 4 * M * kb].view(torch.float32).reshape(M, kb).numpy()
+    return dots.cpu().numpy(), qa, sa
 
 
 def gpu_matmul(case):
@@ -85,7 +96,22 @@ def gpu_matmul(case):
     return Y
 
 
-def check_all(case, what):
+def small_route(case):
+    """Whether qmm_gemm_compint8 takes the one-launch M = 1 kernel: tiled
+    layout, a block of at least one 16-byte unit of codes and at most 1024,
+    and the quantized row within its LDS budget."""
+    if LAYOUT["v"] != "tiled" or case.M != 1:
+        return False
+    if not 128 // case.bits <= case.block_size <= 1024:
+        return False
+    # LDS bytes: the permuted row + unit sums + block scales + share sums.
+    chunks = -(-(case.k_blocks * case.block_size) // 64)
+    rs = 64 * chunks + 64 * {2: 8, 4: 4, 8: 2}[case.bits]
+    lds = -(-rs // 16) * 16 + rs // (128 // case.bits) * 4 + case.k_blocks * 4 + 16 * 8 * 4
+    return lds <= 64 * 1024
+
+
+def check_all(case, what, strict=False):
     print(f"[compint8 {LAYOUT['v']}] {what} M={case.M} K={case.K} N={case.N} bs={case.block_size} "
           f"bits={case.bits} a={case.a_dtype} zp={case.zero_points is not None}", flush=True)
     qa, sa = oracle_quant(case)
@@ -94,23 +120,26 @@ def check_all(case, what):
     assert np.array_equal(gqa, qa), f"{what}: int8 activations differ"
     tiled = LAYOUT["v"] == "tiled"
     mfma_ok = not tiled or case.block_size >= 64
-    small_ok = tiled and case.M == 1 and 128 // case.bits <= case.block_size <= 1024
-    if mfma_ok:
+    small_ok = small_route(case)
+    if mfma_ok or small_ok:
         dots = oracle.compint8_block_dots(qa, u8(case.B), u8(case.zero_points), case.N, case.K,
                                           case.block_size, case.bits)
-        assert np.array_equal(gpu_dots(case), dots), f"{what}: int32 block dots differ"
+        gdots, wqa, wsa = gpu_dots(case)
+        route = "one-launch" if small_ok else "two-launch"
+        assert np.array_equal(wsa, sa), f"{what}: {route} activation scales differ"
+        assert np.array_equal(wqa, qa), f"{what}: {route} int8 activations differ"
+        assert np.array_equal(gdots, dots), f"{what}: {route} int32 block dots differ"
     else:
         with pytest.raises(qmm().QmmError) as err:
             gpu_dots(case)
         assert err.value.status == qmm().QMM_ERR_UNSUPPORTED
-    if not (mfma_ok or small_ok):
         with pytest.raises(qmm().QmmError) as err:
             gpu_matmul(case)
         assert err.value.status == qmm().QMM_ERR_UNSUPPORTED
         return 0.0
     Y, S = oracle.compint8_matmul(qa, sa, u8(case.B), f64(case.scales), u8(case.zero_points),
                                   f64(case.bias), case.N, case.K, case.block_size, case.bits)
-    return assert_within(gpu_matmul(case), Y, S, TOL[case.A.dtype], what)
+    return assert_within(gpu_matmul(case), Y, S, TOL[case.A.dtype], what, strict=strict)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
@@ -150,8 +179,24 @@ def test_batched_decode_workload_full_size(M, variant):
     from block_quantized_weight_matmulnbits_amd.workloads import compint8_case
     bits, bs, asym = variant
     case = compint8_case(M, bits, bs, asym)
-    r = check_all(case, case.meta["name"])
+    r = check_all(case, case.meta["name"], strict=True)
     print(f"  max |err|/S = {r:.3e}")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_one_row_every_block_size(bits):
+    """M = 1 (the one-launch kernel on the tiled layout) for every block size
+    it takes, from one 16-byte unit of codes to 1024: blocks within one wave
+    load (units combined across lanes) and blocks over several loads (int32
+    sums carried between loads), with ragged K so the last block is partial
+    and shares of K that must stay whole blocks."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    sizes = [bs for bs in (16, 32, 64, 128, 256, 512, 1024) if bs >= 128 // bits]
+    for i, bs in enumerate(sizes):
+        for j, (K, N) in enumerate([(4096, 300), (4096 + 64 * 3 + 5, 96), (bs * 9 - 17, 40)]):
+            case = make_matmul_case(1, K, N, bs, bits, a_dtype="bf16", has_zp=(j != 1),
+                                    has_bias=(j == 0), seed=7000 + 100 * bits + 10 * i + j)
+            check_all(case, f"one row b{bits} bs{bs}")
 
 
 def test_quantize_a_ties_and_zero_blocks():

@@ -120,7 +120,7 @@ def test_prefill_workload_sampled_rows():
     A = f64(case.A)[rows]
     Y, S = oracle.matmul_nbits(A, u8(case.B), f64(case.scales), u8(case.zero_points), None,
                                case.N, case.K, case.block_size, case.bits)
-    r = assert_within(y[rows], Y, S, TOL[torch.bfloat16], "prefill")
+    r = assert_within(y[rows], Y, S, TOL[torch.bfloat16], "prefill", strict=True)
     print(f"  max |err|/S = {r:.3e}")
 
 

@@ -1,6 +1,8 @@
 """GPU parity of the M = 1 GEMV (qmm_gemv) against the oracle.
 
-Element-wise within tol * S at small ragged shapes for every (bits, block
+Element-wise within tol * S (strictly, with no output-rounding allowance,
+on the seeded workloads: the tiny configuration and the full layer) at small
+ragged shapes for every (bits, block
 size, dtype, zero point, bias) combination, at the full Llama-3-8B layer
 shapes of the decode workload, and on the degenerate cases.  Every test runs
 on the operator's layout and on the tiled layout written by qmm_repack (the
@@ -39,13 +41,13 @@ def run_gemv(case):
     return Y
 
 
-def check(case, what=""):
+def check(case, what="", strict=False):
     print(f"[gemv {LAYOUT['v']}] {what} M=1 K={case.K} N={case.N} bs={case.block_size} bits={case.bits} "
           f"a={case.a_dtype} s={case.s_dtype} zp={case.zero_points is not None} "
           f"bias={case.bias is not None}", flush=True)
     Y, S = oracle_matmul(case)
     y = run_gemv(case)
-    return assert_within(y, Y[0], S[0], TOL[case.A.dtype], what)
+    return assert_within(y, Y[0], S[0], TOL[case.A.dtype], what, strict=strict)
 
 
 @pytest.mark.parametrize("a_dtype", ["f32", "f16", "bf16"])
@@ -69,14 +71,14 @@ def test_scale_dtypes(s_dtype):
 
 def test_tiny_matmulnbits_config():
     from block_quantized_weight_matmulnbits_amd.workloads import tiny_matmulnbits
-    check(tiny_matmulnbits(), "tiny f32")
+    check(tiny_matmulnbits(), "tiny f32", strict=True)
 
 
 def test_decode_layer_full_shapes():
     """Every projection of the Llama-3-8B layer at full size, all outputs."""
     from block_quantized_weight_matmulnbits_amd.workloads import decode_layer
     for case in decode_layer():
-        r = check(case, f"decode {case.meta['name']}")
+        r = check(case, f"decode {case.meta['name']}", strict=True)
         print(f"  max |err|/S = {r:.3e}")
 
 
@@ -85,7 +87,7 @@ def test_decode_layer_fused_shapes():
     as the benchmark runs it: all outputs."""
     from block_quantized_weight_matmulnbits_amd.workloads import decode_layer_fused
     for case in decode_layer_fused():
-        r = check(case, f"decode fused {case.meta['name']}")
+        r = check(case, f"decode fused {case.meta['name']}", strict=True)
         print(f"  max |err|/S = {r:.3e}")
 
 

@@ -34,21 +34,31 @@ def oracle_matmul(case):
                                case.block_size, case.bits)
 
 
-def assert_within(y_dev, Y, S, tol, what=""):
+def assert_within(y_dev, Y, S, tol, what="", strict=False):
     """Element-wise |y - Y| <= tol * S + u_out * (|Y| + tol * S) + h_out, u_out
     the unit roundoff and h_out half the smallest subnormal of y's dtype;
-    reports the worst |y - Y| / S."""
+    reports the worst |y - Y| / S.
+
+    strict=True asserts the plain bound |y - Y| <= tol * S with no allowance
+    for rounding the result to the output dtype.  That is attainable when
+    |Y| is small next to S, as on the seeded workloads (random signs keep
+    |Y| / S near 1 / sqrt(K)); exact-data and edge cases, where |Y| can
+    approach S, need the output-rounding term."""
     u = OUT_ROUNDOFF[y_dev.dtype]
     y = f64(y_dev).reshape(Y.shape)
     err = np.abs(y - Y)
-    bound = tol * S + u * (np.abs(Y) + tol * S) + OUT_HALF_SUBNORMAL[y_dev.dtype]
+    if strict:
+        bound = tol * S
+    else:
+        bound = tol * S + u * (np.abs(Y) + tol * S) + OUT_HALF_SUBNORMAL[y_dev.dtype]
     bad = err > bound
     if bad.any():
         idx = np.argwhere(bad)[:5]
         with np.errstate(divide="ignore", invalid="ignore"):
             ratio = np.max(np.where(S > 0, err / S, np.inf))
         raise AssertionError(
-            f"{what}: {int(bad.sum())}/{bad.size} elements outside tol={tol}*S; "
+            f"{what}: {int(bad.sum())}/{bad.size} elements outside tol={tol}*S"
+            f"{' (strict)' if strict else ''}; "
             f"max |err|/S = {ratio:.3e}; first at {idx.tolist()}: "
             f"gpu={[y[tuple(i)] for i in idx]} oracle={[Y[tuple(i)] for i in idx]} "
             f"S={[S[tuple(i)] for i in idx]}")
