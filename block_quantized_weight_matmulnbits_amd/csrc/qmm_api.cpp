@@ -159,7 +159,63 @@ int validate_matmul(const char* fn, Route route, const void* A, int a_dtype, con
   return QMM_OK;
 }
 
+int check_workspace(const char* fn, const MatArgs& a, void* workspace, size_t bytes) {
+  const size_t need = qmm::ws_total_bytes(a.M, a.kb, a.block_size);
+  if (workspace == nullptr || bytes < need)
+    return fail(QMM_ERR_WORKSPACE,
+                "%s: the workspace holds %zu bytes at %p, %zu are needed. Why: CompInt8 stores the "
+                "int8 activations and their per-block scales there (the library never allocates). "
+                "How to fix: pass qmm_compint8_workspace_size(M, K, block_size) bytes of device "
+                "memory.", fn, bytes, workspace, need);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(QMM_ERR_WORKSPACE, "%s: the workspace must be 256-byte aligned. How to fix: "
+                "pass the start of a fresh allocation.", fn);
+  return QMM_OK;
+}
+
 }  // namespace
+
+namespace qmm {
+
+int set_error(int code, const char* message) { return fail(code, "%s", message); }
+
+int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t* B,
+                       int b_layout, const void* scales, int s_dtype, const uint8_t* zero_points,
+                       const void* bias, void* Y, int64_t M, int64_t K, int64_t N,
+                       int block_size, int bits, int accuracy_level, void* workspace,
+                       size_t workspace_bytes, hipError_t (*resolve_workspace)(void**),
+                       void* stream) {
+  MatArgs a;
+  int st = validate_matmul(fn, Route::CompInt8, A, a_dtype, B, b_layout, scales, s_dtype,
+                           zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level, &a);
+  if (st != QMM_OK) return st;
+  const bool small = M > 0 && compint8_small_supported(a);
+  if (a.tiled && !small && !compint8_tiled_supported(a))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: on the tiled layout CompInt8 needs "
+                "block_size >= 64 (whole 64-code chunks per block) and at most 896 blocks per "
+                "row, or M = 1 with a block of at least one 16-byte unit of codes and at most "
+                "1024 codes (got M=%lld, block_size=%d, %lld blocks). How to fix: pass the "
+                "operator's layout (QMM_LAYOUT_ORT) for this weight.", fn, (long long)M,
+                block_size, (long long)a.kb);
+  if (M == 0) return QMM_OK;
+  if (resolve_workspace != nullptr) {
+    const hipError_t e = resolve_workspace(&workspace);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  st = check_workspace(fn, a, workspace, workspace_bytes);
+  if (st != QMM_OK) return st;
+  a.stream = (hipStream_t)stream;
+  // M = 1 on the tiled layout: one launch that quantizes the activations in
+  // LDS (the workspace is not touched).
+  if (small) return hip_status(launch_compint8_small(a), fn);
+  int8_t* qa = (int8_t*)workspace;
+  float* sa = (float*)((char*)workspace + ws_qa_bytes(a.M, a.kb, a.block_size));
+  hipError_t e = launch_quantize_a(a, qa, sa);
+  if (e == hipSuccess) e = a.tiled ? launch_compint8_tiled(a, qa, sa) : launch_compint8(a, qa, sa);
+  return hip_status(e, fn);
+}
+
+}  // namespace qmm
 
 extern "C" {
 
@@ -195,51 +251,15 @@ size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size) {
   return qmm::ws_total_bytes(M, kb, block_size);
 }
 
-static int check_workspace(const char* fn, const MatArgs& a, void* workspace, size_t bytes) {
-  const size_t need = qmm::ws_total_bytes(a.M, a.kb, a.block_size);
-  if (workspace == nullptr || bytes < need)
-    return fail(QMM_ERR_WORKSPACE,
-                "%s: the workspace holds %zu bytes at %p, %zu are needed. Why: CompInt8 stores the "
-                "int8 activations and their per-block scales there (the library never allocates). "
-                "How to fix: pass qmm_compint8_workspace_size(M, K, block_size) bytes of device "
-                "memory.", fn, bytes, workspace, need);
-  if (((uintptr_t)workspace & 255) != 0)
-    return fail(QMM_ERR_WORKSPACE, "%s: the workspace must be 256-byte aligned. How to fix: "
-                "pass the start of a fresh allocation.", fn);
-  return QMM_OK;
-}
 
 int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout,
                       const void* scales, int s_dtype, const uint8_t* zero_points,
                       const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
                       int bits, int accuracy_level, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  MatArgs a;
-  int st = validate_matmul("qmm_gemm_compint8", Route::CompInt8, A, a_dtype, B, b_layout, scales,
-                           s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
-                           accuracy_level, &a);
-  if (st != QMM_OK) return st;
-  const bool small = M > 0 && qmm::compint8_small_supported(a);
-  if (a.tiled && !small && !qmm::compint8_tiled_supported(a))
-    return fail(QMM_ERR_UNSUPPORTED, "qmm_gemm_compint8: on the tiled layout CompInt8 needs "
-                "block_size >= 64 (whole 64-code chunks per block) and at most 896 blocks per "
-                "row, or M = 1 with a block of at least one 16-byte unit of codes and at most "
-                "1024 codes (got M=%lld, block_size=%d, %lld blocks). How to fix: pass the "
-                "operator's layout (QMM_LAYOUT_ORT) for this weight.", (long long)M, block_size,
-                (long long)a.kb);
-  if (M == 0) return QMM_OK;
-  st = check_workspace("qmm_gemm_compint8", a, workspace, workspace_bytes);
-  if (st != QMM_OK) return st;
-  a.stream = (hipStream_t)stream;
-  // M = 1 on the tiled layout: one launch that quantizes the activations in
-  // LDS (the workspace is not touched).
-  if (small) return hip_status(qmm::launch_compint8_small(a), "qmm_gemm_compint8");
-  int8_t* qa = (int8_t*)workspace;
-  float* sa = (float*)((char*)workspace + qmm::ws_qa_bytes(a.M, a.kb, a.block_size));
-  hipError_t e = qmm::launch_quantize_a(a, qa, sa);
-  if (e == hipSuccess)
-    e = a.tiled ? qmm::launch_compint8_tiled(a, qa, sa) : qmm::launch_compint8(a, qa, sa);
-  return hip_status(e, "qmm_gemm_compint8");
+  return qmm::gemm_compint8_impl("qmm_gemm_compint8", A, a_dtype, B, b_layout, scales, s_dtype,
+                                 zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level,
+                                 workspace, workspace_bytes, nullptr, stream);
 }
 
 int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,

@@ -80,6 +80,20 @@ hipError_t launch_repack(const MatArgs& a, uint8_t* tiled, bool inverse, uint8_t
 // Codec export: codes [N, K], zero points [N, kb], dequantized weight [N, K].
 hipError_t launch_unpack(const MatArgs& a, uint8_t* codes, uint8_t* zps, float* w);
 
+// The body of qmm_gemm_compint8 (validation, route choice, launches), shared
+// with the entry point that takes no workspace: fn names the entry point in
+// messages; when resolve_workspace is non-null it is called after the
+// arguments have been validated (and only if there is work) to obtain the
+// workspace, which then holds workspace_bytes.
+int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t* B,
+                       int b_layout, const void* scales, int s_dtype, const uint8_t* zero_points,
+                       const void* bias, void* Y, int64_t M, int64_t K, int64_t N,
+                       int block_size, int bits, int accuracy_level, void* workspace,
+                       size_t workspace_bytes, hipError_t (*resolve_workspace)(void**),
+                       void* stream);
+// Record a message for qmm_last_error and return code.
+int set_error(int code, const char* message);
+
 // Workspace layout of CompInt8: qa [M, kb*bs] int8, then sa [M, kb] float,
 // each region 256-byte aligned.
 inline size_t ws_align(size_t v) { return (v + 255) / 256 * 256; }

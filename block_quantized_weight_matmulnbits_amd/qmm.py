@@ -37,6 +37,8 @@ _SIGS = {
     "qmm_compint8_workspace_size": ([_i64, _i64, _i32], _sz),
     "qmm_gemm_compint8": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
                            _i32, _vp, _sz, _vp], _i32),
+    "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64,
+                                   _i32, _i32, _i32, _vp], _i32),
     "qconv_int8": ([_vp, _vp, _vp, _vp, _f32, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "qmm_repacked_bytes": ([_i64, _i64, _i32, _i32, _i32, _i32], _sz),
@@ -174,6 +176,17 @@ def qmm_gemm_compint8(A, B, scales, zero_points, bias, Y, M, K, N, block_size, b
                                  _ptr(Y), M, K, N, block_size, bits, accuracy_level,
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
+
+
+QMM_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024
+
+
+def qmm_gemm_compint8_noalloc(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits,
+                              accuracy_level=4, stream=None):
+    b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
+    _check(lib.qmm_gemm_compint8_noalloc(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points),
+                                         _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
+                                         accuracy_level, _stream(stream)))
 
 
 def qconv_int8(X, W, bias, w_scale, in_scale, out_scale, in_zp, out_zp, clamp_min, clamp_max,

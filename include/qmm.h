@@ -128,6 +128,30 @@ int qmm_gemm_compint8(const void *A, int a_dtype, const uint8_t *B,
                       size_t workspace_bytes, void *stream);
 
 /*
+ * qmm_gemm_compint8 for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid hipMalloc): the same
+ * computation, kernels and results, with the workspace taken from a device
+ * array the library holds (one per device, QMM_NOALLOC_SCRATCH_BYTES, kept
+ * from library load until the process ends) instead of caller memory.  No
+ * call allocates or frees anything.  Arguments as for qmm_gemm_compint8
+ * without the workspace.  Errors: QMM_ERR_WORKSPACE when
+ * qmm_compint8_workspace_size(M, K, block_size) exceeds
+ * QMM_NOALLOC_SCRATCH_BYTES (split A into row batches); QMM_ERR_HIP if the
+ * array's device address cannot be found.  The array is found on the device
+ * current at the call, which must be the stream's device.  All calls on one
+ * device share it: calls that overlap on one device (on different streams,
+ * or from threads without ordering) race and give wrong results.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+
+int qmm_gemm_compint8_noalloc(const void *A, int a_dtype, const uint8_t *B,
+                              int b_layout, const void *scales, int s_dtype,
+                              const uint8_t *zero_points, const void *bias,
+                              void *Y, int64_t M, int64_t K, int64_t N,
+                              int block_size, int bits, int accuracy_level,
+                              void *stream);
+
+/*
  * int8 convolution with requantization (MNN ConvInt8TiledExecutor.cpp:
  * initializeConvInt8QuantInfo, im2col padding with the input zero point,
  * QuanPostTreatParameters clamp; rlx-cpu quant.rs: exec_q_mat_mul).

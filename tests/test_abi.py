@@ -210,3 +210,20 @@ def test_repacked_geometry_is_checked_by_the_binding(qmm):
         short.check(4096, 1024, 32, 4)
     with pytest.raises(ValueError, match="geometry mismatch"):
         qmm.qmm_gemv(None, r, None, None, None, None, 4096, 2048, 32, 4)
+
+
+def test_noalloc_compint8_rejects_on_the_host(qmm):
+    """The CompInt8 entry point without a workspace refuses, before any
+    device work, a problem whose workspace exceeds its fixed device array,
+    and validates its other arguments like qmm_gemm_compint8."""
+    lim = qmm.QMM_NOALLOC_SCRATCH_BYTES
+    assert qmm.qmm_compint8_workspace_size(300, 16384, 128) > lim
+    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 300,
+                                           16384, 64, 128, 4, 4, None)
+    assert st == -3 and "row batches" in qmm.qmm_last_error()
+    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096,
+                                           64, 128, 3, 4, None)
+    assert st == -1 and "bits must be 2, 4 or 8" in qmm.qmm_last_error()
+    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096,
+                                           64, 128, 4, 0, None)
+    assert st == -1 and "accuracy_level must be 4" in qmm.qmm_last_error()
