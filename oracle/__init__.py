@@ -10,8 +10,10 @@ Every function cites the passage of the web pages it follows:
 
 * "onnx-runtime-ep-cpu matmul_nbits.rs" -- MatMulNBits: the module
   documentation (layout ``[N, ceil(K/bs), bs*bits/8]``, LSB first), the
-  ``dequantize_nbits_value`` formula, ``quantize_activation_signed`` and the
-  CompInt8 block dot of ``int4_dot_row_scalar`` / ``int8_row``.
+  ``dequantize_nbits_value`` formula, the group-index branch of
+  ``dequantize_weight`` and the ``g_idx`` checks of ``execute``,
+  ``quantize_activation_signed`` and the CompInt8 block dot of
+  ``int4_dot_row_scalar`` / ``int8_row``.
 * "rlx-cpu quant.rs" -- ``exec_q_mat_mul`` (int32 accumulate, requantize,
   clamp) and the ``QConv2d`` attribute set.
 * "MNN ConvInt8TiledExecutor.cpp" -- zero-point padding of the im2col and the
@@ -64,8 +66,9 @@ def _load():
             "oracle_unpack_zero_points": [vp, i64, i64, i32, vp],
             "oracle_pack_codes": [vp, i64, i64, i64, i32, vp],
             "oracle_pack_zero_points": [vp, i64, i64, i32, vp],
-            "oracle_dequantize": [vp, vp, vp, i64, i64, i64, i32, vp],
-            "oracle_matmul_nbits": [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
+            "oracle_dequantize": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
+            "oracle_matmul_nbits": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
+            "oracle_check_g_idx": [vp, i64, i64, i64],
             "oracle_quantize_a": [vp, i64, i64, i64, vp, vp],
             "oracle_compint8_block_dots": [vp, vp, vp, i64, i64, i64, i64, i32, vp],
             "oracle_compint8_matmul": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
@@ -76,6 +79,7 @@ def _load():
             fn = getattr(_lib, name)
             fn.argtypes = argtypes
             fn.restype = None
+        _lib.oracle_check_g_idx.restype = i64
     return _lib
 
 
@@ -137,22 +141,47 @@ def pack_zero_points(zps, bits):
     return out
 
 
-def dequantize(B, scales, zp, N, K, block_size, bits):
-    """Dense float64 ``[N, K]`` weight (code - zp) * scale."""
+class GroupIndexError(ValueError):
+    """g_idx has the wrong length or an entry outside 0..kb."""
+
+
+def check_g_idx(g_idx, K, block_size):
+    """Range and shape check of group indices (MatMulNBits ``execute``: shape
+    ``[K]`` or ``[kb * block_size]``; ``dequantize_weight``: every entry in
+    ``0..kb``).  Returns the int32 array or raises :class:`GroupIndexError`."""
+    g = _c(np.ravel(g_idx), np.int32)
+    r = _load().oracle_check_g_idx(_ptr(g), g.size, K, block_size)
+    kb = n_blocks(K, block_size)
+    if r == -1:
+        raise GroupIndexError(f"g_idx must have shape [{K}] or [{kb * block_size}], got "
+                              f"[{g.size}]")
+    if r < g.size:
+        raise GroupIndexError(f"g_idx[{r}]={int(g[r])} is outside 0..{kb}")
+    return g
+
+
+def dequantize(B, scales, zp, N, K, block_size, bits, g_idx=None):
+    """Dense float64 ``[N, K]`` weight (code - zp) * scale; with ``g_idx`` the
+    scale and zero point of element k are those of group ``g_idx[k]``."""
     B = _c(B, np.uint8)
     s = _c(scales, np.float64)
     zp = _c(zp, np.uint8)
+    g = None if g_idx is None else check_g_idx(g_idx, K, block_size)
     out = np.empty((N, K), np.float64)
-    _load().oracle_dequantize(_ptr(B), _ptr(s), _ptr(zp), N, K, block_size, bits, _ptr(out))
+    _load().oracle_dequantize(_ptr(B), _ptr(s), _ptr(zp), _ptr(g), N, K, block_size, bits,
+                              _ptr(out))
     return out
 
 
 # -- O2 float matmul ---------------------------------------------------------
 
-def matmul_nbits(A, B, scales, zp, bias, N, K, block_size, bits):
+def matmul_nbits(A, B, scales, zp, bias, N, K, block_size, bits, g_idx=None):
     """Y = A @ W_deq^T (+ bias) in float64, plus the tolerance base S.
 
     ``A`` is ``[M, K]`` (any float dtype, widened exactly to float64).
+    ``g_idx`` (optional, ``[K]`` or ``[kb * block_size]`` int32) selects the
+    scale and zero point of element k (group ``g_idx[k]`` instead of its
+    block); it is range-checked first.
     Returns ``(Y, S)`` with ``S[m, n] = sum_k |A[m,k] w(n,k)| + |bias[n]|``.
     """
     A = _c(np.atleast_2d(A), np.float64)
@@ -161,10 +190,11 @@ def matmul_nbits(A, B, scales, zp, bias, N, K, block_size, bits):
     s = _c(scales, np.float64)
     zp = _c(zp, np.uint8)
     bias = _c(bias, np.float64)
+    g = None if g_idx is None else check_g_idx(g_idx, K, block_size)
     Y = np.empty((M, N), np.float64)
     S = np.empty((M, N), np.float64)
-    _load().oracle_matmul_nbits(_ptr(A), _ptr(B), _ptr(s), _ptr(zp), _ptr(bias), M, N, K,
-                                block_size, bits, _ptr(Y), _ptr(S))
+    _load().oracle_matmul_nbits(_ptr(A), _ptr(B), _ptr(s), _ptr(zp), _ptr(g), _ptr(bias), M, N,
+                                K, block_size, bits, _ptr(Y), _ptr(S))
     return Y, S
 
 

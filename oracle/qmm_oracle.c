@@ -10,7 +10,8 @@
  * Sources (web pages, cited by title and section):
  *   [ORT]  onnx-runtime-ep-cpu 0.1.0-dev.5, src/kernels/matmul_nbits.rs
  *          (MatMulNBits: module documentation, dequantize_nbits_value,
- *           dequantize_weight, prepack_int8_weight, quantize_activation_signed,
+ *           dequantize_weight and its group-index branch, execute's g_idx
+ *           shape check, prepack_int8_weight, quantize_activation_signed,
  *           int4_dot_row_scalar, int8_row, execute's bias step)
  *   [RLX]  rlx-cpu 0.2.13, src/thunk/ops/quant.rs
  *          (exec_q_mat_mul requantize step, compile_q_conv2d attributes)
@@ -122,42 +123,68 @@ EXPORT void oracle_pack_zero_points(const uint8_t *zps, int64_t N, int64_t kb,
         }
 }
 
-/* Dequantized weight w[n*K + k] = (code - zp) * scale[n*kb + b], in double
- * ([ORT] dequantize_nbits_value; scales are given already widened). */
+/* Group whose scale and zero point apply to element k: its block k / bs,
+ * or g_idx[k] when group indices are given ([ORT] dequantize_weight: the
+ * code is still read from block k / bs; only the scale and zero point are
+ * taken from group g_idx[k]).  The caller has range-checked g_idx. */
+static int64_t group_of(const int32_t *g_idx, int64_t k, int64_t bs) {
+    return g_idx ? (int64_t)g_idx[k] : k / bs;
+}
+
+/* Range check of group indices ([ORT] execute: g_idx has shape [K] or
+ * [kb * bs]; dequantize_weight: every entry lies in 0..kb).  Returns -1 if
+ * the shape is wrong, the position of the first out-of-range entry, or
+ * len (no error). */
+EXPORT int64_t oracle_check_g_idx(const int32_t *g_idx, int64_t len, int64_t K,
+                                  int64_t bs) {
+    int64_t kb = n_blocks(K, bs);
+    if (len != K && len != kb * bs) return -1;
+    for (int64_t i = 0; i < len; ++i)
+        if (g_idx[i] < 0 || (int64_t)g_idx[i] >= kb) return i;
+    return len;
+}
+
+/* Dequantized weight w[n*K + k] = (code - zp(g)) * scale[n*kb + g] with g the
+ * group of k (block k / bs, or g_idx[k]), in double ([ORT]
+ * dequantize_nbits_value, dequantize_weight; scales are given already
+ * widened; g_idx may be NULL). */
 EXPORT void oracle_dequantize(const uint8_t *B, const double *scales,
-                              const uint8_t *zp, int64_t N, int64_t K,
-                              int64_t bs, int bits, double *W) {
+                              const uint8_t *zp, const int32_t *g_idx,
+                              int64_t N, int64_t K, int64_t bs, int bits,
+                              double *W) {
     int64_t kb = n_blocks(K, bs);
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
-            int64_t b = k / bs;
+            int64_t g = group_of(g_idx, k, bs);
             double q = (double)code_at(B, n, k, K, bs, bits);
-            double z = (double)zp_at(zp, n, b, kb, bits);
-            W[n * K + k] = (q - z) * scales[n * kb + b];
+            double z = (double)zp_at(zp, n, g, kb, bits);
+            W[n * K + k] = (q - z) * scales[n * kb + g];
         }
 }
 
 /* ------------------------------------------------------------------------ */
 /* O2 float matmul: Y[m, n] = sum_k A[m, k] * w(n, k)  (+ bias[n])            */
 /* ([ORT] module documentation, execute: dequantize then GEMV/GEMM, bias      */
-/*  added after the product)                                                  */
+/*  added after the product; with group indices the scale and zero point of  */
+/*  element k are those of group g_idx[k], [ORT] dequantize_weight)           */
 /* S[m, n] = sum_k |A[m, k] * w(n, k)| + |bias[n]| is the tolerance base.     */
+/* g_idx may be NULL; otherwise it has been range-checked.                    */
 /* ------------------------------------------------------------------------ */
 EXPORT void oracle_matmul_nbits(const double *A, const uint8_t *B,
                                 const double *scales, const uint8_t *zp,
-                                const double *bias, int64_t M, int64_t N,
-                                int64_t K, int64_t bs, int bits, double *Y,
-                                double *S) {
+                                const int32_t *g_idx, const double *bias,
+                                int64_t M, int64_t N, int64_t K, int64_t bs,
+                                int bits, double *Y, double *S) {
     int64_t kb = n_blocks(K, bs);
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0, mag = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                int64_t b = k / bs;
+                int64_t g = group_of(g_idx, k, bs);
                 double q = (double)code_at(B, n, k, K, bs, bits);
-                double z = (double)zp_at(zp, n, b, kb, bits);
-                double w = (q - z) * scales[n * kb + b];
+                double z = (double)zp_at(zp, n, g, kb, bits);
+                double w = (q - z) * scales[n * kb + g];
                 double t = A[m * K + k] * w;
                 acc += t;
                 mag += fabs(t);
