@@ -53,9 +53,10 @@ hipError_t scratch_address(void** out) {
 
 extern "C" int qmm_gemm_compint8_noalloc(const void* A, int a_dtype, const uint8_t* B,
                                          int b_layout, const void* scales, int s_dtype,
-                                         const uint8_t* zero_points, const void* bias, void* Y,
-                                         int64_t M, int64_t K, int64_t N, int block_size,
-                                         int bits, int accuracy_level, void* stream) {
+                                         const uint8_t* zero_points, const int32_t* g_idx,
+                                         int64_t g_idx_len, const void* bias, void* Y, int64_t M,
+                                         int64_t K, int64_t N, int block_size, int bits,
+                                         int accuracy_level, void* stream) {
   const size_t need = qmm_compint8_workspace_size(M, K, block_size);
   if (need > (size_t)QMM_NOALLOC_SCRATCH_BYTES) {
     char msg[512];
@@ -69,7 +70,7 @@ extern "C" int qmm_gemm_compint8_noalloc(const void* A, int a_dtype, const uint8
     return qmm::set_error(QMM_ERR_WORKSPACE, msg);
   }
   return qmm::gemm_compint8_impl("qmm_gemm_compint8_noalloc", A, a_dtype, B, b_layout, scales,
-                                 s_dtype, zero_points, bias, Y, M, K, N, block_size, bits,
-                                 accuracy_level, nullptr, (size_t)QMM_NOALLOC_SCRATCH_BYTES,
-                                 scratch_address, stream);
+                                 s_dtype, zero_points, g_idx, g_idx_len, bias, Y, M, K, N,
+                                 block_size, bits, accuracy_level, nullptr,
+                                 (size_t)QMM_NOALLOC_SCRATCH_BYTES, scratch_address, stream);
 }

@@ -137,12 +137,17 @@ __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
 constexpr int GEMM_WAVES = 8;
 constexpr int GEMM_TPB = 64 * GEMM_WAVES;
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL>
+// GI: group indices (operator layout only): code k of a column takes the
+// scale and zero point of group g_idx[k] (clamped into 0..kb-1) instead of
+// its block's, looked up per code during the dequantization.
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL, bool GI = false>
 __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
-    int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m, int chunks) {
+    int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m, int chunks,
+    const int32_t* __restrict__ g_idx) {
+  static_assert(!(GI && TL), "group indices run on the operator layout");
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int BN = 32 * TN;
@@ -195,6 +200,8 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
       (void*)scales, 0, sc_extent * (int)sizeof(ST), BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
       (void*)zp, 0, HAS_ZP ? zp_extent : 0, BUF_WORD3);
+  const __amdgpu_buffer_rsrc_t rgi = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g_idx, 0, GI ? K * 4 : 0, BUF_WORD3);
   const int cg = ncol / TG, ci = ncol % TG;
   // Byte offset of this thread's codes for the K-step starting at k0 = 64 s:
   // col_code0 + s * code_step.
@@ -231,6 +238,21 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   auto load_b = [&](int k0, int st) {
     const int kt = k0 + khalf;
     const int byte0 = col_code0 + (k0 >> 6) * code_step;
+    if constexpr (GI) {
+      // Codes only; the scales and zero points are looked up per code when
+      // the step is dequantized.
+      if constexpr (WPT >= 4) {
+#pragma unroll
+        for (int w = 0; w < WPT; w += 4) {
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rbc, byte0 + 4 * w, 0, 0);
+          cw[st][w] = t.x; cw[st][w + 1] = t.y; cw[st][w + 2] = t.z; cw[st][w + 3] = t.w;
+        }
+      } else {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbc, byte0, 0, 0);
+        cw[st][0] = t.x; cw[st][1] = t.y;
+      }
+      return;
+    }
     if constexpr (WPT >= 4) {
 #pragma unroll
       for (int w = 0; w < WPT; w += 4) {
@@ -269,6 +291,51 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     if (!dq) return;
     uint16_t* bs = Bs + buf * STAGE;
     const int kt = k0 + khalf;
+    if constexpr (GI) {
+      // Per code k = kt + i: g = g_idx[k] (zero past K, where the activations
+      // are zero), then that group's scale and zero point of this column.
+      // Eight codes at a time, fenced, so the lookups of one group are in
+      // flight together without holding every group's registers.
+      constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+      uint32_t pk[HK / 2];
+#pragma unroll
+      for (int c8 = 0; c8 < HK; c8 += 8) {
+        float s[8], zsv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int g = min(max((int)__builtin_amdgcn_raw_buffer_load_b32(
+                                    rgi, (kt + c8 + j) * 4, 0, 0), 0), kb - 1);
+          const int si = col_sc0 + g;
+          float sv;
+          if constexpr (sizeof(ST) == 4)
+            sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, si * 4, 0, 0));
+          else
+            sv = dt<SDT>::to_f32(__builtin_bit_cast(
+                ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, si * 2, 0, 0)));
+          uint32_t z = 1u << (BITS - 1);
+          if constexpr (HAS_ZP) {
+            const int bit = col_zb0 + g * BITS;
+            z = (__builtin_amdgcn_raw_buffer_load_b8(rzp, ncol_ok ? bit >> 3 : OOB, 0, 0) >>
+                 (bit & 7)) & zm;
+          }
+          s[j] = sv;
+          zsv[j] = (float)z * sv;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const int i0 = c8 + j, i1 = c8 + j + 1;
+          const float q0 = (float)((cw[st][i0 / P] >> ((i0 % P) * BITS)) & zm);
+          const float q1 = (float)((cw[st][i1 / P] >> ((i1 % P) * BITS)) & zm);
+          pk[i0 / 2] = Op::pack(fmaf(q0, s[j], -zsv[j]), fmaf(q1, s[j + 1], -zsv[j + 1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < HK / 8; ++j)
+        *reinterpret_cast<u32x4*>(&bs[lds_at(bcol, (khalf >> 3) + j)]) =
+            u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
+      return;
+    }
     const int blk0 = min(kt >> log2_bs, kb - 1);
     float sf[2], zs[2];
 #pragma unroll
@@ -526,15 +593,19 @@ static hipError_t launch_rows(const MatArgs& a) {
   return hipSuccess;
 }
 
+// Every buffer offset of the MFMA kernel must fit in 31 bits.
+static bool mfma_fits(const MatArgs& a) {
+  const int64_t sz = a.s_dtype == DT_F32 ? 4 : 2;
+  return a.a_dtype != DT_F32 && a.M > 16 && (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 &&
+         a.M * a.K * 2 < 0x7FFFFF00LL && (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
+         (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 < 0x7FFFFF00LL &&
+         (a.N + 32) * a.kb * sz < 0x7FFFFF00LL && a.K * 4 < 0x7FFFFF00LL;
+}
+
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 static hipError_t launch_gemm_t(const MatArgs& a) {
   using ST = typename dt<SDT>::T;
-  // Every buffer offset of the MFMA kernel must fit in 31 bits.
-  const bool mfma_ok = XDT != DT_F32 && a.M > 16 && (a.K % 8) == 0 &&
-                       ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 < 0x7FFFFF00LL &&
-                       (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
-                       (a.N + 32) * (a.chunks + 2) * 64 * BITS / 8 < 0x7FFFFF00LL &&
-                       (a.N + 32) * a.kb * (int64_t)sizeof(ST) < 0x7FFFFF00LL;
+  const bool mfma_ok = mfma_fits(a);
   if constexpr (XDT != DT_F32) {
     if (mfma_ok) {
       // 224-column tiles when they divide N evenly (no partial tiles), else 256.
@@ -559,7 +630,7 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
                          (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
                          (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
                          (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), (int)a.zp_row_bytes,
-                         tiles_m, (int)a.chunks);
+                         tiles_m, (int)a.chunks, (const int32_t*)nullptr);
       return hipGetLastError();
     }
   }
@@ -589,7 +660,58 @@ static hipError_t launch_gemm_x(const MatArgs& a) {
   }
 }
 
+// Group indices on the matrix cores: 256-column tiles, operator layout.
+template <int BITS, int XDT, int SDT, bool HAS_ZP>
+static hipError_t launch_gidx_t(const MatArgs& a) {
+  using ST = typename dt<SDT>::T;
+  const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
+  constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);
+  auto kern = gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
+                     (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
+                     (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
+                     (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), (int)a.zp_row_bytes,
+                     tiles_m, (int)a.chunks, a.g_idx);
+  return hipGetLastError();
+}
+
+template <int BITS, int XDT>
+static hipError_t launch_gidx_s(const MatArgs& a) {
+  auto z = [&](auto sdt) {
+    constexpr int SDT = decltype(sdt)::value;
+    return a.zp ? launch_gidx_t<BITS, XDT, SDT, true>(a) : launch_gidx_t<BITS, XDT, SDT, false>(a);
+  };
+  switch (a.s_dtype) {
+    case DT_F32: return z(std::integral_constant<int, DT_F32>{});
+    case DT_F16: return z(std::integral_constant<int, DT_F16>{});
+    default: return z(std::integral_constant<int, DT_BF16>{});
+  }
+}
+
+template <int BITS>
+static hipError_t launch_gidx_x(const MatArgs& a) {
+  return a.a_dtype == DT_F16 ? launch_gidx_s<BITS, DT_F16>(a) : launch_gidx_s<BITS, DT_BF16>(a);
+}
+
+bool gemm_mfma_gidx_supported(const MatArgs& a) { return !a.tiled && mfma_fits(a); }
+
+hipError_t launch_gemm_mfma_gidx(const MatArgs& a) {
+  switch (a.bits) {
+    case 2: return launch_gidx_x<2>(a);
+    case 4: return launch_gidx_x<4>(a);
+    default: return launch_gidx_x<8>(a);
+  }
+}
+
 hipError_t launch_gemm(const MatArgs& a) {
+  if (a.g_idx) return launch_gidx(a);
   switch (a.bits) {
     case 2: return launch_gemm_x<2>(a);
     case 4: return launch_gemm_x<4>(a);

@@ -173,6 +173,33 @@ int check_workspace(const char* fn, const MatArgs& a, void* workspace, size_t by
   return QMM_OK;
 }
 
+// Group indices (MatMulNBits input 4; matmul_nbits.rs execute: int32 of
+// shape [K] or [kb * block_size]).  The range of the entries is the caller's
+// to check on the host (qmm_check_g_idx): the kernels clamp each entry into
+// 0..kb-1 so that an out-of-range one reads in bounds.
+int validate_g_idx(const char* fn, MatArgs* a, const int32_t* g_idx, int64_t g_idx_len) {
+  if (g_idx == nullptr) {
+    if (g_idx_len != 0)
+      return fail(QMM_ERR_INVALID_ARG, "%s: g_idx is NULL but g_idx_len=%lld. How to fix: pass "
+                  "g_idx_len = 0 without group indices.", fn, (long long)g_idx_len);
+    return QMM_OK;
+  }
+  const int64_t padded = a->kb * a->block_size;
+  if (g_idx_len != a->K && g_idx_len != padded)
+    return fail(QMM_ERR_INVALID_ARG, "%s: g_idx must have shape [%lld] or [%lld], got [%lld]. "
+                "Why: the operator gives one group index per K element (optionally padded to "
+                "whole blocks). How to fix: pass the g_idx tensor's length.", fn,
+                (long long)a->K, (long long)padded, (long long)g_idx_len);
+  if (((uintptr_t)g_idx & 3) != 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: g_idx must be 4-byte aligned (int32).", fn);
+  if (a->tiled)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: group indices are supported on the operator's layout "
+                "only. Why: the tiled buffer is laid out for block-contiguous groups. How to "
+                "fix: pass the operator's B, scales and zero points (QMM_LAYOUT_ORT).", fn);
+  a->g_idx = g_idx;
+  return QMM_OK;
+}
+
 }  // namespace
 
 namespace qmm {
@@ -181,14 +208,24 @@ int set_error(int code, const char* message) { return fail(code, "%s", message);
 
 int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t* B,
                        int b_layout, const void* scales, int s_dtype, const uint8_t* zero_points,
-                       const void* bias, void* Y, int64_t M, int64_t K, int64_t N,
-                       int block_size, int bits, int accuracy_level, void* workspace,
-                       size_t workspace_bytes, hipError_t (*resolve_workspace)(void**),
-                       void* stream) {
+                       const int32_t* g_idx, int64_t g_idx_len, const void* bias, void* Y,
+                       int64_t M, int64_t K, int64_t N, int block_size, int bits,
+                       int accuracy_level, void* workspace, size_t workspace_bytes,
+                       hipError_t (*resolve_workspace)(void**), void* stream) {
   MatArgs a;
   int st = validate_matmul(fn, Route::CompInt8, A, a_dtype, B, b_layout, scales, s_dtype,
                            zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level, &a);
   if (st != QMM_OK) return st;
+  st = validate_g_idx(fn, &a, g_idx, g_idx_len);
+  if (st != QMM_OK) return st;
+  if (a.g_idx != nullptr) {
+    // As the operator routes it: with group indices the weight scale varies
+    // inside an activation block, so there is no per-block integer dot; the
+    // product is computed with float activations (the workspace is unused).
+    if (M == 0) return QMM_OK;
+    a.stream = (hipStream_t)stream;
+    return hip_status(M == 1 ? launch_gemv(a) : launch_gemm(a), fn);
+  }
   const bool small = M > 0 && compint8_small_supported(a);
   if (a.tiled && !small && !compint8_tiled_supported(a))
     return fail(QMM_ERR_UNSUPPORTED, "%s: on the tiled layout CompInt8 needs "
@@ -222,22 +259,28 @@ extern "C" {
 const char* qmm_last_error(void) { return g_last_error.c_str(); }
 
 int qmm_gemv(const void* A, int a_dtype, const uint8_t* B, int b_layout, const void* scales,
-             int s_dtype, const uint8_t* zero_points, const void* bias, void* Y, int64_t K,
-             int64_t N, int block_size, int bits, int accuracy_level, void* stream) {
+             int s_dtype, const uint8_t* zero_points, const int32_t* g_idx, int64_t g_idx_len,
+             const void* bias, void* Y, int64_t K, int64_t N, int block_size, int bits,
+             int accuracy_level, void* stream) {
   MatArgs a;
   int st = validate_matmul("qmm_gemv", Route::Float, A, a_dtype, B, b_layout, scales, s_dtype,
                            zero_points, bias, Y, 1, K, N, block_size, bits, accuracy_level, &a);
+  if (st != QMM_OK) return st;
+  st = validate_g_idx("qmm_gemv", &a, g_idx, g_idx_len);
   if (st != QMM_OK) return st;
   a.stream = (hipStream_t)stream;
   return hip_status(qmm::launch_gemv(a), "qmm_gemv");
 }
 
 int qmm_gemm(const void* A, int a_dtype, const uint8_t* B, int b_layout, const void* scales,
-             int s_dtype, const uint8_t* zero_points, const void* bias, void* Y, int64_t M,
-             int64_t K, int64_t N, int block_size, int bits, int accuracy_level, void* stream) {
+             int s_dtype, const uint8_t* zero_points, const int32_t* g_idx, int64_t g_idx_len,
+             const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
+             int bits, int accuracy_level, void* stream) {
   MatArgs a;
   int st = validate_matmul("qmm_gemm", Route::Float, A, a_dtype, B, b_layout, scales, s_dtype,
                            zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level, &a);
+  if (st != QMM_OK) return st;
+  st = validate_g_idx("qmm_gemm", &a, g_idx, g_idx_len);
   if (st != QMM_OK) return st;
   a.stream = (hipStream_t)stream;
   if (M == 0) return QMM_OK;
@@ -254,12 +297,30 @@ size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size) {
 
 int qmm_gemm_compint8(const void* A, int a_dtype, const uint8_t* B, int b_layout,
                       const void* scales, int s_dtype, const uint8_t* zero_points,
-                      const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
-                      int bits, int accuracy_level, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      const int32_t* g_idx, int64_t g_idx_len, const void* bias, void* Y,
+                      int64_t M, int64_t K, int64_t N, int block_size, int bits,
+                      int accuracy_level, void* workspace, size_t workspace_bytes, void* stream) {
   return qmm::gemm_compint8_impl("qmm_gemm_compint8", A, a_dtype, B, b_layout, scales, s_dtype,
-                                 zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level,
-                                 workspace, workspace_bytes, nullptr, stream);
+                                 zero_points, g_idx, g_idx_len, bias, Y, M, K, N, block_size, bits,
+                                 accuracy_level, workspace, workspace_bytes, nullptr, stream);
+}
+
+int qmm_check_g_idx(const int32_t* g_idx, int64_t g_idx_len, int64_t K, int block_size) {
+  const char* fn = "qmm_check_g_idx";
+  if (g_idx == nullptr || K <= 0 || block_size < 16 || !is_pow2(block_size))
+    return fail(QMM_ERR_INVALID_ARG, "%s: g_idx must be a non-null host array, K > 0 and "
+                "block_size a power of two >= 16.", fn);
+  const int64_t kb = (K + block_size - 1) / block_size;
+  if (g_idx_len != K && g_idx_len != kb * block_size)
+    return fail(QMM_ERR_INVALID_ARG, "%s: g_idx must have shape [%lld] or [%lld], got [%lld].",
+                fn, (long long)K, (long long)(kb * block_size), (long long)g_idx_len);
+  for (int64_t i = 0; i < g_idx_len; ++i)
+    if (g_idx[i] < 0 || (int64_t)g_idx[i] >= kb)
+      return fail(QMM_ERR_INVALID_ARG, "%s: g_idx[%lld]=%d is outside 0..%lld. Why: every "
+                  "group index selects one of the kb = ceil(K / block_size) scales of a row. "
+                  "How to fix: re-export the weight's group indices.", fn, (long long)i,
+                  (int)g_idx[i], (long long)kb);
+  return QMM_OK;
 }
 
 int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,

@@ -14,6 +14,7 @@ struct MatArgs {
   const uint8_t* B = nullptr;     // [N, kb, blob]
   const void* scales = nullptr;   // [N, kb] s_dtype
   const uint8_t* zp = nullptr;    // [N, zp_row_bytes] or null
+  const int32_t* g_idx = nullptr; // [K] group of each K element, or null (block k / bs)
   const void* bias = nullptr;     // [N] a_dtype or null
   void* Y = nullptr;              // [M, N] a_dtype
   int64_t M = 1, K = 0, N = 0;
@@ -31,6 +32,12 @@ struct MatArgs {
 using GemvArgs = MatArgs;
 
 hipError_t launch_gemv(const MatArgs& a);
+// Group indices on the operator's layout (gidx.hip): the fp32 row kernel,
+// or the matrix-core GEMM for 16-bit activations and M > 16.
+hipError_t launch_gidx(const MatArgs& a);
+// The matrix-core GEMM with per-code group lookups (gemm.hip).
+bool gemm_mfma_gidx_supported(const MatArgs& a);
+hipError_t launch_gemm_mfma_gidx(const MatArgs& a);
 // M = 1 on the tiled layout (gemv_tiled.hip).
 bool gemv_tiled_supported(const MatArgs& a);
 hipError_t launch_gemv_tiled(const MatArgs& a);
@@ -87,10 +94,10 @@ hipError_t launch_unpack(const MatArgs& a, uint8_t* codes, uint8_t* zps, float* 
 // workspace, which then holds workspace_bytes.
 int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t* B,
                        int b_layout, const void* scales, int s_dtype, const uint8_t* zero_points,
-                       const void* bias, void* Y, int64_t M, int64_t K, int64_t N,
-                       int block_size, int bits, int accuracy_level, void* workspace,
-                       size_t workspace_bytes, hipError_t (*resolve_workspace)(void**),
-                       void* stream);
+                       const int32_t* g_idx, int64_t g_idx_len, const void* bias, void* Y,
+                       int64_t M, int64_t K, int64_t N, int block_size, int bits,
+                       int accuracy_level, void* workspace, size_t workspace_bytes,
+                       hipError_t (*resolve_workspace)(void**), void* stream);
 // Record a message for qmm_last_error and return code.
 int set_error(int code, const char* message);
 

@@ -32,13 +32,16 @@ lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 _SIGS = {
     "qmm_last_error": ([], ctypes.c_char_p),
-    "qmm_gemv": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
-    "qmm_gemm": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "qmm_gemv": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32,
+                  _i32, _vp], _i32),
+    "qmm_check_g_idx": ([_vp, _i64, _i64, _i32], _i32),
+    "qmm_gemm": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i32,
+                  _i32, _i32, _vp], _i32),
     "qmm_compint8_workspace_size": ([_i64, _i64, _i32], _sz),
-    "qmm_gemm_compint8": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
-                           _i32, _vp, _sz, _vp], _i32),
-    "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64,
-                                   _i32, _i32, _i32, _vp], _i32),
+    "qmm_gemm_compint8": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
+                           _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
+                                   _i64, _i64, _i32, _i32, _i32, _vp], _i32),
     "qconv_int8": ([_vp, _vp, _vp, _vp, _f32, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "qmm_repacked_bytes": ([_i64, _i64, _i32, _i32, _i32, _i32], _sz),
@@ -126,18 +129,33 @@ def _weights(B, scales, K, N, block_size, bits):
     return B.data_ptr(), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales)
 
 
+def _g(g_idx):
+    """(pointer, length) of optional int32 group indices."""
+    return (None, 0) if g_idx is None else (g_idx.data_ptr(), g_idx.numel())
+
+
 def qmm_gemv(A, B, scales, zero_points, bias, Y, K, N, block_size, bits, accuracy_level=0,
-             stream=None):
+             stream=None, g_idx=None):
     b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
-    _check(lib.qmm_gemv(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
-                        _ptr(Y), K, N, block_size, bits, accuracy_level, _stream(stream)))
+    gp, gn = _g(g_idx)
+    _check(lib.qmm_gemv(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), gp, gn,
+                        _ptr(bias), _ptr(Y), K, N, block_size, bits, accuracy_level,
+                        _stream(stream)))
+
+
+def qmm_check_g_idx(g_idx, K, block_size):
+    """Host-side range / shape check of group indices (a CPU int32 tensor)."""
+    g = g_idx.contiguous()
+    _check(lib.qmm_check_g_idx(g.data_ptr(), g.numel(), K, block_size))
 
 
 def qmm_gemm(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, accuracy_level=0,
-             stream=None):
+             stream=None, g_idx=None):
     b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
-    _check(lib.qmm_gemm(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
-                        _ptr(Y), M, K, N, block_size, bits, accuracy_level, _stream(stream)))
+    gp, gn = _g(g_idx)
+    _check(lib.qmm_gemm(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), gp, gn,
+                        _ptr(bias), _ptr(Y), M, K, N, block_size, bits, accuracy_level,
+                        _stream(stream)))
 
 
 def qmm_repacked_bytes(K, N, block_size, bits, s_dtype, has_zero_points) -> int:
@@ -170,10 +188,11 @@ def qmm_compint8_workspace_size(M, K, block_size) -> int:
 
 
 def qmm_gemm_compint8(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, workspace,
-                      accuracy_level=4, stream=None):
+                      accuracy_level=4, stream=None, g_idx=None):
     b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
-    _check(lib.qmm_gemm_compint8(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), _ptr(bias),
-                                 _ptr(Y), M, K, N, block_size, bits, accuracy_level,
+    gp, gn = _g(g_idx)
+    _check(lib.qmm_gemm_compint8(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points), gp, gn,
+                                 _ptr(bias), _ptr(Y), M, K, N, block_size, bits, accuracy_level,
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
 
@@ -182,10 +201,11 @@ QMM_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024
 
 
 def qmm_gemm_compint8_noalloc(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits,
-                              accuracy_level=4, stream=None):
+                              accuracy_level=4, stream=None, g_idx=None):
     b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
+    gp, gn = _g(g_idx)
     _check(lib.qmm_gemm_compint8_noalloc(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points),
-                                         _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
+                                         gp, gn, _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
                                          accuracy_level, _stream(stream)))
 
 

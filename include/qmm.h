@@ -75,17 +75,37 @@ const char *qmm_last_error(void);
  *          buffer written by qmm_repack, layout QMM_LAYOUT_TILED[_ZP])
  *   scales [N, kb]        s_dtype
  *   zero_points [N, ceil(kb*bits/8)] uint8 or NULL
+ *   g_idx  [g_idx_len]    int32 group indices or NULL (then g_idx_len = 0)
  *   bias   [N]            a_dtype or NULL
  *   Y      [N]            a_dtype (written)
  * bits in {2, 4, 8}; block_size a power of two >= 16 (MatMulNBitsFactory::
  * create).  accuracy_level 0..3 select float compute; the hint can only raise
  * precision and every level computes fp32-accumulated products here.
  * accuracy_level 4 (int8 activations) is rejected: use qmm_gemm_compint8.
+ *
+ * Group indices (act-order; matmul_nbits.rs execute and the group-index
+ * branch of dequantize_weight): element k keeps its code from block k / bs
+ * but takes the scale and zero point of group g_idx[k]:
+ *   w(n, k) = (code(n, k) - zp(n, g_idx[k])) * scale[n, g_idx[k]].
+ * g_idx is a device array of g_idx_len = K or kb * block_size int32 values
+ * (the first K are read), operator layout only (QMM_ERR_UNSUPPORTED on a
+ * tiled B).  Every entry must lie in 0..kb-1: check a host copy once with
+ * qmm_check_g_idx.  The kernels clamp an out-of-range entry into that range
+ * (it reads in bounds and gives a wrong result, never a fault).
  */
 int qmm_gemv(const void *A, int a_dtype, const uint8_t *B, int b_layout,
              const void *scales, int s_dtype, const uint8_t *zero_points,
-             const void *bias, void *Y, int64_t K, int64_t N, int block_size,
-             int bits, int accuracy_level, void *stream);
+             const int32_t *g_idx, int64_t g_idx_len, const void *bias,
+             void *Y, int64_t K, int64_t N, int block_size, int bits,
+             int accuracy_level, void *stream);
+
+/*
+ * Range and shape check of group indices held in HOST memory (matmul_nbits.rs
+ * execute: shape [K] or [kb * block_size]; dequantize_weight: every entry in
+ * 0..kb).  QMM_OK, or QMM_ERR_INVALID_ARG naming the first bad entry.
+ */
+int qmm_check_g_idx(const int32_t *g_idx, int64_t g_idx_len, int64_t K,
+                    int block_size);
 
 /*
  * Batched / prefill matmul, A [M, K] -> Y [M, N]; the other arguments as for
@@ -95,8 +115,9 @@ int qmm_gemv(const void *A, int a_dtype, const uint8_t *B, int b_layout,
  */
 int qmm_gemm(const void *A, int a_dtype, const uint8_t *B, int b_layout,
              const void *scales, int s_dtype, const uint8_t *zero_points,
-             const void *bias, void *Y, int64_t M, int64_t K, int64_t N,
-             int block_size, int bits, int accuracy_level, void *stream);
+             const int32_t *g_idx, int64_t g_idx_len, const void *bias, void *Y,
+             int64_t M, int64_t K, int64_t N, int block_size, int bits,
+             int accuracy_level, void *stream);
 
 /*
  * CompInt8 (accuracy_level 4; matmul_nbits.rs: quantize_activation_signed,
@@ -117,14 +138,19 @@ int qmm_gemm(const void *A, int a_dtype, const uint8_t *B, int b_layout,
  * run on the int8 matrix cores), and for M = 1 also when block_size is at
  * least one 16-byte unit of codes (32, 64 or 16 codes for 4, 2 or 8 bits)
  * and at most 1024; otherwise QMM_ERR_UNSUPPORTED.
+ * With group indices (g_idx, as for qmm_gemv) the weight scale changes
+ * inside an activation block, so no per-block integer dot exists; as the
+ * operator does, the product is then computed with float activations (the
+ * result of qmm_gemm) and the workspace is not used.
  */
 size_t qmm_compint8_workspace_size(int64_t M, int64_t K, int block_size);
 
 int qmm_gemm_compint8(const void *A, int a_dtype, const uint8_t *B,
                       int b_layout, const void *scales, int s_dtype,
-                      const uint8_t *zero_points, const void *bias, void *Y,
-                      int64_t M, int64_t K, int64_t N, int block_size,
-                      int bits, int accuracy_level, void *workspace,
+                      const uint8_t *zero_points, const int32_t *g_idx,
+                      int64_t g_idx_len, const void *bias, void *Y, int64_t M,
+                      int64_t K, int64_t N, int block_size, int bits,
+                      int accuracy_level, void *workspace,
                       size_t workspace_bytes, void *stream);
 
 /*
@@ -146,10 +172,10 @@ int qmm_gemm_compint8(const void *A, int a_dtype, const uint8_t *B,
 
 int qmm_gemm_compint8_noalloc(const void *A, int a_dtype, const uint8_t *B,
                               int b_layout, const void *scales, int s_dtype,
-                              const uint8_t *zero_points, const void *bias,
-                              void *Y, int64_t M, int64_t K, int64_t N,
-                              int block_size, int bits, int accuracy_level,
-                              void *stream);
+                              const uint8_t *zero_points, const int32_t *g_idx,
+                              int64_t g_idx_len, const void *bias, void *Y,
+                              int64_t M, int64_t K, int64_t N, int block_size,
+                              int bits, int accuracy_level, void *stream);
 
 /*
  * int8 convolution with requantization (MNN ConvInt8TiledExecutor.cpp:

@@ -45,8 +45,8 @@ def gemv(qmm, **kw):
              Y=FAKE, K=4096, N=4096, bs=32, bits=4, acc=0)
     a.update(kw)
     return qmm.lib.qmm_gemv(a["A"], a["a_dtype"], a["B"], a["b_layout"], a["scales"],
-                            a["s_dtype"], a["zp"], a["bias"], a["Y"], a["K"], a["N"], a["bs"],
-                            a["bits"], a["acc"], None)
+                            a["s_dtype"], a["zp"], a.get("g", None), a.get("glen", 0), a["bias"],
+                            a["Y"], a["K"], a["N"], a["bs"], a["bits"], a["acc"], None)
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -67,6 +67,10 @@ def gemv(qmm, **kw):
     (dict(B=FAKE + 8), -1, "16-byte aligned"),
     (dict(A=FAKE + 1), -1, "aligned to their element size"),
     (dict(K=1 << 31), -2, "below 2^30"),
+    (dict(g=None, glen=5), -1, "g_idx is NULL"),
+    (dict(g=FAKE, glen=100), -1, "g_idx must have shape [4096] or [4096]"),
+    (dict(g=FAKE + 2, glen=4096), -1, "g_idx must be 4-byte aligned"),
+    (dict(g=FAKE, glen=4096, b_layout=2, scales=None), -2, "operator's layout only"),
 ])
 def test_gemv_rejects_bad_arguments(qmm, kw, code, needle):
     assert gemv(qmm, **kw) == code
@@ -77,20 +81,20 @@ def test_gemv_rejects_bad_arguments(qmm, kw, code, needle):
 
 
 def test_compint8_requires_level_4_and_workspace_size(qmm):
-    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096, 4096, 128,
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 4, 4096, 4096, 128,
                                    4, 0, FAKE, 1 << 20, None)
     assert st == -1 and "accuracy_level must be 4" in qmm.qmm_last_error()
     # int8 activations [M, kb*bs] + float scales [M, kb], regions 256-byte aligned.
     ws = qmm.qmm_compint8_workspace_size(16, 4096, 128)
     assert ws >= 16 * 4096 + 4 * 16 * 32 and ws % 256 == 0
     assert qmm.qmm_compint8_workspace_size(1, 100, 64) >= 128 + 4 * 2
-    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096, 4096, 128,
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 4, 4096, 4096, 128,
                                    4, 4, FAKE, 100, None)
     assert st == -3 and "workspace" in qmm.qmm_last_error()
 
 
 def test_gemm_with_m_zero_is_a_noop(qmm):
-    st = qmm.lib.qmm_gemm(None, 2, FAKE, 0, FAKE, 2, None, None, None, 0, 64, 64, 32, 4, 0, None)
+    st = qmm.lib.qmm_gemm(None, 2, FAKE, 0, FAKE, 2, None, None, 0, None, None, 0, 64, 64, 32, 4, 0, None)
     assert st == 0
 
 
@@ -148,12 +152,12 @@ def test_repack_rejects_bad_arguments(qmm):
 
 
 def test_compint8_tiled_layout_needs_whole_chunks_per_block(qmm):
-    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, FAKE, 4, 4096, 4096, 32,
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, 0, None, FAKE, 4, 4096, 4096, 32,
                                    4, 4, FAKE, 1 << 30, None)
     assert st == -2 and "block_size >= 64" in qmm.qmm_last_error()
     # M = 1 takes blocks down to one 16-byte unit of codes (32 codes at 4
     # bits); 16 is shorter, so it is rejected on the host as well.
-    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, FAKE, 1, 4096, 4096, 16,
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, 0, None, FAKE, 1, 4096, 4096, 16,
                                    4, 4, FAKE, 1 << 30, None)
     assert st == -2 and "M = 1" in qmm.qmm_last_error()
 
@@ -218,12 +222,47 @@ def test_noalloc_compint8_rejects_on_the_host(qmm):
     and validates its other arguments like qmm_gemm_compint8."""
     lim = qmm.QMM_NOALLOC_SCRATCH_BYTES
     assert qmm.qmm_compint8_workspace_size(300, 16384, 128) > lim
-    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 300,
+    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 300,
                                            16384, 64, 128, 4, 4, None)
     assert st == -3 and "row batches" in qmm.qmm_last_error()
-    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096,
+    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 4, 4096,
                                            64, 128, 3, 4, None)
     assert st == -1 and "bits must be 2, 4 or 8" in qmm.qmm_last_error()
-    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, FAKE, 4, 4096,
+    st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 4, 4096,
                                            64, 128, 4, 0, None)
     assert st == -1 and "accuracy_level must be 4" in qmm.qmm_last_error()
+
+
+def test_check_g_idx_on_host_arrays(qmm):
+    """qmm_check_g_idx: shape [K] or [kb * bs], every entry in 0..kb-1, the
+    first bad entry named (matmul_nbits.rs execute / dequantize_weight)."""
+    import numpy as np
+    import torch
+    K, bs = 100, 32                                 # kb = 4, padded 128
+    qmm.qmm_check_g_idx(torch.zeros(K, dtype=torch.int32), K, bs)
+    qmm.qmm_check_g_idx(torch.arange(128, dtype=torch.int32) // 32, K, bs)
+    g = torch.zeros(K, dtype=torch.int32)
+    g[37] = 4
+    with pytest.raises(qmm.QmmError, match=r"g_idx\[37\]=4 is outside 0..4"):
+        qmm.qmm_check_g_idx(g, K, bs)
+    g[37] = -1
+    with pytest.raises(qmm.QmmError, match=r"g_idx\[37\]=-1"):
+        qmm.qmm_check_g_idx(g, K, bs)
+    gp = torch.zeros(128, dtype=torch.int32)
+    gp[127] = 7                                    # padding entries are checked too
+    with pytest.raises(qmm.QmmError, match=r"g_idx\[127\]=7"):
+        qmm.qmm_check_g_idx(gp, K, bs)
+    with pytest.raises(qmm.QmmError, match="must have shape"):
+        qmm.qmm_check_g_idx(torch.zeros(101, dtype=torch.int32), K, bs)
+    # Agrees with the oracle's check on random indices.
+    import oracle
+    rng = np.random.default_rng(0)
+    for t in range(20):
+        a = rng.integers(-2, 6, K).astype(np.int32)
+        try:
+            oracle.check_g_idx(a, K, bs)
+            ok = True
+        except oracle.GroupIndexError:
+            ok = False
+        st = qmm.lib.qmm_check_g_idx(a.ctypes.data, K, K, bs)
+        assert (st == 0) == ok
