@@ -165,6 +165,60 @@ def main():
         torch.cuda.synchronize()
         return t_start.elapsed_time(t_end) / args.steps
 
+    def time_steps_host(clist, weights):
+        """ms per layer step as a host issues it: the launches of each step
+        in order, no device-side spin ahead of them, so the host's work per
+        call counts wherever it is longer than the kernels."""
+        launch = series(clist, weights)
+
+        def step(s):
+            for i in range(len(clist)):
+                launch(i, s % n_copies)
+
+        for s in range(args.warmup):
+            step(s)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for s in range(args.steps):
+            step(s)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    def time_graph_steps(clist, weights):
+        """The same step recorded once per weight copy (qmm_step: its launches
+        captured into one HIP graph) and replayed: (host-issued ms, device-only
+        ms) per step."""
+        xs = [c.to(dev).A.reshape(-1) for c in clist]
+        ys = [torch.empty(c.N, dtype=torch.bfloat16, device=dev) for c in clist]
+        steps = []
+        for j in range(n_copies):
+            st = qmm.Step()
+            for i, c in enumerate(clist):
+                B, sc, zp = weights[i][j]
+                st.add_gemv(xs[i], B, sc, zp, None, ys[i], c.K, c.N, c.block_size, c.bits)
+            steps.append(st.finalize())
+        for s in range(args.warmup):
+            steps[s % n_copies].launch(stream)
+        torch.cuda.synchronize()
+        res = []
+        for spin in (False, True):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            if spin:
+                _queue_ahead(args.steps)
+            t0.record(stream)
+            for s in range(args.steps):
+                steps[s % n_copies].launch(stream)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            res.append(t0.elapsed_time(t1) / args.steps)
+        for st in steps:
+            st.close()
+        return res[0], res[1]
+
     def time_kernel(clist, weights, idx):
         """ms per launch of the GEMVs clist[i], i in idx, launched back to back
         (rotating weight copies) between one pair of HIP events on the launch
@@ -185,6 +239,8 @@ def main():
         return e0.elapsed_time(e1) / n
 
     ms_f = time_steps(fcases, ftiled)
+    ms_f_host = time_steps_host(fcases, ftiled)
+    ms_g_host, ms_g_dev = time_graph_steps(fcases, ftiled)
     ms_t = time_steps(cases, tiled)
     ms_o = time_steps(cases, pools)
     # Dominant kernel of the step: the gate|up launch (K = 4096, N = 28672).
@@ -235,6 +291,18 @@ def main():
             "traffic": measured_traffic("gemv_tiled_K4096_N28672_traffic.txt"),
             "avg_launch_us": round(fdom_ms * 1e3, 3),
             "bytes_per_launch": fdom_bytes,
+        },
+        "step_launch": {
+            "what": "the same four-launch step: device-only (launches queued behind a "
+                    "device-side spin) and as a host issues it (no spin: the binding's work "
+                    "per call counts where it is longer than the kernels), with direct "
+                    "qmm_gemv calls and with the calls recorded once as one HIP graph "
+                    "(qmm_step) and replayed",
+            "direct_device_ms": round(ms_f, 5),
+            "direct_host_issued_ms": round(ms_f_host, 5),
+            "graph_device_ms": round(ms_g_dev, 5),
+            "graph_host_issued_ms": round(ms_g_host, 5),
+            "graph_host_issued_GBps": round(fstep_bytes / (ms_g_host * 1e-3) / 1e9, 2),
         },
         "unfused": {
             "what": "the seven projections as seven launches, tiled layout",

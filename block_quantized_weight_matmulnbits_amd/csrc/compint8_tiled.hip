@@ -294,14 +294,8 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   const size_t lds = ct_lds(a.kb, Kp, CS, S, STAGE, rows);
   auto kern = compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE>;
   if (lds > 64 * 1024) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)CT_STAGE_LDS_MAX);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)CT_STAGE_LDS_MAX);
+    if (e != hipSuccess) return e;
   }
   const int grid = (n_slices + CS - 1) / CS;
   using YT = typename dt<YDT>::T;

@@ -618,14 +618,8 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
                                : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, true>;
       else kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, false>
                        : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>;
-      const int which = (n224 ? 1 : 0) + (a.tiled ? 2 : 0);
-      static bool attr_set[4] = {false, false, false, false};
-      if (!attr_set[which]) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set[which] = true;
-      }
+      const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
                          (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
                          (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
@@ -667,13 +661,8 @@ static hipError_t launch_gidx_t(const MatArgs& a) {
   const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
   constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);
   auto kern = gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false, true>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
                      (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
                      (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,

@@ -6,7 +6,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+#include <set>
 #include <string>
+#include <tuple>
 
 #include "../../include/qmm.h"
 #include "qmm_internal.h"
@@ -205,6 +208,20 @@ int validate_g_idx(const char* fn, MatArgs* a, const int32_t* g_idx, int64_t g_i
 namespace qmm {
 
 int set_error(int code, const char* message) { return fail(code, "%s", message); }
+
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::tuple<int, const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, kernel, bytes);
+  if (done.count(key)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert(key);
+  return e;
+}
 
 int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t* B,
                        int b_layout, const void* scales, int s_dtype, const uint8_t* zero_points,

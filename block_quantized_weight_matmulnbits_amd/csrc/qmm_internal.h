@@ -98,6 +98,10 @@ int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t
                        int64_t M, int64_t K, int64_t N, int block_size, int bits,
                        int accuracy_level, void* workspace, size_t workspace_bytes,
                        hipError_t (*resolve_workspace)(void**), void* stream);
+// Allow `kernel` up to `bytes` of dynamic LDS on the current device
+// (hipFuncSetAttribute once per device and kernel; thread-safe).
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+
 // Record a message for qmm_last_error and return code.
 int set_error(int code, const char* message);
 

@@ -42,6 +42,17 @@ _SIGS = {
                            _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
                                    _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "qmm_step_create": ([_vp], _i32),
+    "qmm_step_add_gemv": ([_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64,
+                           _i32, _i32, _i32], _i32),
+    "qmm_step_add_gemm": ([_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64,
+                           _i64, _i32, _i32, _i32], _i32),
+    "qmm_step_add_gemm_compint8": ([_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp,
+                                    _i64, _i64, _i64, _i32, _i32, _i32, _vp, _sz], _i32),
+    "qmm_step_finalize": ([_vp], _i32),
+    "qmm_step_launch": ([_vp, _vp], _i32),
+    "qmm_step_size": ([_vp], _i32),
+    "qmm_step_destroy": ([_vp], None),
     "qconv_int8": ([_vp, _vp, _vp, _vp, _f32, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "qmm_repacked_bytes": ([_i64, _i64, _i32, _i32, _i32, _i32], _sz),
@@ -207,6 +218,73 @@ def qmm_gemm_compint8_noalloc(A, B, scales, zero_points, bias, Y, M, K, N, block
     _check(lib.qmm_gemm_compint8_noalloc(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points),
                                          gp, gn, _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
                                          accuracy_level, _stream(stream)))
+
+
+class Step:
+    """A recorded sequence of matmul calls replayed as one HIP graph
+    (qmm_step_* in include/qmm.h).  add_gemv / add_gemm / add_gemm_compint8
+    take the arguments of the functions of the same name (without a stream);
+    finalize() validates and captures; launch(stream) replays.  The tensors
+    passed are kept referenced for the step's life, since the graph holds
+    their device addresses."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib.qmm_step_create(ctypes.byref(h)))
+        self._h = h
+        self._keep = []
+
+    def _add(self, fn, tensors, *args):
+        self._keep.extend(t for t in tensors if t is not None)
+        _check(fn(self._h, *args))
+
+    def add_gemv(self, A, B, scales, zero_points, bias, Y, K, N, block_size, bits,
+                 accuracy_level=0, g_idx=None):
+        b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
+        gp, gn = _g(g_idx)
+        self._add(lib.qmm_step_add_gemv, (A, B, scales, zero_points, bias, Y, g_idx), _ptr(A),
+                  _dt(A), b, layout, s, sdt, _ptr(zero_points), gp, gn, _ptr(bias), _ptr(Y), K, N,
+                  block_size, bits, accuracy_level)
+
+    def add_gemm(self, A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits,
+                 accuracy_level=0, g_idx=None):
+        b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
+        gp, gn = _g(g_idx)
+        self._add(lib.qmm_step_add_gemm, (A, B, scales, zero_points, bias, Y, g_idx), _ptr(A),
+                  _dt(A), b, layout, s, sdt, _ptr(zero_points), gp, gn, _ptr(bias), _ptr(Y), M, K,
+                  N, block_size, bits, accuracy_level)
+
+    def add_gemm_compint8(self, A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits,
+                          workspace, accuracy_level=4, g_idx=None):
+        b, layout, s, sdt = _weights(B, scales, K, N, block_size, bits)
+        gp, gn = _g(g_idx)
+        self._add(lib.qmm_step_add_gemm_compint8,
+                  (A, B, scales, zero_points, bias, Y, g_idx, workspace), _ptr(A), _dt(A), b,
+                  layout, s, sdt, _ptr(zero_points), gp, gn, _ptr(bias), _ptr(Y), M, K, N,
+                  block_size, bits, accuracy_level, _ptr(workspace),
+                  workspace.numel() * workspace.element_size())
+
+    def finalize(self):
+        _check(lib.qmm_step_finalize(self._h))
+        return self
+
+    def launch(self, stream=None):
+        _check(lib.qmm_step_launch(self._h, _stream(stream)))
+
+    def __len__(self):
+        return int(lib.qmm_step_size(self._h))
+
+    def close(self):
+        if self._h:
+            lib.qmm_step_destroy(self._h)
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def qconv_int8(X, W, bias, w_scale, in_scale, out_scale, in_zp, out_zp, clamp_min, clamp_max,

@@ -178,6 +178,69 @@ int qmm_gemm_compint8_noalloc(const void *A, int a_dtype, const uint8_t *B,
                               int bits, int accuracy_level, void *stream);
 
 /*
+ * A step: a fixed sequence of matmul calls (say the projections of one
+ * decode step) recorded once and replayed as one HIP graph.  The pages find
+ * the decode step's cost outside the kernels -- per-operator dispatch and
+ * fork/join made decode 2.3x slower, and a persistent pool took it from 6 to
+ * 28 tok/s (matmul_nbits.rs, module notes on the decode step and the
+ * persistent decode pool); here that cost is the host's validation and
+ * enqueue per call, which a small projection's kernel does not cover.
+ *   qmm_step_create        a new, empty step (host object; never NULL on QMM_OK)
+ *   qmm_step_add_gemv / _gemm / _gemm_compint8
+ *                          record one call with the arguments of qmm_gemv /
+ *                          qmm_gemm / qmm_gemm_compint8 (no stream); nothing
+ *                          is validated or enqueued yet
+ *   qmm_step_finalize      validate every recorded call and capture their
+ *                          launches into a graph on the current device (an
+ *                          internal stream; error: the first failing call's
+ *                          status, its position in the message)
+ *   qmm_step_launch        enqueue the whole sequence on `stream` with one
+ *                          graph launch (the device current at finalize)
+ *   qmm_step_size          number of recorded calls
+ *   qmm_step_destroy       free the step and its graph (NULL is a no-op)
+ * A replay runs exactly the direct calls' kernels with the same arguments:
+ * every pointer recorded must stay valid until the step is destroyed, and
+ * inputs are changed in place between launches.  The recorded calls enqueue
+ * no memory-set operations.  A step is not thread-safe; launches of one step
+ * on different streams may overlap and then race on its outputs.
+ */
+typedef struct qmm_step qmm_step;
+
+int qmm_step_create(qmm_step **step);
+
+int qmm_step_add_gemv(qmm_step *step, const void *A, int a_dtype,
+                      const uint8_t *B, int b_layout, const void *scales,
+                      int s_dtype, const uint8_t *zero_points,
+                      const int32_t *g_idx, int64_t g_idx_len,
+                      const void *bias, void *Y, int64_t K, int64_t N,
+                      int block_size, int bits, int accuracy_level);
+
+int qmm_step_add_gemm(qmm_step *step, const void *A, int a_dtype,
+                      const uint8_t *B, int b_layout, const void *scales,
+                      int s_dtype, const uint8_t *zero_points,
+                      const int32_t *g_idx, int64_t g_idx_len,
+                      const void *bias, void *Y, int64_t M, int64_t K,
+                      int64_t N, int block_size, int bits, int accuracy_level);
+
+int qmm_step_add_gemm_compint8(qmm_step *step, const void *A, int a_dtype,
+                               const uint8_t *B, int b_layout,
+                               const void *scales, int s_dtype,
+                               const uint8_t *zero_points,
+                               const int32_t *g_idx, int64_t g_idx_len,
+                               const void *bias, void *Y, int64_t M,
+                               int64_t K, int64_t N, int block_size,
+                               int bits, int accuracy_level, void *workspace,
+                               size_t workspace_bytes);
+
+int qmm_step_finalize(qmm_step *step);
+
+int qmm_step_launch(const qmm_step *step, void *stream);
+
+int qmm_step_size(const qmm_step *step);
+
+void qmm_step_destroy(qmm_step *step);
+
+/*
  * int8 convolution with requantization (MNN ConvInt8TiledExecutor.cpp:
  * initializeConvInt8QuantInfo, im2col padding with the input zero point,
  * QuanPostTreatParameters clamp; rlx-cpu quant.rs: exec_q_mat_mul).

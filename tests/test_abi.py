@@ -266,3 +266,23 @@ def test_check_g_idx_on_host_arrays(qmm):
             ok = False
         st = qmm.lib.qmm_check_g_idx(a.ctypes.data, K, K, bs)
         assert (st == 0) == ok
+
+
+def test_step_object_host_checks(qmm):
+    """qmm_step_*: create / record / destroy on the host; finalizing an empty
+    step and launching an unfinalized one are rejected before any device
+    work."""
+    import ctypes as c
+    h = c.c_void_p()
+    assert qmm.lib.qmm_step_create(c.byref(h)) == 0 and h.value
+    assert qmm.lib.qmm_step_size(h) == 0
+    assert qmm.lib.qmm_step_finalize(h) == -1
+    assert "no call was recorded" in qmm.qmm_last_error()
+    assert qmm.lib.qmm_step_add_gemv(h, FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE,
+                                     4096, 4096, 32, 4, 0) == 0
+    assert qmm.lib.qmm_step_size(h) == 1
+    assert qmm.lib.qmm_step_launch(h, None) == -1
+    assert "not finalized" in qmm.qmm_last_error()
+    qmm.lib.qmm_step_destroy(h)
+    qmm.lib.qmm_step_destroy(None)
+    assert qmm.lib.qmm_step_create(None) == -1
