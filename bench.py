@@ -67,6 +67,8 @@ def parse():
                         "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
+    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny"], default=None,
+                   help="time only this workload and print its object (profiling runs)")
     p.add_argument("--read-sweep", action="store_true",
                    help="only sweep the plain streaming read (bench_probe/) over launch shapes "
                         "and sizes and print a markdown table")
@@ -93,6 +95,20 @@ def main():
     torch.cuda.set_device(dev)
     if args.read_sweep:
         read_sweep(dev, torch.cuda.current_stream(dev))
+        return
+    if args.only:
+        from block_quantized_weight_matmulnbits_amd import qmm
+        stream = torch.cuda.current_stream(dev)
+        if args.copy_calibration:
+            src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        fn = {"compint8": bench_compint8, "prefill": bench_prefill, "conv": bench_conv,
+              "tiny": bench_tiny}[args.only]
+        print(json.dumps({args.only: fn(qmm, dev, stream, args)}), flush=True)
         return
     if args.copy_calibration:
         src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
@@ -328,12 +344,14 @@ def main():
     }
 
     out["roofline"]["read_ceiling"] = read_ceiling(dev, stream, fdom_bytes, fdom_ms)
+    out["tiny"] = bench_tiny(qmm, dev, stream, args)
     out["prefill_gemm"] = bench_prefill(qmm, dev, stream, args)
     out["compint8"] = bench_compint8(qmm, dev, stream, args)
     out["conv_int8"] = bench_conv(qmm, dev, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
+        out["cpu_baseline_configs"] = cpu_baseline_configs(args.cpu_seconds / 4)
 
     print(json.dumps(out), flush=True)
 
@@ -502,6 +520,35 @@ def read_sweep(dev, stream):
     probe.release()
 
 
+def bench_tiny(qmm, dev, stream, args):
+    """The tiny configuration (M=1, K=N=256, f32, 4-bit symmetric block 32):
+    a latency case (43,008 bytes, 5 ns at HBM peak).  Per launch: device-only
+    (launches queued behind a spin) and host-issued (one launch after another,
+    each waited for: what a caller sees for one call)."""
+    from block_quantized_weight_matmulnbits_amd.workloads import tiny_matmulnbits
+    c = tiny_matmulnbits().to(dev)
+    y = torch.empty(c.N, dtype=torch.float32, device=dev)
+    x = c.A.reshape(-1)
+
+    def run(_):
+        qmm.qmm_gemv(x, c.B, c.scales, None, None, y, c.K, c.N, c.block_size, c.bits, 0, stream)
+
+    dev_ms = _time_launches(run, max(100, args.steps), stream)
+    # One call at a time, synchronized: the latency of a lone call.
+    n = 200
+    t0 = time.perf_counter()
+    for i in range(n):
+        run(i)
+        torch.cuda.synchronize()
+    lone_us = (time.perf_counter() - t0) / n * 1e6
+    nbytes = c.weight_bytes() + c.K * 4 + c.N * 4
+    return {"workload": "tiny MatMulNBits M=1 K=256 N=256, f32 activations, 4-bit symmetric "
+                        "block 32, f32 scales, f32 output (operator layout)",
+            "bytes_per_launch": nbytes,
+            "device_us_per_launch": round(dev_ms * 1e3, 3),
+            "host_call_and_sync_us": round(lone_us, 2)}
+
+
 def bench_prefill(qmm, dev, stream, args):
     """Prefill GEMM M=2048, K=4096, N=14336 (4-bit asymmetric bs 32, bf16), on
     the operator's layout and on the tiled layout (weights repacked once,
@@ -623,6 +670,76 @@ def cpu_baseline(cases, seconds):
                   f"{el:.1f} s, OpenMP over output columns",
         "ms_per_step": round(el / reps * 1e3, 2),
     }
+
+
+def _timed(fn, seconds):
+    """Run fn() until `seconds` have passed (at least once); seconds per call."""
+    fn()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return el / reps, reps
+
+
+def cpu_baseline_configs(seconds):
+    """The oracle on the other configurations, each on a bounded sample,
+    scaled to the configuration's own unit."""
+    import numpy as np
+
+    import oracle
+    from block_quantized_weight_matmulnbits_amd.workloads import (COMPINT8_VARIANTS,
+                                                                   compint8_case, make_conv_case,
+                                                                   prefill_gemm, tiny_matmulnbits)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    f64 = lambda t: None if t is None else t.double().numpy()
+    u8 = lambda t: None if t is None else t.numpy()
+    res = {"cores": threads, "kind": "oracle"}
+    # Tiny: the whole problem.
+    c = tiny_matmulnbits()
+    sec, reps = _timed(lambda: oracle.matmul_nbits(f64(c.A), u8(c.B), f64(c.scales), None, None,
+                                                   c.N, c.K, c.block_size, c.bits), seconds / 4)
+    res["tiny"] = {"us_per_call": round(sec * 1e6, 2), "sample": "the whole problem",
+                   "reps": reps}
+    # CompInt8: quantize the activations and the full matmul, on 512 columns.
+    ci8 = {}
+    for bits, bs, asym in COMPINT8_VARIANTS:
+        for M in (1, 16):
+            c = compint8_case(M, bits, bs, asym)
+            ncol = 512
+            B, S = u8(c.B[:ncol]), f64(c.scales[:ncol])
+            Z = None if c.zero_points is None else u8(c.zero_points[:ncol])
+            A = c.A.float().numpy()
+
+            def run(A=A, B=B, S=S, Z=Z, c=c, ncol=ncol):
+                qa, sa = oracle.quantize_a(A, c.K, c.block_size)
+                oracle.compint8_matmul(qa, sa, B, S, Z, None, ncol, c.K, c.block_size, c.bits)
+
+            sec, reps = _timed(run, seconds / 8)
+            byts = (c.weight_bytes() * ncol // c.N) + A.size * 2 + M * ncol * 2
+            ci8[f"b{bits}_bs{bs}_M{M}"] = {"GBps": round(byts / sec / 1e9, 4), "reps": reps}
+    res["compint8"] = {"sample": "512 of the 14336 columns (all K), activations quantized "
+                                 "in every call", "per_case": ci8}
+    # Prefill: 4 rows of A against every column.
+    c = prefill_gemm()
+    A = f64(c.A[:4])
+    sec, reps = _timed(lambda: oracle.matmul_nbits(A, u8(c.B), f64(c.scales), u8(c.zero_points),
+                                                   None, c.N, c.K, c.block_size, c.bits),
+                       seconds / 4)
+    res["prefill_gemm"] = {"tflops": round(2.0 * 4 * c.N * c.K / sec / 1e12, 6),
+                           "sample": "4 of the 2048 rows, every column", "reps": reps}
+    # Conv: the whole problem (one thread: the oracle's conv loop is serial).
+    c = make_conv_case()
+    sec, reps = _timed(lambda: oracle.conv_int8(c.X.numpy(), c.W.numpy(), c.bias.numpy(),
+                                                c.w_scale.numpy(), c.in_scale, c.out_scale,
+                                                c.in_zp, c.out_zp, c.clamp_min, c.clamp_max,
+                                                c.stride, c.pad), seconds / 4)
+    res["conv_int8"] = {"us_per_call": round(sec * 1e6, 1),
+                        "int8_tops": round(231211008 / sec / 1e12, 6),
+                        "sample": "the whole problem (serial loop)", "reps": reps}
+    return res
 
 
 if __name__ == "__main__":
