@@ -15,7 +15,9 @@ Every function cites the passage of the web pages it follows:
   ``quantize_activation_signed`` and the CompInt8 block dot of
   ``int4_dot_row_scalar`` / ``int8_row``.
 * "rlx-cpu quant.rs" -- ``exec_q_mat_mul`` (int32 accumulate, requantize,
-  clamp) and the ``QConv2d`` attribute set.
+  clamp), the ``QConv2d`` attribute set, ``dequant_matmul_nvfp4`` and the
+  low-precision scaled-GEMM reference (``lowp_dequantize``,
+  ``lowp_scaled_matmul``) for block-scaled FP4 weights.
 * "MNN ConvInt8TiledExecutor.cpp" -- zero-point padding of the im2col and the
   clamp defaults.
 
@@ -69,6 +71,11 @@ def _load():
             "oracle_dequantize": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
             "oracle_matmul_nbits": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
             "oracle_check_g_idx": [vp, i64, i64, i64],
+            "oracle_fp4_dequantize": [vp, vp, i32, ctypes.c_double, i64, i64, vp],
+            "oracle_fp4_matmul": [vp, vp, vp, i32, ctypes.c_double, vp, i64, i64, i64, vp, vp],
+            "oracle_e2m1": [ctypes.c_uint],
+            "oracle_e8m0": [ctypes.c_uint],
+            "oracle_e4m3": [ctypes.c_uint],
             "oracle_quantize_a": [vp, i64, i64, i64, vp, vp],
             "oracle_compint8_block_dots": [vp, vp, vp, i64, i64, i64, i64, i32, vp],
             "oracle_compint8_matmul": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
@@ -80,6 +87,8 @@ def _load():
             fn.argtypes = argtypes
             fn.restype = None
         _lib.oracle_check_g_idx.restype = i64
+        for name in ("oracle_e2m1", "oracle_e8m0", "oracle_e4m3"):
+            getattr(_lib, name).restype = ctypes.c_double
     return _lib
 
 
@@ -237,6 +246,51 @@ def compint8_matmul(qa, sa, B, scales, zp, bias, N, K, block_size, bits):
                                    _ptr(_c(scales, np.float64)), _ptr(_c(zp, np.uint8)),
                                    _ptr(_c(bias, np.float64)), M, N, K, block_size, bits,
                                    _ptr(Y), _ptr(S))
+    return Y, S
+
+
+# -- Block-scaled FP4 weights ([RLX] dequant_matmul_nvfp4, lowp_*) ------------
+
+FP4_FORMATS = {"mxfp4": 0, "nvfp4": 1}
+FP4_BLOCK = {"mxfp4": 32, "nvfp4": 16}
+
+
+def e2m1(code):
+    """Value of an FP4 E2M1 code (OCP Microscaling element format)."""
+    return _load().oracle_e2m1(int(code))
+
+
+def e8m0(byte):
+    """Value of an E8M0 scale byte: 2^(e - 127), nan for 255."""
+    return _load().oracle_e8m0(int(byte))
+
+
+def e4m3(byte):
+    """Value of an FP8 E4M3 byte (bias 7, subnormals, nan = S.1111.111)."""
+    return _load().oracle_e4m3(int(byte))
+
+
+def fp4_dequantize(W, scales, fmt, global_scale, N, K):
+    """Dense float64 ``[N, K]`` weight e2m1(code) * scale * global_scale."""
+    W = _c(W, np.uint8)
+    s = _c(scales, np.uint8)
+    out = np.empty((N, K), np.float64)
+    _load().oracle_fp4_dequantize(_ptr(W), _ptr(s), FP4_FORMATS[fmt], float(global_scale), N, K,
+                                  _ptr(out))
+    return out
+
+
+def fp4_matmul(A, W, scales, fmt, global_scale, bias, N, K):
+    """Y = A @ W_fp4^T (+ bias) in float64 and the tolerance base S, for
+    ``fmt`` "mxfp4" (E8M0 scales per 32) or "nvfp4" (E4M3 per 16, times
+    ``global_scale``)."""
+    A = _c(np.atleast_2d(A), np.float64)
+    M = A.shape[0]
+    Y = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _load().oracle_fp4_matmul(_ptr(A), _ptr(_c(W, np.uint8)), _ptr(_c(scales, np.uint8)),
+                              FP4_FORMATS[fmt], float(global_scale), _ptr(_c(bias, np.float64)),
+                              M, N, K, _ptr(Y), _ptr(S))
     return Y, S
 
 

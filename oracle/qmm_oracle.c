@@ -299,6 +299,91 @@ EXPORT void oracle_compint8_matmul(const int8_t *qa, const float *sa,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block-scaled FP4 weights ([RLX] dequant_matmul_nvfp4 and the low-precision */
+/* scaled-GEMM reference lowp_scaled_matmul / lowp_dequantize).  Each weight  */
+/* is an FP4 E2M1 code times its block's scale, blocks of bs elements along   */
+/* K: MXFP4 = E8M0 scale per 32, NVFP4 = E4M3 scale per 16 and one f32 global */
+/* scale.  The element formats are decoded from their published definitions  */
+/* (OCP Microscaling formats; the NVFP4 scale is OCP FP8 E4M3):              */
+/*   E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is the  */
+/*         subnormal m * 0.5, else 2^(e-1) * (1 + m/2); no inf or nan.        */
+/*   E8M0: 2^(e - 127); e = 255 is nan.                                        */
+/*   E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is the */
+/*         subnormal m/8 * 2^-6; S.1111.111 is nan; no inf.                   */
+/* Layout (reading): weights [N, ceil(K/bs), bs/2] bytes, element k of row n  */
+/* in byte k/2 of the row, the low nibble for even k (the nibble order of     */
+/* [RLX] dequant_matmul_nvfp4, rows K-last as the rhs of lowp_scaled_matmul); */
+/* scales [N, ceil(K/bs)] bytes.                                              */
+/* ------------------------------------------------------------------------ */
+EXPORT double oracle_e2m1(unsigned code) {
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+EXPORT double oracle_e8m0(unsigned byte) {
+    if ((byte & 0xFF) == 0xFF) return NAN;
+    return ldexp(1.0, (int)(byte & 0xFF) - 127);
+}
+
+EXPORT double oracle_e4m3(unsigned byte) {
+    int sign = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp(m / 8.0, -6);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* fmt 0: MXFP4 (bs 32, E8M0 scales); fmt 1: NVFP4 (bs 16, E4M3 scales).   */
+static int fp4_block(int fmt) { return fmt == 0 ? 32 : 16; }
+
+static double fp4_weight(const uint8_t *W, const uint8_t *scales, int fmt,
+                         double global_scale, int64_t n, int64_t k, int64_t K) {
+    int64_t bs = fp4_block(fmt);
+    int64_t kb = n_blocks(K, bs);
+    unsigned byte = W[n * kb * (bs / 2) + k / 2];
+    unsigned code = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    uint8_t sb = scales[n * kb + k / bs];
+    double s = fmt == 0 ? oracle_e8m0(sb) : oracle_e4m3(sb);
+    return oracle_e2m1(code) * s * global_scale;
+}
+
+/* Dense weight [N, K] in double. */
+EXPORT void oracle_fp4_dequantize(const uint8_t *W, const uint8_t *scales, int fmt,
+                                  double global_scale, int64_t N, int64_t K,
+                                  double *out) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = fp4_weight(W, scales, fmt, global_scale, n, k, K);
+}
+
+/* Y[m, n] = sum_k A[m, k] * w(n, k) (+ bias[n]) in double; S as for O2. */
+EXPORT void oracle_fp4_matmul(const double *A, const uint8_t *W,
+                              const uint8_t *scales, int fmt, double global_scale,
+                              const double *bias, int64_t M, int64_t N, int64_t K,
+                              double *Y, double *S) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double t = A[m * K + k] *
+                           fp4_weight(W, scales, fmt, global_scale, n, k, K);
+                acc += t;
+                mag += fabs(t);
+            }
+            if (bias) {
+                acc += bias[n];
+                mag += fabs(bias[n]);
+            }
+            Y[m * N + n] = acc;
+            if (S) S[m * N + n] = mag;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O5 int8 convolution with requantization.                                   */
 /* acc = bias[oc] + sum over taps and input channels of                       */
 /*       (x - in_zp) * w, an out-of-bounds tap reading x = in_zp             */
