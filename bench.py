@@ -67,7 +67,7 @@ def parse():
                         "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
-    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny"], default=None,
+    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4"], default=None,
                    help="time only this workload and print its object (profiling runs)")
     p.add_argument("--read-sweep", action="store_true",
                    help="only sweep the plain streaming read (bench_probe/) over launch shapes "
@@ -107,7 +107,7 @@ def main():
             torch.cuda.synchronize()
             del src, dst
         fn = {"compint8": bench_compint8, "prefill": bench_prefill, "conv": bench_conv,
-              "tiny": bench_tiny}[args.only]
+              "tiny": bench_tiny, "fp4": bench_fp4}[args.only]
         print(json.dumps({args.only: fn(qmm, dev, stream, args)}), flush=True)
         return
     if args.copy_calibration:
@@ -348,6 +348,7 @@ def main():
     out["prefill_gemm"] = bench_prefill(qmm, dev, stream, args)
     out["compint8"] = bench_compint8(qmm, dev, stream, args)
     out["conv_int8"] = bench_conv(qmm, dev, stream, args)
+    out["fp4"] = bench_fp4(qmm, dev, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
@@ -616,6 +617,50 @@ def bench_compint8(qmm, dev, stream, args):
                                "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
                                "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             res[f"b{bits}_bs{bs}_M{M}"] = entry
+    return res
+
+
+def bench_fp4(qmm, dev, stream, args):
+    """Block-scaled FP4 weights (MXFP4 / NVFP4), bf16 activations: the decode
+    GEMV on a 4096 x 14336 projection (weights rotating through copies, so
+    they stream from HBM) and the prefill GEMM M=2048 K=4096 N=14336."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
+    res = {}
+    for fmt in ("mxfp4", "nvfp4"):
+        c = make_fp4_case(1, 4096, 14336, fmt, a_dtype="bf16", seed=41).to(dev)
+        nbytes = c.weight_bytes() + c.K * 2 + c.N * 2
+        copies = max(2, -(-POOL_BYTES // nbytes))
+        pool = [(c.W, c.scales)] + [(c.W.clone(), c.scales.clone()) for _ in range(copies - 1)]
+        y = torch.empty(1, c.N, dtype=torch.bfloat16, device=dev)
+
+        def run(i, c=c, pool=pool, y=y):
+            W, S = pool[i % len(pool)]
+            qmm.qmm_gemm_fp4(c.A, W, S, c.fmt, c.global_scale, None, y, 1, c.K, c.N, stream)
+
+        ms = _time_launches(run, max(20, args.steps), stream)
+        del pool
+        p = make_fp4_case(2048, 4096, 14336, fmt, a_dtype="bf16", seed=42).to(dev)
+        Y = torch.empty(p.M, p.N, dtype=torch.bfloat16, device=dev)
+
+        def runp(_, p=p, Y=Y):
+            qmm.qmm_gemm_fp4(p.A, p.W, p.scales, p.fmt, p.global_scale, None, Y, p.M, p.K, p.N,
+                             stream)
+
+        for i in range(3):
+            runp(i)
+        torch.cuda.synchronize()
+        msp = _time_launches(runp, max(5, args.steps // 20), stream)
+        flop = 2.0 * p.M * p.N * p.K
+        res[fmt] = {
+            "gemv_K4096_N14336": {"us": round(ms * 1e3, 3), "bytes": nbytes,
+                                  "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "prefill_M2048_K4096_N14336": {"ms": round(msp, 4),
+                                           "tflops": round(flop / (msp * 1e-3) / 1e12, 2),
+                                           "frac_bf16_peak": round(
+                                               flop / (msp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        }
+        del p, Y
     return res
 
 

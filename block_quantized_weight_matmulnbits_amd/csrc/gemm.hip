@@ -140,14 +140,20 @@ constexpr int GEMM_TPB = 64 * GEMM_WAVES;
 // GI: group indices (operator layout only): code k of a column takes the
 // scale and zero point of group g_idx[k] (clamped into 0..kb-1) instead of
 // its block's, looked up per code during the dequantization.
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL, bool GI = false>
+// WF: block-scaled FP4 weights (1 + FP4_MX or 1 + FP4_NV; operator layout,
+// BITS = 4, no zero points): codes are E2M1 values (v_cvt_scalef32_pk_f32_fp4
+// with a unit scale), scales are one E8M0 / E4M3 byte per block, and the
+// result is multiplied by gscale.  Each weight, e2m1 * scale, has at most 6
+// significant bits, so its rounding to the activation dtype is exact.
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL, bool GI = false, int WF = 0>
 __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
     int log2_bs, int log2_blob, int zp_row_bytes, int tiles_m, int chunks,
-    const int32_t* __restrict__ g_idx) {
+    const int32_t* __restrict__ g_idx, float gscale) {
   static_assert(!(GI && TL), "group indices run on the operator layout");
+  static_assert(!WF || (BITS == 4 && !TL && !GI && !HAS_ZP), "FP4 weights: operator layout");
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int BN = 32 * TN;
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   const __amdgpu_buffer_rsrc_t rbc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)B, 0, code_extent, BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)scales, 0, sc_extent * (int)sizeof(ST), BUF_WORD3);
+      (void*)scales, 0, sc_extent * (WF ? 1 : (int)sizeof(ST)), BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
       (void*)zp, 0, HAS_ZP ? zp_extent : 0, BUF_WORD3);
   const __amdgpu_buffer_rsrc_t rgi = __builtin_amdgcn_make_buffer_rsrc(
@@ -220,6 +226,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   u32x4 av[4];                       // A chunks of the next step
   uint32_t cw[2][WPT];               // codes, two steps
   ST scr[2][2];                      // scales of the (at most 2) blocks of 32 codes
+  uint32_t sc8[2][2];                // WF: their scale bytes
   uint32_t zbr[2][2];                // zero-point bytes of those blocks
 
   auto load_a = [&](int k0) {
@@ -268,7 +275,9 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     for (int i = 0; i < 2; ++i) {
       const int b = min(blk0 + i, kb - 1);
       const int si = col_sc0 + b * sc_stride;
-      if constexpr (sizeof(ST) == 4)
+      if constexpr (WF)
+        sc8[st][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, si, 0, 0);
+      else if constexpr (sizeof(ST) == 4)
         scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, si * 4, 0, 0));
       else
         scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, si * 2, 0, 0));
@@ -340,6 +349,11 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     float sf[2], zs[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if constexpr (WF) {
+        sf[i] = fp4_scale(sc8[st][i], WF - 1);
+        zs[i] = 0.0f;
+        continue;
+      }
       sf[i] = dt<SDT>::to_f32(scr[st][i]);
       uint32_t z = 1u << (BITS - 1);
       if constexpr (HAS_ZP) {
@@ -354,7 +368,18 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     // exact and so is the difference; one rounding to the activation dtype.
     auto dequant_word = [&](int w, float s, float z) {
       float q[P];
-      word_codes_f32<BITS>(cw[st][w], q);
+      if constexpr (WF) {
+        // Byte j of the word: E2M1 values of codes 2j (low nibble), 2j + 1.
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[st][w], 1.0f, 0);
+        const f2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[st][w], 1.0f, 1);
+        const f2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[st][w], 1.0f, 2);
+        const f2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[st][w], 1.0f, 3);
+        q[0] = c0.x; q[1] = c0.y; q[2] = c1.x; q[3] = c1.y;
+        q[4] = c2.x; q[5] = c2.y; q[6] = c3.x; q[7] = c3.y;
+      } else {
+        word_codes_f32<BITS>(cw[st][w], q);
+      }
 #pragma unroll
       for (int j = 0; j < P; j += 2) pk[(w * P + j) / 2] = Op::pack(fmaf(q[j], s, -z), fmaf(q[j + 1], s, -z));
     };
@@ -462,7 +487,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm + i * 16 + rr + e;
-        if (m < M) Y[(int64_t)m * N + n] = Op::round(acc[i][j][e] + bv);
+        if (m < M) Y[(int64_t)m * N + n] = Op::round((WF ? acc[i][j][e] * gscale : acc[i][j][e]) + bv);
       }
     }
   }
@@ -624,7 +649,7 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
                          (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
                          (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
                          (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), (int)a.zp_row_bytes,
-                         tiles_m, (int)a.chunks, (const int32_t*)nullptr);
+                         tiles_m, (int)a.chunks, (const int32_t*)nullptr, 1.0f);
       return hipGetLastError();
     }
   }
@@ -667,7 +692,7 @@ static hipError_t launch_gidx_t(const MatArgs& a) {
                      (const uint16_t*)a.A, a.B, (const ST*)a.scales, a.zp,
                      (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
                      (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), (int)a.zp_row_bytes,
-                     tiles_m, (int)a.chunks, a.g_idx);
+                     tiles_m, (int)a.chunks, a.g_idx, 1.0f);
   return hipGetLastError();
 }
 
@@ -690,6 +715,44 @@ static hipError_t launch_gidx_x(const MatArgs& a) {
 }
 
 bool gemm_mfma_gidx_supported(const MatArgs& a) { return !a.tiled && mfma_fits(a); }
+
+// FP4 weights on the matrix cores: the 4-bit operator-layout geometry with
+// blocks of 32 (MXFP4) or 16 (NVFP4) and one scale byte per block.
+static MatArgs fp4_as_mat(const Fp4Args& f) {
+  MatArgs a;
+  a.A = f.A; a.B = f.W; a.scales = f.scales; a.bias = f.bias; a.Y = f.Y;
+  a.M = f.M; a.K = f.K; a.N = f.N; a.kb = f.kb;
+  a.block_size = f.format == FP4_MX ? 32 : 16;
+  a.blob = a.block_size / 2;
+  a.bits = 4; a.a_dtype = f.a_dtype; a.s_dtype = DT_F32;   // 4-byte bound in mfma_fits
+  a.stream = f.stream;
+  return a;
+}
+
+bool gemm_mfma_fp4_supported(const Fp4Args& f) { return mfma_fits(fp4_as_mat(f)); }
+
+template <int XDT, int WF>
+static hipError_t launch_fp4_mfma_t(const Fp4Args& f) {
+  const MatArgs a = fp4_as_mat(f);
+  const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
+  constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);
+  auto kern = gemm_mfma_kernel<4, XDT, DT_BF16, false, 8, false, false, WF>;
+  const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
+                     (const uint16_t*)a.A, a.B, (const uint16_t*)a.scales, (const uint8_t*)nullptr,
+                     (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M, (int)a.K, (int)a.N,
+                     (int)a.kb, ilog2i(a.block_size), ilog2i(a.blob), 0, tiles_m, 0,
+                     (const int32_t*)nullptr, f.global_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma_fp4(const Fp4Args& f) {
+  const bool f16 = f.a_dtype == DT_F16;
+  if (f.format == FP4_MX)
+    return f16 ? launch_fp4_mfma_t<DT_F16, 1 + FP4_MX>(f) : launch_fp4_mfma_t<DT_BF16, 1 + FP4_MX>(f);
+  return f16 ? launch_fp4_mfma_t<DT_F16, 1 + FP4_NV>(f) : launch_fp4_mfma_t<DT_BF16, 1 + FP4_NV>(f);
+}
 
 hipError_t launch_gemm_mfma_gidx(const MatArgs& a) {
   switch (a.bits) {

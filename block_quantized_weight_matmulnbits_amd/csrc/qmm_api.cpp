@@ -340,6 +340,42 @@ int qmm_check_g_idx(const int32_t* g_idx, int64_t g_idx_len, int64_t K, int bloc
   return QMM_OK;
 }
 
+int qmm_gemm_fp4(const void* A, int a_dtype, const uint8_t* W, const uint8_t* scales,
+                 int format, float global_scale, const void* bias, void* Y, int64_t M,
+                 int64_t K, int64_t N, void* stream) {
+  const char* fn = "qmm_gemm_fp4";
+  if (format != QMM_MXFP4 && format != QMM_NVFP4)
+    return fail(QMM_ERR_INVALID_ARG, "%s: format=%d is not a qmm_fp4_format. How to fix: pass "
+                "QMM_MXFP4 (E8M0 scales per 32) or QMM_NVFP4 (E4M3 scales per 16).", fn, format);
+  if (K <= 0 || N <= 0 || M < 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: K and N must be positive and M >= 0 (got M=%lld "
+                "K=%lld N=%lld).", fn, (long long)M, (long long)K, (long long)N);
+  if (dtype_size(a_dtype) == 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: a_dtype=%d is not a qmm_dtype. How to fix: pass "
+                "QMM_F32, QMM_F16 or QMM_BF16.", fn, a_dtype);
+  if (W == nullptr || scales == nullptr || (M > 0 && (A == nullptr || Y == nullptr)))
+    return fail(QMM_ERR_INVALID_ARG, "%s: A, W, scales and Y must be non-null device "
+                "pointers (bias may be NULL).", fn);
+  if (!aligned(W, 16))
+    return fail(QMM_ERR_INVALID_ARG, "%s: W must be 16-byte aligned. Why: the kernels read "
+                "codes with 128-bit loads. How to fix: pass a freshly allocated tensor.", fn);
+  const int asz = dtype_size(a_dtype);
+  if (!aligned(A, asz) || !aligned(Y, asz) || !aligned(bias, asz))
+    return fail(QMM_ERR_INVALID_ARG, "%s: A, Y and bias must be aligned to their element size.",
+                fn);
+  const int64_t bs = format == QMM_MXFP4 ? 32 : 16;
+  const int64_t kb = (K + bs - 1) / bs;
+  if (N * kb * bs / 2 + 64 > INT32_MAX / 2 || M * K > INT32_MAX / 2 || K > INT32_MAX / 4)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: the weight or activations are too large for 32-bit "
+                "offsets. How to fix: split the matmul along N or M.", fn);
+  if (M == 0) return QMM_OK;
+  qmm::Fp4Args a;
+  a.A = A; a.W = W; a.scales = scales; a.global_scale = global_scale; a.bias = bias; a.Y = Y;
+  a.M = M; a.K = K; a.N = N; a.kb = kb; a.format = format; a.a_dtype = a_dtype;
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_fp4(a), fn);
+}
+
 int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,
                float in_scale, float out_scale, int in_zp, int out_zp, int clamp_min,
                int clamp_max, int Nb, int H, int W, int C, int Co, int KH, int KW, int stride_h,

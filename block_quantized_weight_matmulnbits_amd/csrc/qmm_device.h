@@ -114,4 +114,26 @@ __device__ __forceinline__ uint32_t load_zp(const uint8_t* __restrict__ zrow, in
   }
 }
 
+// Block-scaled FP4 weight formats: MXFP4 (E8M0 scale per 32) and NVFP4
+// (E4M3 scale per 16, with a global scale).
+enum : int { FP4_MX = 0, FP4_NV = 1 };
+
+// A decoded FP4 block scale, exact in fp32 (nan stays nan): E8M0 is
+// 2^(e - 127) (255 = nan; 0 = 2^-127, an fp32 subnormal); E4M3 has bias 7,
+// subnormals m/8 * 2^-6 and nan S.1111.111.
+__device__ __forceinline__ float fp4_scale(uint32_t byte, int fmt) {
+  byte &= 0xFFu;
+  if (fmt == FP4_MX) {
+    if (byte == 0xFFu) return __uint_as_float(0x7FC00000u);
+    if (byte == 0u) return __uint_as_float(0x00400000u);
+    return __uint_as_float(byte << 23);
+  }
+  const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
+  float v;
+  if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
+  else if (e == 0u) v = (float)m * 0x1p-9f;
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));   // 2^(e-7) * (1 + m/8)
+  return (byte & 0x80u) ? -v : v;
+}
+
 }  // namespace qmm

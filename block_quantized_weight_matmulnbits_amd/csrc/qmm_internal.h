@@ -65,6 +65,24 @@ hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float
 hipError_t launch_compint8_tiled_dots(const MatArgs& a, const int8_t* qa, const float* sa,
                                       int32_t* dots);
 
+// Block-scaled FP4 weights (fp4.hip): a validated problem.
+struct Fp4Args {
+  const void* A = nullptr;        // [M, K] a_dtype
+  const uint8_t* W = nullptr;     // [N, kb, bs/2] E2M1 codes
+  const uint8_t* scales = nullptr;  // [N, kb] E8M0 (MXFP4) or E4M3 (NVFP4) bytes
+  float global_scale = 1.0f;
+  const void* bias = nullptr;     // [N] a_dtype or null
+  void* Y = nullptr;              // [M, N] a_dtype
+  int64_t M = 1, K = 0, N = 0, kb = 0;
+  int format = 0;                 // 0 = MXFP4, 1 = NVFP4
+  int a_dtype = 0;
+  hipStream_t stream = nullptr;
+};
+hipError_t launch_fp4(const Fp4Args& a);
+// The matrix-core GEMM on FP4 weights (gemm.hip): 16-bit activations, M > 16.
+bool gemm_mfma_fp4_supported(const Fp4Args& a);
+hipError_t launch_gemm_mfma_fp4(const Fp4Args& a);
+
 // int8 convolution (validated NHWC / OHWI problem).
 struct ConvArgs {
   const int8_t* X = nullptr;

@@ -42,6 +42,7 @@ _SIGS = {
                            _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
                                    _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "qmm_gemm_fp4": ([_vp, _i32, _vp, _vp, _i32, _f32, _vp, _vp, _i64, _i64, _i64, _vp], _i32),
     "qmm_step_create": ([_vp], _i32),
     "qmm_step_add_gemv": ([_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64,
                            _i32, _i32, _i32], _i32),
@@ -218,6 +219,17 @@ def qmm_gemm_compint8_noalloc(A, B, scales, zero_points, bias, Y, M, K, N, block
     _check(lib.qmm_gemm_compint8_noalloc(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points),
                                          gp, gn, _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
                                          accuracy_level, _stream(stream)))
+
+
+QMM_MXFP4, QMM_NVFP4 = 0, 1
+FP4_FORMAT = {"mxfp4": QMM_MXFP4, "nvfp4": QMM_NVFP4}
+
+
+def qmm_gemm_fp4(A, W, scales, fmt, global_scale, bias, Y, M, K, N, stream=None):
+    """Block-scaled FP4 weights; ``fmt`` is "mxfp4" / "nvfp4" or the enum."""
+    f = FP4_FORMAT.get(fmt, fmt)
+    _check(lib.qmm_gemm_fp4(_ptr(A), _dt(A), _ptr(W), _ptr(scales), f, float(global_scale),
+                            _ptr(bias), _ptr(Y), M, K, N, _stream(stream)))
 
 
 class Step:

@@ -176,6 +176,54 @@ def prefill_gemm(seed: int = 4, M: int = 2048, K: int = 4096, N: int = 14336) ->
 
 
 @dataclass
+class Fp4Case:
+    """Block-scaled FP4 weights (MXFP4 / NVFP4) with float activations."""
+    M: int
+    K: int
+    N: int
+    fmt: str                        # "mxfp4" (E8M0 / 32) or "nvfp4" (E4M3 / 16)
+    A: torch.Tensor                 # [M, K] a_dtype
+    W: torch.Tensor                 # [N, kb, bs/2] uint8 E2M1 codes
+    scales: torch.Tensor            # [N, kb] uint8 scale bytes
+    global_scale: float
+    bias: torch.Tensor | None
+
+    @property
+    def block_size(self) -> int:
+        return 32 if self.fmt == "mxfp4" else 16
+
+    def weight_bytes(self) -> int:
+        return self.W.numel() + self.scales.numel()
+
+    def to(self, device) -> "Fp4Case":
+        mv = lambda t: None if t is None else t.to(device)
+        return Fp4Case(self.M, self.K, self.N, self.fmt, mv(self.A), mv(self.W),
+                       mv(self.scales), self.global_scale, mv(self.bias))
+
+
+def make_fp4_case(M: int, K: int, N: int, fmt: str, *, a_dtype: str = "bf16",
+                  has_bias: bool = False, seed: int = 0) -> Fp4Case:
+    """Random block-scaled FP4 inputs: activations N(0,1), codes uniform random
+    bytes (every nibble uniform over the 16 E2M1 codes), scale bytes uniform
+    over a range of ordinary magnitudes -- E8M0 118..125 (2^-9 .. 2^-2) for
+    MXFP4; E4M3 0x18..0x37 (2^-4 .. 2^-1 * 1.875) and a global scale 0.25 for
+    NVFP4 -- so that weights are of the size of the integer workloads'."""
+    rng = np.random.default_rng(seed)
+    bs = 32 if fmt == "mxfp4" else 16
+    kb = n_blocks(K, bs)
+    A = _half(rng.standard_normal((M, K), dtype=np.float32), a_dtype)
+    W = torch.from_numpy(rng.integers(0, 256, size=(N, kb, bs // 2), dtype=np.uint8))
+    if fmt == "mxfp4":
+        sc = rng.integers(118, 126, size=(N, kb), dtype=np.uint8)
+        g = 1.0
+    else:
+        sc = rng.integers(0x18, 0x38, size=(N, kb), dtype=np.uint8)
+        g = 0.25
+    bias = _half(rng.standard_normal(N, dtype=np.float32), a_dtype) if has_bias else None
+    return Fp4Case(M, K, N, fmt, A, W, torch.from_numpy(sc), g, bias)
+
+
+@dataclass
 class ConvCase:
     X: torch.Tensor         # NHWC int8
     W: torch.Tensor         # OHWI int8

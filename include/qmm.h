@@ -178,6 +178,34 @@ int qmm_gemm_compint8_noalloc(const void *A, int a_dtype, const uint8_t *B,
                               int bits, int accuracy_level, void *stream);
 
 /*
+ * Matmul with block-scaled FP4 weights (rlx-cpu quant.rs: dequant_matmul_nvfp4,
+ * lowp_dequantize):
+ *   w(n, k) = e2m1(code(n, k)) * scale(n, k / bs) * global_scale
+ *   Y[m, n] = sum_k A[m, k] * w(n, k)  (+ bias[n]),  fp32 accumulate
+ * QMM_MXFP4: bs = 32, scales are E8M0 bytes (2^(e-127); 255 is nan).
+ * QMM_NVFP4: bs = 16, scales are FP8 E4M3 bytes (bias 7; S.1111.111 is nan).
+ * E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit) codes 0..15 are
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives.
+ *   A      [M, K]          a_dtype (f32, f16, bf16)
+ *   W      [N, kb, bs/2]   uint8, kb = ceil(K / bs), 16-byte aligned: element
+ *                          k of row n in byte k/2 of the row, low nibble for
+ *                          even k (rows are K-last; the page's dequantizer
+ *                          flattens a [K, N] index the same way)
+ *   scales [N, kb]         uint8 scale bytes
+ *   global_scale           multiplies every weight (NVFP4's per-tensor f32
+ *                          scale; MXFP4 weights pass 1)
+ *   bias [N], Y [M, N]     a_dtype (bias may be NULL)
+ * M = 1 runs a GEMV; 16-bit activations with M > 16 the matrix cores (each
+ * weight is exact in bf16 / f16); the rest an fp32 kernel.  M = 0 is a no-op.
+ */
+typedef enum qmm_fp4_format { QMM_MXFP4 = 0, QMM_NVFP4 = 1 } qmm_fp4_format;
+
+int qmm_gemm_fp4(const void *A, int a_dtype, const uint8_t *W,
+                 const uint8_t *scales, int format, float global_scale,
+                 const void *bias, void *Y, int64_t M, int64_t K, int64_t N,
+                 void *stream);
+
+/*
  * A step: a fixed sequence of matmul calls (say the projections of one
  * decode step) recorded once and replayed as one HIP graph.  The pages find
  * the decode step's cost outside the kernels -- per-operator dispatch and

@@ -1,0 +1,155 @@
+"""GPU parity of block-scaled FP4 weights (qmm_gemm_fp4) against the oracle.
+
+rlx-cpu quant.rs (dequant_matmul_nvfp4, lowp_dequantize): w = e2m1(code) *
+block scale (* global scale).  MXFP4 (E8M0 per 32) and NVFP4 (E4M3 per 16),
+f32 / bf16 / f16 activations, M = 1 (the GEMV), small M (fp32 rows) and
+M > 16 (matrix cores for 16-bit activations), ragged K and N.  Exact data
+(small-integer activations, power-of-two scales) must equal the oracle's
+value rounded once to the output dtype; random data is within tol * S
+(strictly on a decode-size projection).  Every E2M1 code and every scale
+byte class (normal, subnormal, zero, nan) is exercised.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.util import TOL, assert_within, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def qmm():
+    from block_quantized_weight_matmulnbits_amd import qmm as q
+    return q
+
+
+def run(case):
+    c = case.to(DEV)
+    Y = torch.empty(case.M, case.N, dtype=c.A.dtype, device=DEV)
+    qmm().qmm_gemm_fp4(c.A, c.W, c.scales, case.fmt, case.global_scale, c.bias, Y, case.M,
+                       case.K, case.N)
+    torch.cuda.synchronize()
+    return Y
+
+
+def oracle_y(case):
+    return oracle.fp4_matmul(f64(case.A).reshape(case.M, case.K), case.W.numpy(),
+                             case.scales.numpy(), case.fmt, case.global_scale, f64(case.bias),
+                             case.N, case.K)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("a_dtype", ["bf16", "f16", "f32"])
+def test_random_data_within_tolerance(fmt, a_dtype):
+    from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
+    for i, (M, K, N) in enumerate([(1, 32, 1), (1, 1000, 129), (1, 8200, 70), (3, 520, 33),
+                                   (17, 1024, 300), (64, 4096, 520)]):
+        case = make_fp4_case(M, K, N, fmt, a_dtype=a_dtype, has_bias=(i % 2 == 1),
+                             seed=4000 + 10 * i + (fmt == "nvfp4"))
+        print(f"[fp4] {fmt} M={M} K={K} N={N} a={a_dtype}", flush=True)
+        Y, S = oracle_y(case)
+        r = assert_within(run(case), Y, S, TOL[case.A.dtype], f"fp4 {fmt}")
+        print(f"  max |err|/S = {r:.3e}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("a_dtype", ["bf16", "f16", "f32"])
+def test_exact_data_bit_for_bit(fmt, a_dtype):
+    """Activations in {-3..3}, power-of-two scales, global scale 1 or 0.5:
+    every product and partial sum is exact, so the result is the oracle's
+    value rounded once."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
+    rng = np.random.default_rng(7)
+    for i, (M, K, N) in enumerate([(1, 256, 40), (5, 300, 17), (40, 512, 300)]):
+        case = make_fp4_case(M, K, N, fmt, a_dtype=a_dtype, has_bias=True, seed=i)
+        case.A = torch.from_numpy(rng.integers(-3, 4, (M, K)).astype(np.float32)).to(case.A.dtype)
+        kb = case.scales.shape[1]
+        if fmt == "mxfp4":
+            case.scales = torch.from_numpy(rng.integers(124, 128, (N, kb)).astype(np.uint8))
+        else:
+            # E4M3 powers of two 2^-3 .. 2^0 (mantissa 0).
+            case.scales = torch.from_numpy((rng.integers(4, 8, (N, kb)) << 3).astype(np.uint8))
+            case.global_scale = 0.5
+        case.bias = torch.from_numpy(rng.integers(-8, 9, N).astype(np.float32)).to(case.A.dtype)
+        print(f"[fp4 exact] {fmt} M={M} K={K} N={N} a={a_dtype}", flush=True)
+        Y, _ = oracle_y(case)
+        y = run(case)
+        assert torch.equal(y.cpu(), torch.from_numpy(Y).to(case.A.dtype)), (M, K, N)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_every_code_and_scale_class(fmt):
+    """Each of the 16 E2M1 codes alone in a row (all other codes 0), under
+    normal, subnormal and zero scales, on the GEMV and the matrix cores."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
+    bs = 32 if fmt == "mxfp4" else 16
+    for M in (1, 20):
+        case = make_fp4_case(M, 64, 48, fmt, a_dtype="bf16", seed=11)
+        case.A = torch.ones(M, 64, dtype=torch.bfloat16)
+        W = np.zeros((48, 64 // bs, bs // 2), np.uint8)
+        for n in range(48):
+            code = n % 16
+            k = (n * 5) % 64
+            W[n].reshape(-1)[k // 2] = code if k % 2 == 0 else code << 4
+        case.W = torch.from_numpy(W)
+        sc = np.full((48, 64 // bs), 127 if fmt == "mxfp4" else 0x38, np.uint8)
+        if fmt == "mxfp4":
+            sc[16:32] = 27       # 2^-100
+            sc[32:40] = 200      # 2^73
+        else:
+            sc[16:32] = 0x01     # smallest subnormal 2^-9
+            sc[32:40] = 0x00     # zero
+            sc[40:48] = 0xB8     # -1.0
+        case.scales = torch.from_numpy(sc)
+        case.global_scale = 1.0
+        Y, S = oracle_y(case)
+        y = run(case)
+        assert_within(y, Y, S, TOL[torch.bfloat16], f"codes {fmt} M={M}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_nan_scale_gives_nan_row(fmt):
+    from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
+    for M in (1, 20):
+        case = make_fp4_case(M, 128, 64, fmt, a_dtype="bf16", seed=3)
+        sc = case.scales.numpy().copy()
+        sc[5, 1] = 0xFF if fmt == "mxfp4" else 0x7F
+        case.scales = torch.from_numpy(sc)
+        y = run(case).float().cpu()
+        assert torch.isnan(y[:, 5]).all() and not torch.isnan(y[:, 4]).any()
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_decode_and_prefill_shapes(fmt):
+    """A 4096 x 14336 decode projection (every output, strict tol * S) and a
+    prefill slice M = 256 (sampled rows)."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
+    case = make_fp4_case(1, 4096, 14336, fmt, a_dtype="bf16", seed=31)
+    print(f"[fp4 full] {fmt} decode", flush=True)
+    Y, S = oracle_y(case)
+    r = assert_within(run(case), Y, S, TOL[torch.bfloat16], f"fp4 decode {fmt}", strict=True)
+    print(f"  max |err|/S = {r:.3e}")
+    case = make_fp4_case(256, 4096, 4096, fmt, a_dtype="bf16", seed=32)
+    y = run(case).cpu()
+    rows = [0, 77, 255]
+    sub = case.A[rows]
+    Y, S = oracle.fp4_matmul(f64(sub), case.W.numpy(), case.scales.numpy(), fmt,
+                             case.global_scale, None, case.N, case.K)
+    assert_within(y[rows], Y, S, TOL[torch.bfloat16], f"fp4 prefill {fmt}", strict=True)
+
+
+def test_rejects_bad_arguments():
+    q = qmm()
+    x = torch.zeros(1, 64, dtype=torch.bfloat16, device=DEV)
+    W = torch.zeros(8, 2, 16, dtype=torch.uint8, device=DEV)
+    s = torch.zeros(8, 2, dtype=torch.uint8, device=DEV)
+    y = torch.empty(1, 8, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_gemm_fp4(x, W, s, 7, 1.0, None, y, 1, 64, 8)
+    assert e.value.status == q.QMM_ERR_INVALID_ARG
+    Wb = torch.zeros(8 * 2 * 16 + 8, dtype=torch.uint8, device=DEV)[8:]
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_gemm_fp4(x, Wb, s, "mxfp4", 1.0, None, y, 1, 64, 8)
+    assert "16-byte aligned" in str(e.value)
