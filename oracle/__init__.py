@@ -71,6 +71,8 @@ def _load():
             "oracle_dequantize": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
             "oracle_matmul_nbits": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
             "oracle_check_g_idx": [vp, i64, i64, i64],
+            "oracle_quantize_a16": [vp, i64, i64, i64, vp, vp],
+            "oracle_int16_matmul": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
             "oracle_fp4_dequantize": [vp, vp, i32, ctypes.c_double, i64, i64, vp],
             "oracle_fp4_matmul": [vp, vp, vp, i32, ctypes.c_double, vp, i64, i64, i64, vp, vp],
             "oracle_e2m1": [ctypes.c_uint],
@@ -222,6 +224,33 @@ def quantize_a(A, K, block_size):
     sa = np.empty((M, kb), np.float32)
     _load().oracle_quantize_a(_ptr(A), M, K, block_size, _ptr(qa), _ptr(sa))
     return qa, sa
+
+
+def quantize_a16(A, K, block_size):
+    """Per-row, per-block symmetric int16 quantization (the int16-activation
+    route of MatMulNBits ``execute``): ``qa`` ``[M, kb*bs]`` int16 (zero past
+    K), ``sa`` ``[M, kb]`` float32 = max|x| / 32767."""
+    A = _c(np.atleast_2d(A), np.float32)
+    M = A.shape[0]
+    kb = n_blocks(K, block_size)
+    qa = np.empty((M, kb * block_size), np.int16)
+    sa = np.empty((M, kb), np.float32)
+    _load().oracle_quantize_a16(_ptr(A), M, K, block_size, _ptr(qa), _ptr(sa))
+    return qa, sa
+
+
+def int16_matmul(qa, sa, B, scales, zp, bias, N, K, block_size, bits):
+    """int16-activation output in float64 and its tolerance base ``S``."""
+    qa = _c(qa, np.int16)
+    sa = _c(sa, np.float32)
+    M = qa.shape[0]
+    Y = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _load().oracle_int16_matmul(_ptr(qa), _ptr(sa), _ptr(_c(B, np.uint8)),
+                                _ptr(_c(scales, np.float64)), _ptr(_c(zp, np.uint8)),
+                                _ptr(_c(bias, np.float64)), M, N, K, block_size, bits, _ptr(Y),
+                                _ptr(S))
+    return Y, S
 
 
 def compint8_block_dots(qa, B, zp, N, K, block_size, bits):

@@ -51,13 +51,25 @@ static int64_t zp_row_bytes(int64_t kb, int bits) { return (kb * bits + 7) / 8; 
 
 /* Code of element k of output row n ([ORT] dequantize_nbits_value): inside
  * block k / bs the element sits at bit offset (k % bs) * bits, counted from
- * the least-significant bit of the block's first byte. */
+ * the least-significant bit of the block's first byte.
+ * 3-bit codes ([MNN] weight reorder for 3 bits: the code 0..7 is split into
+ * a 2-bit main plane and a 1-bit aux plane, laid out [main | aux]; offset
+ * -4): a block's blob is bs/4 bytes of the low two bits of each code (four
+ * per byte, LSB first) followed by bs/8 bytes of the high bits (eight per
+ * byte, LSB first); the bit order is the operator's LSB-first one. */
 static unsigned code_at(const uint8_t *B, int64_t n, int64_t k, int64_t K,
                         int64_t bs, int bits) {
     int64_t kb = n_blocks(K, bs);
     int64_t blob = blob_bytes(bs, bits);
     const uint8_t *row = B + n * kb * blob;
     int64_t block = k / bs;
+    if (bits == 3) {
+        const uint8_t *base = row + block * blob;
+        int64_t i = k % bs;
+        unsigned lo = (base[i / 4] >> (2 * (i % 4))) & 3u;
+        unsigned hi = (base[bs / 4 + i / 8] >> (i % 8)) & 1u;
+        return lo | (hi << 2);
+    }
     int64_t bit = (k % bs) * bits;
     unsigned byte = row[block * blob + bit / 8];
     unsigned mask = (1u << bits) - 1u;
@@ -73,7 +85,10 @@ static unsigned zp_at(const uint8_t *zp, int64_t n, int64_t b, int64_t kb,
     const uint8_t *row = zp + n * zp_row_bytes(kb, bits);
     int64_t bit = b * bits;
     unsigned mask = (1u << bits) - 1u;
-    return (row[bit / 8] >> (bit % 8)) & mask;
+    unsigned v = row[bit / 8] >> (bit % 8);
+    /* 3 bits: a value may continue into the next byte (LSB-first stream). */
+    if (bit % 8 + bits > 8) v |= (unsigned)row[bit / 8 + 1] << (8 - bit % 8);
+    return v & mask;
 }
 
 /* codes[n*K + k] for every n < N, k < K. */
@@ -103,6 +118,14 @@ EXPORT void oracle_pack_codes(const uint8_t *codes, int64_t N, int64_t K,
     for (int64_t n = 0; n < N; ++n) {
         uint8_t *row = B + n * kb * blob;
         for (int64_t k = 0; k < K; ++k) {
+            if (bits == 3) {
+                uint8_t *base = row + (k / bs) * blob;
+                int64_t i = k % bs;
+                unsigned c = codes[n * K + k] & mask;
+                base[i / 4] |= (uint8_t)((c & 3u) << (2 * (i % 4)));
+                base[bs / 4 + i / 8] |= (uint8_t)((c >> 2) << (i % 8));
+                continue;
+            }
             int64_t bit = (k % bs) * bits;
             row[(k / bs) * blob + bit / 8] |=
                 (uint8_t)((codes[n * K + k] & mask) << (bit % 8));
@@ -119,7 +142,9 @@ EXPORT void oracle_pack_zero_points(const uint8_t *zps, int64_t N, int64_t kb,
     for (int64_t n = 0; n < N; ++n)
         for (int64_t b = 0; b < kb; ++b) {
             int64_t bit = b * bits;
-            zp[n * rb + bit / 8] |= (uint8_t)((zps[n * kb + b] & mask) << (bit % 8));
+            unsigned v = (zps[n * kb + b] & mask) << (bit % 8);
+            zp[n * rb + bit / 8] |= (uint8_t)(v & 0xFFu);
+            if (v >> 8) zp[n * rb + bit / 8 + 1] |= (uint8_t)(v >> 8);
         }
 }
 
@@ -235,6 +260,75 @@ EXPORT void oracle_quantize_a(const float *A, int64_t M, int64_t K, int64_t bs,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* int16 activations ([ORT] execute, the 8-bit route: the activation is        */
+/* quantized to int16 per K-block and reduced against the u8 weight with an   */
+/* integer dot; the quantizer's body is not on the page).  Reading: the int8   */
+/* quantizer with 32767: sa = max|x| / 32767 (binary32), qa = clamp(rne(x /   */
+/* sa), -32767, 32767), 0 past K and for an all-zero block.                    */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_quantize_a16(const float *A, int64_t M, int64_t K,
+                                int64_t bs, int16_t *qa, float *sa) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t padded = kb * bs;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < kb; ++b) {
+            int64_t k0 = b * bs, k1 = k0 + bs < K ? k0 + bs : K;
+            float amax = 0.0f;
+            for (int64_t k = k0; k < k1; ++k) {
+                float a = fabsf(A[m * K + k]);
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 32767.0f;
+            sa[m * kb + b] = scale;
+            for (int64_t k = k0; k < k0 + bs; ++k) {
+                int16_t v = 0;
+                if (k < K && scale != 0.0f) {
+                    float r = rintf(A[m * K + k] / scale);
+                    if (r > 32767.0f) r = 32767.0f;
+                    if (r < -32767.0f) r = -32767.0f;
+                    v = (int16_t)r;
+                }
+                qa[m * padded + k] = v;
+            }
+        }
+}
+
+/* Y[m, n] = sum_b dot * sa[m, b] * s[n, b] (+ bias), dot = sum over block b */
+/* of qa16 * (code - zp), exact in int64; double accumulation; S as for O4. */
+EXPORT void oracle_int16_matmul(const int16_t *qa, const float *sa,
+                                const uint8_t *B, const double *scales,
+                                const uint8_t *zp, const double *bias,
+                                int64_t M, int64_t N, int64_t K, int64_t bs,
+                                int bits, double *Y, double *S) {
+    int64_t kb = n_blocks(K, bs);
+    int64_t padded = kb * bs;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < kb; ++b) {
+                int64_t z = (int64_t)zp_at(zp, n, b, kb, bits);
+                int64_t dot = 0, adot = 0;
+                for (int64_t k = b * bs; k < (b + 1) * bs && k < K; ++k) {
+                    int64_t t = (int64_t)qa[m * padded + k] *
+                                ((int64_t)code_at(B, n, k, K, bs, bits) - z);
+                    dot += t;
+                    adot += t < 0 ? -t : t;
+                }
+                double f = (double)sa[m * kb + b] * scales[n * kb + b];
+                acc += (double)dot * f;
+                mag += (double)adot * fabs(f);
+            }
+            if (bias) {
+                acc += bias[n];
+                mag += fabs(bias[n]);
+            }
+            Y[m * N + n] = acc;
+            if (S) S[m * N + n] = mag;
+        }
 }
 
 /* ------------------------------------------------------------------------ */
