@@ -1,8 +1,10 @@
 // codec.hip -- device-side codec of the MatMulNBits layout, exported for the
 // bit-exact tests: per element, the code at bit (k % bs) * bits of block k / bs
-// (least-significant bits first), the block's zero point (packed the same way,
-// default 2^(bits-1)) and the dequantized fp32 weight (code - zp) * scale
-// (onnx-runtime-ep-cpu matmul_nbits.rs: dequantize_nbits_value).
+// (least-significant bits first; 3-bit codes in the 2 + 1 bit-plane blob of
+// MNN ConvInt8TiledExecutor.cpp's 3-bit reorder), the block's zero point
+// (packed the same way, default 2^(bits-1)) and the dequantized fp32 weight
+// (code - zp) * scale (onnx-runtime-ep-cpu matmul_nbits.rs:
+// dequantize_nbits_value).
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -21,13 +23,26 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
   const int n = (int)(i / K), k = (int)(i % K);
   const int b = k / bs;
   const uint32_t mask = (bits == 8) ? 0xFFu : ((1u << bits) - 1u);
-  const int bit = (k % bs) * bits;
-  const uint32_t byte = B[((int64_t)n * kb + b) * blob + (bit >> 3)];
-  const uint32_t q = (byte >> (bit & 7)) & mask;
+  const uint8_t* blk = B + ((int64_t)n * kb + b) * blob;
+  uint32_t q;
+  if (bits == 3) {
+    // 2 + 1 bit planes: low two bits at bits 2 (i % 4) of byte i / 4, the
+    // high bit at bit i % 8 of byte bs / 4 + i / 8.
+    const int i = k % bs;
+    q = (((uint32_t)blk[i / 4] >> (2 * (i % 4))) & 3u) |
+        ((((uint32_t)blk[bs / 4 + i / 8] >> (i % 8)) & 1u) << 2);
+  } else {
+    const int bit = (k % bs) * bits;
+    q = ((uint32_t)blk[bit >> 3] >> (bit & 7)) & mask;
+  }
   uint32_t z = 1u << (bits - 1);
   if (zp) {
+    // One LSB-first stream per row; a 3-bit value may cross a byte.
     const int zbit = b * bits;
-    z = ((uint32_t)zp[(int64_t)n * zp_row_bytes + (zbit >> 3)] >> (zbit & 7)) & mask;
+    const uint8_t* zr = zp + (int64_t)n * zp_row_bytes;
+    uint32_t v = (uint32_t)zr[zbit >> 3] >> (zbit & 7);
+    if ((zbit & 7) + bits > 8) v |= (uint32_t)zr[(zbit >> 3) + 1] << (8 - (zbit & 7));
+    z = v & mask;
   }
   if (codes) codes[i] = (uint8_t)q;
   if (zps && k % bs == 0) zps[(int64_t)n * kb + b] = (uint8_t)z;

@@ -35,11 +35,14 @@ constexpr int CI8_LDS_BYTES = 64 * 1024;
 // ---------------------------------------------------------------------------
 // Step 1: activation quantization, one wave per (m, block).
 // ---------------------------------------------------------------------------
-template <int XDT>
+// QT = int8_t: sa = max|x| / 127 (CompInt8); QT = int16_t: sa = max|x| / 32767
+// (the int16-activation route), codes clamped to +-QMAX.
+template <int XDT, typename QT = int8_t>
 __global__ __launch_bounds__(256) void quantize_a_kernel(const typename dt<XDT>::T* __restrict__ A,
-                                                         int8_t* __restrict__ qa,
+                                                         QT* __restrict__ qa,
                                                          float* __restrict__ sa, int M, int K,
                                                          int bs, int kb) {
+  constexpr float QMAX = sizeof(QT) == 1 ? 127.0f : 32767.0f;
   // Blocks of up to QA_REG * 64 activations are read once and kept in
   // registers between the maximum and the quantization (one global round
   // trip); longer blocks read their activations a second time.
@@ -67,12 +70,12 @@ __global__ __launch_bounds__(256) void quantize_a_kernel(const typename dt<XDT>:
   // Wave max (exact: max is order independent).
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float scale = amax / 127.0f;   // IEEE binary32 division
+  const float scale = amax / QMAX;     // IEEE binary32 division
   if (lane == 0) sa[(int64_t)m * kb + b] = scale;
   auto quant = [&](float x) {
     float r = rintf(x / scale);        // IEEE division, ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int8_t)r;
+    r = fminf(fmaxf(r, -QMAX), QMAX);
+    return (QT)r;
   };
   if (in_regs) {
 #pragma unroll
@@ -80,12 +83,12 @@ __global__ __launch_bounds__(256) void quantize_a_kernel(const typename dt<XDT>:
       const int e = lane + 64 * i;
       // Positions past K (the padding of the last block) are zero; so is
       // every position of a block whose scale is 0.
-      if (e < bs) qa[(int64_t)m * padded + k0 + e] = (k0 + e < K && scale != 0.0f) ? quant(xv[i]) : 0;
+      if (e < bs) qa[(int64_t)m * padded + k0 + e] = (k0 + e < K && scale != 0.0f) ? quant(xv[i]) : (QT)0;
     }
   } else {
     for (int e = lane; e < bs; e += 64) {
       const int k = k0 + e;
-      int8_t v = 0;
+      QT v = 0;
       if (k < K && scale != 0.0f) v = quant(dt<XDT>::to_f32(A[(int64_t)m * K + k]));
       qa[(int64_t)m * padded + k] = v;
     }
@@ -328,25 +331,34 @@ static int ilog2(int64_t v) {
   return l;
 }
 
-hipError_t launch_quantize_a(const MatArgs& a, int8_t* qa, float* sa) {
+template <typename QT>
+static hipError_t launch_quantize_t(const MatArgs& a, QT* qa, float* sa) {
   const int blocks = (int)(a.M * a.kb);
   const int grid = (blocks + 3) / 4;
   if (blocks == 0) return hipSuccess;
   switch (a.a_dtype) {
     case DT_F32:
-      hipLaunchKernelGGL((quantize_a_kernel<DT_F32>), dim3(grid), dim3(256), 0, a.stream,
+      hipLaunchKernelGGL((quantize_a_kernel<DT_F32, QT>), dim3(grid), dim3(256), 0, a.stream,
                          (const float*)a.A, qa, sa, (int)a.M, (int)a.K, (int)a.block_size, (int)a.kb);
       break;
     case DT_F16:
-      hipLaunchKernelGGL((quantize_a_kernel<DT_F16>), dim3(grid), dim3(256), 0, a.stream,
+      hipLaunchKernelGGL((quantize_a_kernel<DT_F16, QT>), dim3(grid), dim3(256), 0, a.stream,
                          (const _Float16*)a.A, qa, sa, (int)a.M, (int)a.K, (int)a.block_size, (int)a.kb);
       break;
     default:
-      hipLaunchKernelGGL((quantize_a_kernel<DT_BF16>), dim3(grid), dim3(256), 0, a.stream,
+      hipLaunchKernelGGL((quantize_a_kernel<DT_BF16, QT>), dim3(grid), dim3(256), 0, a.stream,
                          (const uint16_t*)a.A, qa, sa, (int)a.M, (int)a.K, (int)a.block_size, (int)a.kb);
       break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_a(const MatArgs& a, int8_t* qa, float* sa) {
+  return launch_quantize_t<int8_t>(a, qa, sa);
+}
+
+hipError_t launch_quantize_a16(const MatArgs& a, int16_t* qa, float* sa) {
+  return launch_quantize_t<int16_t>(a, qa, sa);
 }
 
 template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS>

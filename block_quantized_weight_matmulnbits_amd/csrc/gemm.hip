@@ -764,6 +764,7 @@ hipError_t launch_gemm_mfma_gidx(const MatArgs& a) {
 
 hipError_t launch_gemm(const MatArgs& a) {
   if (a.g_idx) return launch_gidx(a);
+  if (a.bits == 3) return launch_generic_float(a);
   switch (a.bits) {
     case 2: return launch_gemm_x<2>(a);
     case 4: return launch_gemm_x<4>(a);

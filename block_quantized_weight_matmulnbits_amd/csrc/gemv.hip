@@ -486,6 +486,7 @@ static hipError_t launch_gemv_x(const GemvArgs& a) {
 
 hipError_t launch_gemv(const GemvArgs& a) {
   if (a.g_idx) return launch_gidx(a);
+  if (a.bits == 3) return launch_generic_float(a);
   // The tiled layout: its own split-K kernel, or for f32 activations and
   // blocks shorter than a 16-byte unit of codes, the row kernel of the GEMM.
   if (a.tiled) return gemv_tiled_supported(a) ? launch_gemv_tiled(a) : launch_gemm(a);

@@ -1,0 +1,254 @@
+// generic.hip -- one operator-layout kernel for the code widths and
+// activation types the specialized kernels do not take: 3-bit weights
+// (float, int8 and int16 activations) and int16 activations (any width).
+//
+// Definitions:
+//  * Float activations (onnx-runtime-ep-cpu matmul_nbits.rs: module
+//    documentation, dequantize_nbits_value): y = sum_b s[n,b] *
+//    sum_{k in b} x[k] * (code - zp), fp32.
+//  * int8 (CompInt8) or int16 activations, quantized per block beforehand
+//    (quantize_a_kernel): dot[m,n,b] = sum_{k in b} qa * (code - zp), exact
+//    int32, y = sum_b float(dot) * (sa[m,b] * s[n,b]).  The int16 route is the
+//    8-bit route of execute on that page (activations quantized to int16 per
+//    K-block, an integer dot against the codes); with |qa| <= 32767 and
+//    |code - zp| <= 255 the dot of a block of at most 128 codes is exact in
+//    int32.
+//  * 3-bit codes (MNN ConvInt8TiledExecutor.cpp, the 3-bit weight reorder):
+//    a block's blob is bs/4 bytes of the low two bits of each code (LSB
+//    first) then bs/8 bytes of the high bits; zero points are one LSB-first
+//    3-bit stream per row; default zero point 4.
+//
+// Work split: a workgroup of 4 waves owns 4 * R output columns; a wave walks
+// the blocks of its R columns with one lane per block (lanes stride over the
+// row's blocks), so each block's sum is formed in one lane and scaled once.
+// The activations of MT rows are staged in LDS per chunk of whole blocks
+// (fp32 values, or the int8 / int16 codes widened to int32).
+#include <algorithm>
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+namespace {
+
+enum : int { ACT_F = 0, ACT_I8 = 1, ACT_I16 = 2 };
+constexpr int GN_R = 2;          // output columns per wave
+
+// 16 codes of a block, starting at code i0 (a multiple of 16) of the block
+// whose blob starts at `blk` (bs codes).
+template <int BITS>
+__device__ __forceinline__ void codes16(const uint8_t* __restrict__ blk, int bs, int i0,
+                                        int (&c)[16]) {
+  if constexpr (BITS == 3) {
+    const uint8_t* lo = blk + i0 / 4;            // 4 bytes, 2 bits per code
+    const uint8_t* hi = blk + bs / 4 + i0 / 8;   // 2 bytes, 1 bit per code
+    const uint32_t l = (uint32_t)lo[0] | ((uint32_t)lo[1] << 8) | ((uint32_t)lo[2] << 16) |
+                       ((uint32_t)lo[3] << 24);
+    const uint32_t h = (uint32_t)hi[0] | ((uint32_t)hi[1] << 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[j] = (int)(((l >> (2 * j)) & 3u) | (((h >> j) & 1u) << 2));
+  } else {
+    constexpr int P = 32 / BITS;
+    constexpr uint32_t m = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(blk + i0 * BITS / 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[j] = (int)((w[j / P] >> ((j % P) * BITS)) & m);
+  }
+}
+
+// Zero point of block b from a packed zero-point row (LSB-first stream; a
+// 3-bit value may continue into the next byte).
+template <int BITS, bool HAS_ZP>
+__device__ __forceinline__ int zero_point(const uint8_t* __restrict__ zrow, int b) {
+  if constexpr (!HAS_ZP) {
+    return 1 << (BITS - 1);
+  } else {
+    constexpr uint32_t m = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+    const int bit = b * BITS;
+    uint32_t v = (uint32_t)zrow[bit >> 3] >> (bit & 7);
+    if ((bit & 7) + BITS > 8) v |= (uint32_t)zrow[(bit >> 3) + 1] << (8 - (bit & 7));
+    return (int)(v & m);
+  }
+}
+
+template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, int MT, bool DOTS>
+__global__ __launch_bounds__(256) void generic_rows_kernel(
+    const void* __restrict__ A, const void* __restrict__ qa, const float* __restrict__ sa,
+    const uint8_t* __restrict__ B, const typename dt<SDT>::T* __restrict__ scales,
+    const uint8_t* __restrict__ zp, const void* __restrict__ bias, void* __restrict__ Y,
+    int32_t* __restrict__ dots, int Mp, int M, int K, int N, int bs, int kb, int blob,
+    int zp_row_bytes, int chunk_blocks) {
+  extern __shared__ float gn_lds[];
+  float* xs = gn_lds;                                        // [MT][chunk] fp32 (ACT_F)
+  int* qs = reinterpret_cast<int*>(gn_lds);                  // [MT][chunk] int32 (ACT_I*)
+  using XT = typename dt<XDT>::T;
+  const int chunk = chunk_blocks * bs;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = (blockIdx.x * 4 + wave) * GN_R;
+  const int64_t padded = (int64_t)kb * bs;
+  float acc[GN_R][MT];
+#pragma unroll
+  for (int r = 0; r < GN_R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  for (int b0 = 0; b0 < kb; b0 += chunk_blocks) {
+    const int k0 = b0 * bs;
+    __syncthreads();
+    for (int t = threadIdx.x; t < MT * chunk; t += 256) {
+      const int m = t / chunk, e = t % chunk, k = k0 + e;
+      if constexpr (ACT == ACT_F) {
+        xs[t] = (m < Mp && k < K) ? dt<XDT>::to_f32(reinterpret_cast<const XT*>(A)[(int64_t)m * K + k])
+                                  : 0.0f;
+      } else if constexpr (ACT == ACT_I8) {
+        qs[t] = (m < Mp && k < padded) ? (int)reinterpret_cast<const int8_t*>(qa)[m * padded + k] : 0;
+      } else {
+        qs[t] = (m < Mp && k < padded) ? (int)reinterpret_cast<const int16_t*>(qa)[m * padded + k] : 0;
+      }
+    }
+    __syncthreads();
+    const int b1 = min(kb, b0 + chunk_blocks);
+    for (int b = b0 + lane; b < b1; b += 64) {
+#pragma unroll
+      for (int r = 0; r < GN_R; ++r) {
+        const int n = n0 + r;
+        if (n >= N) continue;
+        const uint8_t* blk = B + ((int64_t)n * kb + b) * blob;
+        const int z = zero_point<BITS, HAS_ZP>(zp + (int64_t)n * zp_row_bytes, b);
+        const float s = dt<SDT>::to_f32(scales[(int64_t)n * kb + b]);
+        float df[MT];
+        int di[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          df[m] = 0.0f;
+          di[m] = 0;
+        }
+        const int e0 = (b - b0) * bs;
+        for (int i0 = 0; i0 < bs; i0 += 16) {
+          int c[16];
+          codes16<BITS>(blk, bs, i0, c);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int w = c[j] - z;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              if constexpr (ACT == ACT_F) df[m] = fmaf(xs[m * chunk + e0 + i0 + j], (float)w, df[m]);
+              else di[m] += qs[m * chunk + e0 + i0 + j] * w;
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if constexpr (ACT == ACT_F) {
+            acc[r][m] = fmaf(df[m], s, acc[r][m]);
+          } else {
+            if constexpr (DOTS) {
+              if (m < Mp) dots[((int64_t)m * N + n) * kb + b] = di[m];
+            }
+            const float sab = m < Mp ? sa[(int64_t)m * kb + b] : 0.0f;
+            acc[r][m] = fmaf((float)di[m], sab * s, acc[r][m]);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (DOTS) return;
+#pragma unroll
+  for (int r = 0; r < GN_R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float v = wave_sum(acc[r][m]);
+      const int n = n0 + r;
+      if (lane == 0 && n < N && m < Mp) {
+        float o = v;
+        if (bias) o += dt<XDT>::to_f32(reinterpret_cast<const XT*>(bias)[n]);
+        reinterpret_cast<XT*>(Y)[(int64_t)m * N + n] = dt<XDT>::from_f32(o);
+      }
+    }
+}
+
+int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS>
+hipError_t launch_gn_t(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  constexpr int MT = 4;
+  using ST = typename dt<SDT>::T;
+  // Whole blocks per staged chunk: at least one, about 2048 activations.
+  const int chunk_blocks = (int)std::max<int64_t>(1, 2048 / a.block_size);
+  const size_t lds = (size_t)MT * chunk_blocks * a.block_size * 4;
+  auto kern = generic_rows_kernel<ACT, BITS, XDT, SDT, HAS_ZP, MT, DOTS>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int grid = (int)((a.N + 4 * GN_R - 1) / (4 * GN_R));
+  const int64_t padded = a.kb * a.block_size;
+  for (int64_t m0 = 0; m0 < a.M; m0 += MT) {
+    const int Mp = (int)std::min<int64_t>(MT, a.M - m0);
+    const int qb = ACT == ACT_I16 ? 2 : 1;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, a.stream,
+                       ACT == ACT_F ? (const void*)((const char*)a.A + m0 * a.K * dtype_bytes(a.a_dtype))
+                                    : a.A,
+                       qa ? (const void*)((const char*)qa + m0 * padded * qb) : nullptr,
+                       sa ? sa + m0 * a.kb : nullptr, a.B, (const ST*)a.scales, a.zp, a.bias,
+                       DOTS ? nullptr : (void*)((char*)a.Y + m0 * a.N * dtype_bytes(a.a_dtype)),
+                       DOTS ? dots + m0 * a.N * a.kb : nullptr, Mp, (int)a.M, (int)a.K, (int)a.N,
+                       (int)a.block_size, (int)a.kb, (int)a.blob, (int)a.zp_row_bytes,
+                       chunk_blocks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int ACT, int BITS, int XDT, bool DOTS>
+hipError_t launch_gn_s(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  auto z = [&](auto sdt) {
+    constexpr int SDT = decltype(sdt)::value;
+    return a.zp ? launch_gn_t<ACT, BITS, XDT, SDT, true, DOTS>(a, qa, sa, dots)
+                : launch_gn_t<ACT, BITS, XDT, SDT, false, DOTS>(a, qa, sa, dots);
+  };
+  switch (a.s_dtype) {
+    case DT_F32: return z(std::integral_constant<int, DT_F32>{});
+    case DT_F16: return z(std::integral_constant<int, DT_F16>{});
+    default: return z(std::integral_constant<int, DT_BF16>{});
+  }
+}
+
+template <int ACT, int BITS, bool DOTS>
+hipError_t launch_gn_x(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  switch (a.a_dtype) {
+    case DT_F32: return launch_gn_s<ACT, BITS, DT_F32, DOTS>(a, qa, sa, dots);
+    case DT_F16: return launch_gn_s<ACT, BITS, DT_F16, DOTS>(a, qa, sa, dots);
+    default: return launch_gn_s<ACT, BITS, DT_BF16, DOTS>(a, qa, sa, dots);
+  }
+}
+
+template <int ACT, bool DOTS>
+hipError_t launch_gn_b(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  switch (a.bits) {
+    case 2: return launch_gn_x<ACT, 2, DOTS>(a, qa, sa, dots);
+    case 3: return launch_gn_x<ACT, 3, DOTS>(a, qa, sa, dots);
+    case 4: return launch_gn_x<ACT, 4, DOTS>(a, qa, sa, dots);
+    default: return launch_gn_x<ACT, 8, DOTS>(a, qa, sa, dots);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_generic_float(const MatArgs& a) {
+  return launch_gn_b<ACT_F, false>(a, nullptr, nullptr, nullptr);
+}
+
+hipError_t launch_generic_int(const MatArgs& a, const void* qa, int act_bytes, const float* sa,
+                              int32_t* dots) {
+  if (act_bytes == 1)
+    return dots ? launch_gn_b<ACT_I8, true>(a, qa, sa, dots)
+                : launch_gn_b<ACT_I8, false>(a, qa, sa, nullptr);
+  return dots ? launch_gn_b<ACT_I16, true>(a, qa, sa, dots)
+              : launch_gn_b<ACT_I16, false>(a, qa, sa, nullptr);
+}
+
+}  // namespace qmm

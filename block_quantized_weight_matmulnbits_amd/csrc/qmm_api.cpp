@@ -59,10 +59,10 @@ int validate_matmul(const char* fn, Route route, const void* A, int a_dtype, con
                     int b_layout, const void* scales, int s_dtype, const uint8_t* zp,
                     const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
                     int bits, int accuracy_level, MatArgs* out) {
-  if (bits != 2 && bits != 4 && bits != 8)
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
     return fail(QMM_ERR_INVALID_ARG,
-                "%s: bits must be 2, 4 or 8, got bits=%d. Why: other packed widths have no "
-                "validated unpacking path. How to fix: export the weight with bits=2, 4 or 8.",
+                "%s: bits must be 2, 3, 4 or 8, got bits=%d. Why: other packed widths have no "
+                "validated unpacking path. How to fix: export the weight with bits=2, 3, 4 or 8.",
                 fn, bits);
   if (block_size < 16 || !is_pow2(block_size))
     return fail(QMM_ERR_INVALID_ARG,
@@ -95,6 +95,12 @@ int validate_matmul(const char* fn, Route route, const void* A, int a_dtype, con
                 "operator's [N, kb, block_size*bits/8] bytes, or QMM_LAYOUT_TILED[_ZP] for a "
                 "buffer written by qmm_repack.", fn, b_layout);
   const bool tiled = b_layout != QMM_LAYOUT_ORT;
+  if (bits == 3 && (tiled || block_size > qmm::GENERIC_MAX_BS))
+    return fail(QMM_ERR_UNSUPPORTED,
+                "%s: 3-bit weights run on the operator's layout with block_size <= %lld (got "
+                "layout %d, block_size %d). Why: the tiled layout and the repack are defined for "
+                "2, 4 and 8 bits. How to fix: pass the operator's B (QMM_LAYOUT_ORT).", fn,
+                (long long)qmm::GENERIC_MAX_BS, b_layout, block_size);
   if (tiled && (scales != nullptr || zp != nullptr))
     return fail(QMM_ERR_INVALID_ARG,
                 "%s: with a tiled layout the scales and zero_points arguments must be NULL. "
@@ -199,6 +205,10 @@ int validate_g_idx(const char* fn, MatArgs* a, const int32_t* g_idx, int64_t g_i
     return fail(QMM_ERR_UNSUPPORTED, "%s: group indices are supported on the operator's layout "
                 "only. Why: the tiled buffer is laid out for block-contiguous groups. How to "
                 "fix: pass the operator's B, scales and zero points (QMM_LAYOUT_ORT).", fn);
+  if (a->bits == 3)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: group indices are not supported with 3-bit weights. "
+                "Why: the group-index kernels read codes as one bit stream per row, the 3-bit "
+                "blob holds two bit planes per block.", fn);
   a->g_idx = g_idx;
   return QMM_OK;
 }
@@ -265,7 +275,10 @@ int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t
   int8_t* qa = (int8_t*)workspace;
   float* sa = (float*)((char*)workspace + ws_qa_bytes(a.M, a.kb, a.block_size));
   hipError_t e = launch_quantize_a(a, qa, sa);
-  if (e == hipSuccess) e = a.tiled ? launch_compint8_tiled(a, qa, sa) : launch_compint8(a, qa, sa);
+  if (e == hipSuccess) {
+    if (a.bits == 3) e = launch_generic_int(a, qa, 1, sa, nullptr);
+    else e = a.tiled ? launch_compint8_tiled(a, qa, sa) : launch_compint8(a, qa, sa);
+  }
   return hip_status(e, fn);
 }
 
@@ -338,6 +351,67 @@ int qmm_check_g_idx(const int32_t* g_idx, int64_t g_idx_len, int64_t K, int bloc
                   "How to fix: re-export the weight's group indices.", fn, (long long)i,
                   (int)g_idx[i], (long long)kb);
   return QMM_OK;
+}
+
+size_t qmm_int16_workspace_size(int64_t M, int64_t K, int block_size) {
+  if (M < 0 || K <= 0 || block_size <= 0) return 0;
+  const int64_t kb = (K + block_size - 1) / block_size;
+  return qmm::ws16_total_bytes(M, kb, block_size);
+}
+
+// Shared by qmm_gemm_int16 and its block-dot export: validation, workspace,
+// quantization, then the generic kernel (dots non-null: the export).
+static int int16_impl(const char* fn, const void* A, int a_dtype, const uint8_t* B,
+                      int b_layout, const void* scales, int s_dtype, const uint8_t* zero_points,
+                      const void* bias, void* Y, int64_t M, int64_t K, int64_t N, int block_size,
+                      int bits, void* workspace, size_t workspace_bytes, int32_t* dots,
+                      void* stream) {
+  MatArgs a;
+  int st = validate_matmul(fn, Route::Float, A, a_dtype, B, b_layout, scales, s_dtype,
+                           zero_points, bias, dots ? (void*)dots : Y, M, K, N, block_size, bits,
+                           0, &a);
+  if (st != QMM_OK) return st;
+  if (a.tiled || block_size > 128)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: int16 activations run on the operator's layout with "
+                "block_size <= 128 (got layout %d, block_size %d). Why: a block's dot of int16 "
+                "activations and codes is exact in int32 up to 128 codes. How to fix: use "
+                "qmm_gemm, or a smaller block.", fn, b_layout, block_size);
+  if (M == 0) return QMM_OK;
+  const size_t need = qmm::ws16_total_bytes(a.M, a.kb, a.block_size);
+  if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0)
+    return fail(QMM_ERR_WORKSPACE, "%s: the workspace holds %zu bytes at %p, %zu are needed "
+                "(256-byte aligned). Why: the int16 activations and their block scales are "
+                "stored there. How to fix: pass qmm_int16_workspace_size(M, K, block_size) "
+                "bytes.", fn, workspace_bytes, workspace, need);
+  a.stream = (hipStream_t)stream;
+  int16_t* qa = (int16_t*)workspace;
+  float* sa = (float*)((char*)workspace + qmm::ws16_qa_bytes(a.M, a.kb, a.block_size));
+  hipError_t e = hipSuccess;
+  if (dots) e = hipMemsetAsync(dots, 0, (size_t)(a.M * a.N * a.kb) * sizeof(int32_t), a.stream);
+  if (e == hipSuccess) e = qmm::launch_quantize_a16(a, qa, sa);
+  if (e == hipSuccess) e = qmm::launch_generic_int(a, qa, 2, sa, dots);
+  return hip_status(e, fn);
+}
+
+int qmm_gemm_int16(const void* A, int a_dtype, const uint8_t* B, int b_layout,
+                   const void* scales, int s_dtype, const uint8_t* zero_points, const void* bias,
+                   void* Y, int64_t M, int64_t K, int64_t N, int block_size, int bits,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return int16_impl("qmm_gemm_int16", A, a_dtype, B, b_layout, scales, s_dtype, zero_points,
+                    bias, Y, M, K, N, block_size, bits, workspace, workspace_bytes, nullptr,
+                    stream);
+}
+
+int qmm_debug_int16_block_dots(const void* A, int a_dtype, const uint8_t* B,
+                               const uint8_t* zero_points, int64_t M, int64_t K, int64_t N,
+                               int block_size, int bits, int32_t* dots, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (dots == nullptr)
+    return fail(QMM_ERR_INVALID_ARG, "qmm_debug_int16_block_dots: dots must be non-null.");
+  // Scales are not read by the block dots; B stands in for the pointer.
+  return int16_impl("qmm_debug_int16_block_dots", A, a_dtype, B, QMM_LAYOUT_ORT, B, QMM_F32,
+                    zero_points, nullptr, nullptr, M, K, N, block_size, bits, workspace,
+                    workspace_bytes, dots, stream);
 }
 
 int qmm_gemm_fp4(const void* A, int a_dtype, const uint8_t* W, const uint8_t* scales,
@@ -434,6 +508,9 @@ int qmm_repack(const uint8_t* B, const void* scales, int s_dtype, const uint8_t*
                            s_dtype, zero_points, nullptr, (void*)B, 0, K, N, block_size, bits, 0,
                            &a);
   if (st != QMM_OK) return st;
+  if (bits == 3)
+    return fail(QMM_ERR_UNSUPPORTED, "qmm_repack: 3-bit weights have no tiled layout. How to "
+                "fix: pass the operator's layout to the matmuls.");
   const size_t need = qmm_repacked_bytes(K, N, block_size, bits, s_dtype, zero_points != nullptr);
   if (out == nullptr || out_bytes < need || ((uintptr_t)out & 255) != 0)
     return fail(QMM_ERR_INVALID_ARG, "qmm_repack: out must be a 256-byte aligned device buffer "
@@ -452,6 +529,8 @@ int qmm_unrepack(const void* tiled, int has_zero_points, int64_t K, int64_t N, i
   int st = validate_matmul("qmm_unrepack", Route::Float, B, QMM_BF16, B, QMM_LAYOUT_ORT, scales,
                            s_dtype, nullptr, nullptr, (void*)B, 0, K, N, block_size, bits, 0, &a);
   if (st != QMM_OK) return st;
+  if (bits == 3)
+    return fail(QMM_ERR_UNSUPPORTED, "qmm_unrepack: 3-bit weights have no tiled layout.");
   if (tiled == nullptr || ((uintptr_t)tiled & 255) != 0 || (has_zero_points && !zero_points))
     return fail(QMM_ERR_INVALID_ARG, "qmm_unrepack: tiled must be a 256-byte aligned repacked "
                 "buffer, and zero_points non-NULL when it holds zero points.");
@@ -530,9 +609,11 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
     return hip_status(e, "qmm_debug_compint8_block_dots");
   }
   if (e == hipSuccess) e = qmm::launch_quantize_a(a, qa, sa);
-  if (e == hipSuccess)
-    e = a.tiled ? qmm::launch_compint8_tiled_dots(a, qa, sa, dots)
-                : qmm::launch_compint8_dots(a, qa, sa, dots);
+  if (e == hipSuccess) {
+    if (a.bits == 3) e = qmm::launch_generic_int(a, qa, 1, sa, dots);
+    else e = a.tiled ? qmm::launch_compint8_tiled_dots(a, qa, sa, dots)
+                     : qmm::launch_compint8_dots(a, qa, sa, dots);
+  }
   return hip_status(e, "qmm_debug_compint8_block_dots");
 }
 

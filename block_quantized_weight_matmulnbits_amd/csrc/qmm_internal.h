@@ -105,6 +105,29 @@ hipError_t launch_repack(const MatArgs& a, uint8_t* tiled, bool inverse, uint8_t
 // Codec export: codes [N, K], zero points [N, kb], dequantized weight [N, K].
 hipError_t launch_unpack(const MatArgs& a, uint8_t* codes, uint8_t* zps, float* w);
 
+// Workspace layout of CompInt8: qa [M, kb*bs] int8, then sa [M, kb] float,
+// each region 256-byte aligned.
+inline size_t ws_align(size_t v) { return (v + 255) / 256 * 256; }
+inline size_t ws_qa_bytes(int64_t M, int64_t kb, int64_t bs) { return ws_align((size_t)(M * kb * bs)); }
+inline size_t ws_total_bytes(int64_t M, int64_t kb, int64_t bs) {
+  return ws_qa_bytes(M, kb, bs) + ws_align((size_t)(M * kb * 4));
+}
+
+// The generic operator-layout kernel (generic.hip): 3-bit codes, and int8
+// / int16 activations quantized per block (qa, sa) for any code width; with
+// dots non-null the exact int32 block dots [M, N, kb] are written instead of
+// Y.  Blocks of at most GENERIC_MAX_BS codes.
+constexpr int64_t GENERIC_MAX_BS = 8192;
+hipError_t launch_generic_float(const MatArgs& a);
+hipError_t launch_generic_int(const MatArgs& a, const void* qa, int act_bytes, const float* sa,
+                              int32_t* dots);
+// int16 activations: qa16 [M, kb*bs] int16 and sa [M, kb] f32 (compint8.hip).
+hipError_t launch_quantize_a16(const MatArgs& a, int16_t* qa, float* sa);
+inline size_t ws16_qa_bytes(int64_t M, int64_t kb, int64_t bs) { return ws_align((size_t)(M * kb * bs * 2)); }
+inline size_t ws16_total_bytes(int64_t M, int64_t kb, int64_t bs) {
+  return ws16_qa_bytes(M, kb, bs) + ws_align((size_t)(M * kb * 4));
+}
+
 // The body of qmm_gemm_compint8 (validation, route choice, launches), shared
 // with the entry point that takes no workspace: fn names the entry point in
 // messages; when resolve_workspace is non-null it is called after the
@@ -123,12 +146,5 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 // Record a message for qmm_last_error and return code.
 int set_error(int code, const char* message);
 
-// Workspace layout of CompInt8: qa [M, kb*bs] int8, then sa [M, kb] float,
-// each region 256-byte aligned.
-inline size_t ws_align(size_t v) { return (v + 255) / 256 * 256; }
-inline size_t ws_qa_bytes(int64_t M, int64_t kb, int64_t bs) { return ws_align((size_t)(M * kb * bs)); }
-inline size_t ws_total_bytes(int64_t M, int64_t kb, int64_t bs) {
-  return ws_qa_bytes(M, kb, bs) + ws_align((size_t)(M * kb * 4));
-}
 
 }  // namespace qmm

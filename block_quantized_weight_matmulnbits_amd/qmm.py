@@ -42,6 +42,11 @@ _SIGS = {
                            _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
                                    _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "qmm_int16_workspace_size": ([_i64, _i64, _i32], _sz),
+    "qmm_gemm_int16": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                        _vp, _sz, _vp], _i32),
+    "qmm_debug_int16_block_dots": ([_vp, _i32, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz,
+                                    _vp], _i32),
     "qmm_gemm_fp4": ([_vp, _i32, _vp, _vp, _i32, _f32, _vp, _vp, _i64, _i64, _i64, _vp], _i32),
     "qmm_step_create": ([_vp], _i32),
     "qmm_step_add_gemv": ([_vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64,
@@ -219,6 +224,27 @@ def qmm_gemm_compint8_noalloc(A, B, scales, zero_points, bias, Y, M, K, N, block
     _check(lib.qmm_gemm_compint8_noalloc(_ptr(A), _dt(A), b, layout, s, sdt, _ptr(zero_points),
                                          gp, gn, _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
                                          accuracy_level, _stream(stream)))
+
+
+def qmm_int16_workspace_size(M, K, block_size) -> int:
+    return int(lib.qmm_int16_workspace_size(M, K, block_size))
+
+
+def qmm_gemm_int16(A, B, scales, zero_points, bias, Y, M, K, N, block_size, bits, workspace,
+                   stream=None):
+    """int16 activations (operator layout); ``B`` is the operator's tensor."""
+    _check(lib.qmm_gemm_int16(_ptr(A), _dt(A), _ptr(B), QMM_LAYOUT_ORT, _ptr(scales), _dt(scales),
+                              _ptr(zero_points), _ptr(bias), _ptr(Y), M, K, N, block_size, bits,
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+
+
+def qmm_debug_int16_block_dots(A, B, zero_points, M, K, N, block_size, bits, dots, workspace,
+                               stream=None):
+    _check(lib.qmm_debug_int16_block_dots(_ptr(A), _dt(A), _ptr(B), _ptr(zero_points), M, K, N,
+                                          block_size, bits, _ptr(dots), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
 
 
 QMM_MXFP4, QMM_NVFP4 = 0, 1

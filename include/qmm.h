@@ -78,9 +78,17 @@ const char *qmm_last_error(void);
  *   g_idx  [g_idx_len]    int32 group indices or NULL (then g_idx_len = 0)
  *   bias   [N]            a_dtype or NULL
  *   Y      [N]            a_dtype (written)
- * bits in {2, 4, 8}; block_size a power of two >= 16 (MatMulNBitsFactory::
+ * bits in {2, 3, 4, 8}; block_size a power of two >= 16 (MatMulNBitsFactory::
  * create).  accuracy_level 0..3 select float compute; the hint can only raise
  * precision and every level computes fp32-accumulated products here.
+ * 3-bit weights (MNN ConvInt8TiledExecutor.cpp: the 3-bit reorder splits
+ * each code 0..7 into a 2-bit and a 1-bit plane, offset -4): a block's blob
+ * of 3 * block_size / 8 bytes is block_size / 4 bytes of the codes' low two
+ * bits (code i at bits 2 (i % 4) of byte i / 4) then block_size / 8 bytes of
+ * their high bits (code i at bit i % 8 of byte block_size / 4 + i / 8);
+ * zero points are one LSB-first 3-bit stream per row of ceil(kb * 3 / 8)
+ * bytes (a value may cross a byte), default 4.  3-bit weights take the
+ * operator's layout only, block_size <= 8192, and no group indices.
  * accuracy_level 4 (int8 activations) is rejected: use qmm_gemm_compint8.
  *
  * Group indices (act-order; matmul_nbits.rs execute and the group-index
@@ -176,6 +184,36 @@ int qmm_gemm_compint8_noalloc(const void *A, int a_dtype, const uint8_t *B,
                               int64_t g_idx_len, const void *bias, void *Y,
                               int64_t M, int64_t K, int64_t N, int block_size,
                               int bits, int accuracy_level, void *stream);
+
+/*
+ * int16 activations (matmul_nbits.rs execute, the 8-bit route: the
+ * activation is quantized to int16 per K-block and reduced against the codes
+ * with an integer dot; that page keeps int16 because it matches the fp32
+ * result).  Per row m and block b: sa = max|x| / 32767 (IEEE binary32
+ * division), qa = clamp(round_half_even(x / sa), -32767, 32767) (0 past K and
+ * for sa == 0); dot = sum qa * (code - zp) exactly in int32 and Y[m, n] =
+ * sum_b float(dot) * (sa[m, b] * scale[n, b]) (+ bias[n]) in fp32.  Any code
+ * width (2, 3, 4, 8), the operator's layout, block_size <= 128 (the int32
+ * dot is exact); otherwise QMM_ERR_UNSUPPORTED.  workspace: at least
+ * qmm_int16_workspace_size(M, K, block_size) bytes, 256-byte aligned; on
+ * return it holds qa [M, kb * block_size] int16 at offset 0 and sa [M, kb]
+ * float32 at the next 256-byte boundary.  Arguments otherwise as qmm_gemm.
+ * qmm_debug_int16_block_dots writes the int32 block dots [M, N, kb] (same
+ * workspace contract; scales are not read).
+ */
+size_t qmm_int16_workspace_size(int64_t M, int64_t K, int block_size);
+
+int qmm_gemm_int16(const void *A, int a_dtype, const uint8_t *B, int b_layout,
+                   const void *scales, int s_dtype, const uint8_t *zero_points,
+                   const void *bias, void *Y, int64_t M, int64_t K, int64_t N,
+                   int block_size, int bits, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+int qmm_debug_int16_block_dots(const void *A, int a_dtype, const uint8_t *B,
+                               const uint8_t *zero_points, int64_t M, int64_t K,
+                               int64_t N, int block_size, int bits,
+                               int32_t *dots, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * Matmul with block-scaled FP4 weights (rlx-cpu quant.rs: dequant_matmul_nvfp4,

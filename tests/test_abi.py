@@ -50,8 +50,9 @@ def gemv(qmm, **kw):
 
 
 @pytest.mark.parametrize("kw,code,needle", [
-    (dict(bits=3), -1, "bits must be 2, 4 or 8"),
-    (dict(bits=16), -1, "bits must be 2, 4 or 8"),
+    (dict(bits=5), -1, "bits must be 2, 3, 4 or 8"),
+    (dict(bits=3, b_layout=1, scales=None), -2, "3-bit weights run on the operator's layout"),
+    (dict(bits=16), -1, "bits must be 2, 3, 4 or 8"),
     (dict(bs=8), -1, "power of two and at least 16"),
     (dict(bs=48), -1, "power of two and at least 16"),
     (dict(K=0), -1, "K and N must be positive"),
@@ -71,6 +72,8 @@ def gemv(qmm, **kw):
     (dict(g=FAKE, glen=100), -1, "g_idx must have shape [4096] or [4096]"),
     (dict(g=FAKE + 2, glen=4096), -1, "g_idx must be 4-byte aligned"),
     (dict(g=FAKE, glen=4096, b_layout=2, scales=None), -2, "operator's layout only"),
+    (dict(bits=3, g=FAKE, glen=4096), -2, "not supported with 3-bit weights"),
+    (dict(bits=3, bs=16384, K=16384), -2, "block_size <= 8192"),
 ])
 def test_gemv_rejects_bad_arguments(qmm, kw, code, needle):
     assert gemv(qmm, **kw) == code
@@ -226,11 +229,39 @@ def test_noalloc_compint8_rejects_on_the_host(qmm):
                                            16384, 64, 128, 4, 4, None)
     assert st == -3 and "row batches" in qmm.qmm_last_error()
     st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 4, 4096,
-                                           64, 128, 3, 4, None)
-    assert st == -1 and "bits must be 2, 4 or 8" in qmm.qmm_last_error()
+                                           64, 128, 5, 4, None)
+    assert st == -1 and "bits must be 2, 3, 4 or 8" in qmm.qmm_last_error()
     st = qmm.lib.qmm_gemm_compint8_noalloc(FAKE, 2, FAKE, 0, FAKE, 2, None, None, 0, None, FAKE, 4, 4096,
                                            64, 128, 4, 0, None)
     assert st == -1 and "accuracy_level must be 4" in qmm.qmm_last_error()
+
+
+def test_int16_activations_reject_on_the_host(qmm):
+    """qmm_gemm_int16 and its block-dot export: operator layout, block_size
+    <= 128 and a workspace of qmm_int16_workspace_size bytes, checked before
+    any device work."""
+    ws = qmm.qmm_int16_workspace_size(4, 4096, 64)
+    kb = 4096 // 64
+    assert ws == -(-4 * 4096 * 2 // 256) * 256 + -(-4 * kb * 4 // 256) * 256
+    assert qmm.qmm_int16_workspace_size(-1, 4096, 64) == 0
+
+    def call(bs=64, layout=0, scales=FAKE, w=FAKE, wbytes=1 << 30, bits=4):
+        return qmm.lib.qmm_gemm_int16(FAKE, 2, FAKE, layout, scales, 2, None, None, FAKE, 4, 4096,
+                                      64, bs, bits, w, wbytes, None)
+    assert call(bs=256) == -2 and "block_size <= 128" in qmm.qmm_last_error()
+    assert call(layout=1, scales=None) == -2 and "operator's layout" in qmm.qmm_last_error()
+    assert call(w=None) == -3 and "qmm_int16_workspace_size" in qmm.qmm_last_error()
+    assert call(wbytes=ws - 1) == -3
+    assert call(w=FAKE + 16) == -3
+    assert call(bits=5) == -1
+    st = qmm.lib.qmm_debug_int16_block_dots(FAKE, 2, FAKE, None, 4, 4096, 64, 64, 4, None, FAKE,
+                                            1 << 30, None)
+    assert st == -1 and "dots must be non-null" in qmm.qmm_last_error()
+
+
+def test_three_bit_weights_have_no_tiled_layout(qmm):
+    assert qmm.lib.qmm_repack(FAKE, FAKE, 2, None, 4096, 64, 32, 3, FAKE, 1 << 30, None) == -2
+    assert "no tiled layout" in qmm.qmm_last_error()
 
 
 def test_check_g_idx_on_host_arrays(qmm):
