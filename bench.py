@@ -67,7 +67,7 @@ def parse():
                         "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
-    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4"], default=None,
+    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4", "lowbit"], default=None,
                    help="time only this workload and print its object (profiling runs)")
     p.add_argument("--read-sweep", action="store_true",
                    help="only sweep the plain streaming read (bench_probe/) over launch shapes "
@@ -107,7 +107,7 @@ def main():
             torch.cuda.synchronize()
             del src, dst
         fn = {"compint8": bench_compint8, "prefill": bench_prefill, "conv": bench_conv,
-              "tiny": bench_tiny, "fp4": bench_fp4}[args.only]
+              "tiny": bench_tiny, "fp4": bench_fp4, "lowbit": bench_lowbit}[args.only]
         print(json.dumps({args.only: fn(qmm, dev, stream, args)}), flush=True)
         return
     if args.copy_calibration:
@@ -349,6 +349,7 @@ def main():
     out["compint8"] = bench_compint8(qmm, dev, stream, args)
     out["conv_int8"] = bench_conv(qmm, dev, stream, args)
     out["fp4"] = bench_fp4(qmm, dev, stream, args)
+    out["lowbit"] = bench_lowbit(qmm, dev, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
@@ -661,6 +662,61 @@ def bench_fp4(qmm, dev, stream, args):
                                                flop / (msp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         }
         del p, Y
+    return res
+
+
+def bench_lowbit(qmm, dev, stream, args):
+    """3-bit weights (bs 32, asymmetric, bf16 scales) and 8-bit weights with
+    int16 activations (bs 32, asymmetric) on the decode-shaped projection
+    K=4096 N=14336, operator layout, bf16 activations: the float GEMV / GEMM
+    (3-bit) at M in {1, 16}, CompInt8 (3-bit) and the int16 route (8-bit) at
+    M in {1, 4, 16}.  Weights rotate through copies so each launch streams them
+    from HBM; times include the activation quantization."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    res = {}
+    for bits, route in ((3, "float"), (3, "compint8"), (8, "int16")):
+        base = make_matmul_case(1, 4096, 14336, 32, bits, a_dtype="bf16", has_zp=True,
+                                seed=50 + bits).to(dev)
+        nbytes = base.weight_bytes()
+        n_copies = max(2, -(-POOL_BYTES // nbytes))
+        pool = [(base.B, base.scales, base.zero_points)] + [
+            (base.B.clone(), base.scales.clone(), base.zero_points.clone())
+            for _ in range(n_copies - 1)]
+        for M in ((1, 16) if route == "float" else (1, 4, 16)):
+            c = make_matmul_case(M, 4096, 14336, 32, bits, a_dtype="bf16", has_zp=True,
+                                 seed=60 + M)
+            A = c.A.to(dev)
+            Y = torch.empty(M, c.N, dtype=torch.bfloat16, device=dev)
+            if route == "compint8":
+                ws = torch.empty(qmm.qmm_compint8_workspace_size(M, c.K, 32), dtype=torch.uint8,
+                                 device=dev)
+            elif route == "int16":
+                ws = torch.empty(qmm.qmm_int16_workspace_size(M, c.K, 32), dtype=torch.uint8,
+                                 device=dev)
+
+            def run(i, route=route, A=A, Y=Y, M=M, c=c, bits=bits):
+                B, sc, zp = pool[i % len(pool)]
+                if route == "float" and M == 1:
+                    qmm.qmm_gemv(A.reshape(-1), B, sc, zp, None, Y.reshape(-1), c.K, c.N, 32,
+                                 bits, stream=stream)
+                elif route == "float":
+                    qmm.qmm_gemm(A, B, sc, zp, None, Y, M, c.K, c.N, 32, bits, stream=stream)
+                elif route == "compint8":
+                    qmm.qmm_gemm_compint8(A, B, sc, zp, None, Y, M, c.K, c.N, 32, bits, ws, 4,
+                                          stream)
+                else:
+                    qmm.qmm_gemm_int16(A, B, sc, zp, None, Y, M, c.K, c.N, 32, bits, ws, stream)
+
+            for i in range(3):
+                run(i)
+            torch.cuda.synchronize()
+            ms = _time_launches(run, max(10, args.steps // 4), stream)
+            byts = nbytes + A.numel() * 2 + M * c.N * 2
+            res[f"b{bits}_{route}_M{M}"] = {
+                "us": round(ms * 1e3, 2), "bytes": byts,
+                "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del pool
     return res
 
 

@@ -21,8 +21,11 @@
 // Work split: a workgroup of 4 waves owns 4 * R output columns; a wave walks
 // the blocks of its R columns with one lane per block (lanes stride over the
 // row's blocks), so each block's sum is formed in one lane and scaled once.
-// The activations of MT rows are staged in LDS per chunk of whole blocks
-// (fp32 values, or the int8 / int16 codes widened to int32).
+// The activations of MT rows (MT = 1 for a single row) are staged in LDS per
+// chunk of up to 64 whole blocks (fp32 values, or the int8 / int16 codes
+// widened to int32), each block followed by one pad word: lane l reads block
+// l of the chunk at a stride of bs + 1 words, an odd stride, so the 64 lanes
+// of a read hit 64 different banks.
 #include <algorithm>
 
 #include "qmm_device.h"
@@ -33,7 +36,7 @@ namespace qmm {
 namespace {
 
 enum : int { ACT_F = 0, ACT_I8 = 1, ACT_I16 = 2 };
-constexpr int GN_R = 2;          // output columns per wave
+constexpr int GN_R = 4;          // output columns per wave
 
 // 16 codes of a block, starting at code i0 (a multiple of 16) of the block
 // whose blob starts at `blk` (bs codes).
@@ -41,11 +44,10 @@ template <int BITS>
 __device__ __forceinline__ void codes16(const uint8_t* __restrict__ blk, int bs, int i0,
                                         int (&c)[16]) {
   if constexpr (BITS == 3) {
-    const uint8_t* lo = blk + i0 / 4;            // 4 bytes, 2 bits per code
-    const uint8_t* hi = blk + bs / 4 + i0 / 8;   // 2 bytes, 1 bit per code
-    const uint32_t l = (uint32_t)lo[0] | ((uint32_t)lo[1] << 8) | ((uint32_t)lo[2] << 16) |
-                       ((uint32_t)lo[3] << 24);
-    const uint32_t h = (uint32_t)hi[0] | ((uint32_t)hi[1] << 8);
+    // A blob of 3 bs / 8 bytes is even-sized, so both planes are 2-aligned.
+    const uint16_t* lo = reinterpret_cast<const uint16_t*>(blk + i0 / 4);  // 2 bits per code
+    const uint32_t l = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+    const uint32_t h = *reinterpret_cast<const uint16_t*>(blk + bs / 4 + i0 / 8);  // 1 bit
 #pragma unroll
     for (int j = 0; j < 16; ++j) c[j] = (int)(((l >> (2 * j)) & 3u) | (((h >> j) & 1u) << 2));
   } else {
@@ -80,10 +82,12 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
     int32_t* __restrict__ dots, int Mp, int M, int K, int N, int bs, int kb, int blob,
     int zp_row_bytes, int chunk_blocks) {
   extern __shared__ float gn_lds[];
-  float* xs = gn_lds;                                        // [MT][chunk] fp32 (ACT_F)
-  int* qs = reinterpret_cast<int*>(gn_lds);                  // [MT][chunk] int32 (ACT_I*)
+  float* xs = gn_lds;                                        // [MT][chunk_p] fp32 (ACT_F)
+  int* qs = reinterpret_cast<int*>(gn_lds);                  // [MT][chunk_p] int32 (ACT_I*)
   using XT = typename dt<XDT>::T;
   const int chunk = chunk_blocks * bs;
+  const int chunk_p = chunk_blocks * (bs + 1);               // one pad word per block
+  const int bs_log2 = __builtin_ctz(bs);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = (blockIdx.x * 4 + wave) * GN_R;
@@ -99,13 +103,14 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
     __syncthreads();
     for (int t = threadIdx.x; t < MT * chunk; t += 256) {
       const int m = t / chunk, e = t % chunk, k = k0 + e;
+      const int at = m * chunk_p + e + (e >> bs_log2);
       if constexpr (ACT == ACT_F) {
-        xs[t] = (m < Mp && k < K) ? dt<XDT>::to_f32(reinterpret_cast<const XT*>(A)[(int64_t)m * K + k])
-                                  : 0.0f;
+        xs[at] = (m < Mp && k < K) ? dt<XDT>::to_f32(reinterpret_cast<const XT*>(A)[(int64_t)m * K + k])
+                                   : 0.0f;
       } else if constexpr (ACT == ACT_I8) {
-        qs[t] = (m < Mp && k < padded) ? (int)reinterpret_cast<const int8_t*>(qa)[m * padded + k] : 0;
+        qs[at] = (m < Mp && k < padded) ? (int)reinterpret_cast<const int8_t*>(qa)[m * padded + k] : 0;
       } else {
-        qs[t] = (m < Mp && k < padded) ? (int)reinterpret_cast<const int16_t*>(qa)[m * padded + k] : 0;
+        qs[at] = (m < Mp && k < padded) ? (int)reinterpret_cast<const int16_t*>(qa)[m * padded + k] : 0;
       }
     }
     __syncthreads();
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
           df[m] = 0.0f;
           di[m] = 0;
         }
-        const int e0 = (b - b0) * bs;
+        const int e0 = (b - b0) * (bs + 1);
         for (int i0 = 0; i0 < bs; i0 += 16) {
           int c[16];
           codes16<BITS>(blk, bs, i0, c);
@@ -134,8 +139,8 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
             const int w = c[j] - z;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-              if constexpr (ACT == ACT_F) df[m] = fmaf(xs[m * chunk + e0 + i0 + j], (float)w, df[m]);
-              else di[m] += qs[m * chunk + e0 + i0 + j] * w;
+              if constexpr (ACT == ACT_F) df[m] = fmaf(xs[m * chunk_p + e0 + i0 + j], (float)w, df[m]);
+              else di[m] += qs[m * chunk_p + e0 + i0 + j] * w;
             }
           }
         }
@@ -171,13 +176,14 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
 
 int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
 
-template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS>
-hipError_t launch_gn_t(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
-  constexpr int MT = 4;
+template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS, int MT>
+hipError_t launch_gn_m(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
   using ST = typename dt<SDT>::T;
-  // Whole blocks per staged chunk: at least one, about 2048 activations.
-  const int chunk_blocks = (int)std::max<int64_t>(1, 2048 / a.block_size);
-  const size_t lds = (size_t)MT * chunk_blocks * a.block_size * 4;
+  // Whole blocks per staged chunk: one per lane (64) where that fits in about
+  // 40 KiB of LDS, else fewer, at least one.
+  const int64_t per_block = (int64_t)MT * (a.block_size + 1) * 4;
+  const int chunk_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(64, 40960 / per_block));
+  const size_t lds = (size_t)(chunk_blocks * per_block);
   auto kern = generic_rows_kernel<ACT, BITS, XDT, SDT, HAS_ZP, MT, DOTS>;
   if (lds > 64 * 1024) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
@@ -201,6 +207,12 @@ hipError_t launch_gn_t(const MatArgs& a, const void* qa, const float* sa, int32_
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS>
+hipError_t launch_gn_t(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  return a.M == 1 ? launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 1>(a, qa, sa, dots)
+                  : launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 4>(a, qa, sa, dots);
 }
 
 template <int ACT, int BITS, int XDT, bool DOTS>
