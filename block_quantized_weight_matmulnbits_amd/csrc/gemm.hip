@@ -124,7 +124,7 @@ __device__ __forceinline__ void word_codes_f32(uint32_t w, float* q) {
 // outputs as 4 x TN v_mfma_f32_16x16x32 tiles.
 // Per K-step of GBK = 64: thread t dequantizes 32 codes of column t >> 1
 // (half t & 1 of the step); threads t >= 2 * BN only copy A.
-// Pipeline: A chunks are prefetched into registers one step ahead, the codes,
+// Pipeline: A tiles are loaded into LDS one step ahead, the codes,
 // scales and zero points two steps ahead (register stage = step parity, fixed
 // at compile time by unrolling the loop by two); the next step is written to
 // the other LDS buffer, after this step's MFMAs by waves 0-3 and (its B tile)
@@ -223,20 +223,28 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   const int zb_stride = TL ? TG * BITS : BITS;
 
   // Register stages.
-  u32x4 av[4];                       // A chunks of the next step
   uint32_t cw[2][WPT];               // codes, two steps
   ST scr[2][2];                      // scales of the (at most 2) blocks of 32 codes
   uint32_t sc8[2][2];                // WF: their scale bytes
   uint32_t zbr[2][2];                // zero-point bytes of those blocks
 
-  auto load_a = [&](int k0) {
+  // The A tile goes from memory straight into LDS buffer buf (buffer loads
+  // with the LDS flag, no registers, no LDS write instructions): load i of
+  // wave w fills the 1 KiB of LDS rows 8 q .. 8 q + 7, q = 8 i + w, one
+  // 16-byte piece per lane at offset 16 * lane.  The slot a lane fills is
+  // fixed, so the lane fetches the piece lds_at places there: piece
+  // (lane & 7) ^ f of row 8 q + lane / 8, where f, that row's XOR, depends only
+  // on the wave's parity and the lane.
+  const int a_rw = 8 * wave + (lane >> 3);
+  const int a_k = ((lane & 7) ^ (((a_rw >> 1) & 7) ^ ((a_rw & 1) << 2))) * 8;
+  auto load_a = [&](int k0, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * GEMM_TPB;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      const int row = m0 + r, k = k0 + kc;
-      const bool ok = row < M && k < K;    // K % 8 == 0: a chunk is all in or all out
-      av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (row * K + k) * 2 : OOB, 0, 0);
+      const int row = m0 + 64 * i + a_rw, k = k0 + a_k;
+      const bool ok = row < M && k < K;    // K % 8 == 0: a piece is all in or all out
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(As + buf * STAGE + (8 * i + wave) * 512),
+          16, ok ? (row * K + k) * 2 : OOB, 0, 0, 0);
     }
   };
   // Codes past the row's last block (k0 + 64 > kb * bs) come from the next
@@ -284,15 +292,6 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
       if constexpr (HAS_ZP)
         zbr[st][i] = __builtin_amdgcn_raw_buffer_load_b8(
             rzp, ncol_ok ? (col_zb0 + b * zb_stride) >> 3 : OOB, 0, 0);
-    }
-  };
-  auto store_a = [&](int buf) {
-    uint16_t* as = As + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * GEMM_TPB;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&as[lds_at(r, kc >> 3)]) = av[i];
     }
   };
   // Dequantize register stage `st` (step starting at k0) into LDS buffer buf.
@@ -413,6 +412,9 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   auto mfma_step = [&](int buf) {
     const uint16_t* as = As + buf * STAGE;
     const uint16_t* bs = Bs + buf * STAGE;
+    // Raised priority while this wave feeds the matrix cores: the other wave
+    // of its SIMD, dequantizing, takes the issue slots the MFMAs leave.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 32) {
       typename Op::V af[TM];
@@ -428,6 +430,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
         for (int i = 0; i < TM; ++i) acc[i][j] = Op::run(af[i], bf, acc[i][j]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // One pipelined step s (register stage and LDS buffer = s & 1 = ST).
   // Waves are placed on the four SIMDs round robin, so waves w and w + 4
@@ -435,29 +438,26 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   // dequantization, the other four after it, so on each SIMD one wave's
   // vector work overlaps the other's matrix work (measured: 0.298 -> 0.280 ms
   // on the tiled layout; pairing odd with even waves instead gives 0.286).
-  // The A copy comes after the MFMAs in both orders: its loads were issued
-  // at the start of the step and need the time to arrive.
+  // The next A tile is loaded into the other LDS buffer at the start of the
+  // step; the barrier at its end waits for those loads.
   auto step = [&](int s, auto st_tag, auto deq_first) {
     constexpr int ST_ = decltype(st_tag)::value;
-    load_a((s + 1) * GBK);
+    load_a((s + 1) * GBK, ST_ ^ 1);
     load_b((s + 2) * GBK, ST_);
     if constexpr (decltype(deq_first)::value) {
       store_b((s + 1) * GBK, ST_ ^ 1, ST_ ^ 1);
       mfma_step(ST_);
-      store_a(ST_ ^ 1);
     } else {
       mfma_step(ST_);
-      store_a(ST_ ^ 1);
       store_b((s + 1) * GBK, ST_ ^ 1, ST_ ^ 1);
     }
     __syncthreads();
   };
 
   const int nsteps = (K + GBK - 1) / GBK;
-  load_a(0);
+  load_a(0, 0);
   load_b(0, 0);
   load_b(GBK, 1);
-  store_a(0);
   store_b(0, 0, 0);
   __syncthreads();
   // The two orders are two copies of the loop (one wave-uniform branch

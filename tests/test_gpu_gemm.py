@@ -108,6 +108,21 @@ def test_224_column_tiles_ragged():
         assert torch.equal(run_gemm_tiled(case), y), ("tiled", M, K, N)
 
 
+@pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_large_m_ragged(a_dtype, bits, bs):
+    """M >= 1024 (several rounds of 256-row tiles, a partial last tile):
+    exact data bit for bit on both layouts, with ragged N and K (K % 64 != 0)."""
+    for i, (M, K, N) in enumerate([(1024, 200, 224), (1100, 264, 300), (1537, 1000, 112)]):
+        case = exact_case(M, K, N, bs, bits, a_dtype, seed=3000 + 10 * bits + bs + i)
+        print(f"[gemm large-M exact] M={M} K={K} N={N} bs={bs} bits={bits} a={a_dtype}", flush=True)
+        Y, _ = oracle_matmul(case)
+        expect = torch.from_numpy(Y).to(case.A.dtype)
+        assert torch.equal(run_gemm(case).cpu(), expect), (M, K, N)
+        assert torch.equal(run_gemm_tiled(case).cpu(), expect), ("tiled", M, K, N)
+
+
 def test_prefill_workload_sampled_rows():
     """Full prefill shape; the oracle computes every output of 48 sampled rows
     (each over the full K and N)."""
