@@ -412,9 +412,6 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   auto mfma_step = [&](int buf) {
     const uint16_t* as = As + buf * STAGE;
     const uint16_t* bs = Bs + buf * STAGE;
-    // Raised priority while this wave feeds the matrix cores: the other wave
-    // of its SIMD, dequantizing, takes the issue slots the MFMAs leave.
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 32) {
       typename Op::V af[TM];
@@ -430,7 +427,6 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
         for (int i = 0; i < TM; ++i) acc[i][j] = Op::run(af[i], bf, acc[i][j]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
   };
   // One pipelined step s (register stage and LDS buffer = s & 1 = ST).
   // Waves are placed on the four SIMDs round robin, so waves w and w + 4
