@@ -572,7 +572,7 @@ def bench_prefill(qmm, dev, stream, args):
         for i in range(3):
             run(i)
         torch.cuda.synchronize()
-        ms = _time_launches(run, max(5, args.steps // 20), stream)
+        ms = _time_launches(run, max(20, args.steps // 5), stream)
         tflops = flop / (ms * 1e-3) / 1e12
         res[name] = {"ms": round(ms, 4), "tflops": round(tflops, 2),
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
@@ -650,7 +650,7 @@ def bench_fp4(qmm, dev, stream, args):
         for i in range(3):
             runp(i)
         torch.cuda.synchronize()
-        msp = _time_launches(runp, max(5, args.steps // 20), stream)
+        msp = _time_launches(runp, max(20, args.steps // 5), stream)
         flop = 2.0 * p.M * p.N * p.K
         res[fmt] = {
             "gemv_K4096_N14336": {"us": round(ms * 1e3, 3), "bytes": nbytes,
