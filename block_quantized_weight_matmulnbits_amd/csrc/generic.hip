@@ -59,6 +59,55 @@ __device__ __forceinline__ void codes16(const uint8_t* __restrict__ blk, int bs,
   }
 }
 
+// The raw 32-bit words of 16 codes (starting at code i0, a multiple of 16)
+// of the block whose blob starts at blk: 3-bit: the 2-bit plane's word and
+// the 1-bit plane's 16 bits; otherwise 16 * BITS / 32 code words.
+template <int BITS>
+struct Raw16 {
+  static constexpr int W = BITS == 3 ? 2 : 16 * BITS / 32;
+};
+template <int BITS>
+__device__ __forceinline__ void load_raw16(const uint8_t* __restrict__ blk, int bs, int i0,
+                                           uint32_t (&w)[Raw16<BITS>::W]) {
+  if constexpr (BITS == 3) {
+    const uint16_t* lo = reinterpret_cast<const uint16_t*>(blk + i0 / 4);
+    w[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+    w[1] = *reinterpret_cast<const uint16_t*>(blk + bs / 4 + i0 / 8);
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + i0 * BITS / 8);
+#pragma unroll
+    for (int i = 0; i < Raw16<BITS>::W; ++i) w[i] = p[i];
+  }
+}
+template <int BITS>
+__device__ __forceinline__ void decode16(const uint32_t (&w)[Raw16<BITS>::W], int (&c)[16]) {
+  if constexpr (BITS == 3) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      c[j] = (int)(((w[0] >> (2 * j)) & 3u) | (((w[1] >> j) & 1u) << 2));
+  } else {
+    constexpr int P = 32 / BITS;
+    constexpr uint32_t m = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[j] = (int)((w[j / P] >> ((j % P) * BITS)) & m);
+  }
+}
+
+// Zero point of block b of a packed zero-point row of row_bytes bytes,
+// without a branch: both bytes a 3-bit value can touch are read (the second
+// clamped into the row).
+template <int BITS, bool HAS_ZP>
+__device__ __forceinline__ int zero_point2(const uint8_t* __restrict__ zrow, int b, int row_bytes) {
+  if constexpr (!HAS_ZP) {
+    return 1 << (BITS - 1);
+  } else {
+    constexpr uint32_t m = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+    const int bit = b * BITS, i = bit >> 3;
+    const uint32_t v = (uint32_t)zrow[i] | ((uint32_t)zrow[min(i + 1, row_bytes - 1)] << 8);
+    return (int)((v >> (bit & 7)) & m);
+  }
+}
+
 // Zero point of block b from a packed zero-point row (LSB-first stream; a
 // 3-bit value may continue into the next byte).
 template <int BITS, bool HAS_ZP>
@@ -174,7 +223,193 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Unit form (blocks of at most 512 codes): lane l of a wave takes unit
+// (16 codes) u0 + l of each of the wave's GU_R columns, so a wave covers 1024
+// codes of a column per pass and every lane is busy whatever the block size.
+// Each lane reads its unit's activations of MT rows straight from memory
+// (16-byte loads; the vector stays in the caches): no staging, no barrier.  Per code: (code - zp) as an integer, then
+// an fp32 FMA with the activation (float) or an integer multiply-add (int).
+// Float: each unit's sum is scaled by its block's scale.  Integer: the
+// block's UB = bs / 16 lanes (aligned, adjacent) add their exact int32 sums
+// by XOR shuffles, and the first lane scales the block dot once.
+// ---------------------------------------------------------------------------
+constexpr int GU_R = 2;            // columns per wave
+constexpr int GU_MAX_BS = 512;     // a block spans at most 32 lanes
+
+template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, int MT, bool DOTS>
+__global__ __launch_bounds__(256) void generic_unit_kernel(
+    const void* __restrict__ A, const void* __restrict__ qa, const float* __restrict__ sa,
+    const uint8_t* __restrict__ B, const typename dt<SDT>::T* __restrict__ scales,
+    const uint8_t* __restrict__ zp, const void* __restrict__ bias, void* __restrict__ Y,
+    int32_t* __restrict__ dots, int Mp, int K, int N, int bs, int kb, int blob,
+    int zp_row_bytes) {
+  using XT = typename dt<XDT>::T;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = (blockIdx.x * 4 + wave) * GU_R;
+  const int ub_log2 = __builtin_ctz(bs) - 4;           // units per block, log2
+  const int units = kb << ub_log2;                      // units per column
+  const int64_t padded = (int64_t)kb * bs;
+  // 16-byte activation loads: float rows whose units are wholly inside or
+  // wholly past K and 16-byte aligned; the quantized rows always are (padded
+  // to whole blocks, 256-byte aligned).
+  const bool vec = ACT != ACT_F || ((K % 16) == 0 && (((uintptr_t)A) & 15) == 0);
+  float acc[GU_R][MT];
+#pragma unroll
+  for (int r = 0; r < GU_R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  // Units start at multiples of 64 per pass, so the lanes of one block are
+  // aligned and adjacent.
+  for (int ub = 0; ub < units; ub += 64) {
+    {
+      const int u = ub + lane;
+      const bool live = u < units;
+      const int uc = live ? u : 0;                      // in-bounds stand-in
+      const int b = uc >> ub_log2, ui = uc & ((1 << ub_log2) - 1);
+      const int64_t k0 = (int64_t)uc * 16;
+      // This unit's activations of the MT rows (rows past Mp read row 0 and
+      // are discarded), read straight from memory: the vector is small and
+      // stays in the caches, so there is no staging and no barrier.
+      float xf[MT][16];
+      int xi[MT][16];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int64_t mr = m < Mp ? m : 0;
+        if constexpr (ACT == ACT_F) {
+          if (vec) {
+            const bool in = k0 < K;
+            const XT* xr = reinterpret_cast<const XT*>(A) + mr * K + (in ? k0 : 0);
+            if constexpr (sizeof(XT) == 4) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const u32x4 w = reinterpret_cast<const u32x4*>(xr)[v];
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xf[m][4 * v + j] = in ? __uint_as_float(ww[j]) : 0.0f;
+              }
+            } else {
+#pragma unroll
+              for (int v = 0; v < 2; ++v) {
+                const u32x4 w = reinterpret_cast<const u32x4*>(xr)[v];
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                  xf[m][8 * v + j] = in ? dt<XDT>::to_f32(__builtin_bit_cast(
+                                              XT, (uint16_t)(ww[j / 2] >> (16 * (j & 1)))))
+                                        : 0.0f;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int64_t k = k0 + j;
+              xf[m][j] = k < K ? dt<XDT>::to_f32(reinterpret_cast<const XT*>(A)[mr * K + k]) : 0.0f;
+            }
+          }
+        } else if constexpr (ACT == ACT_I8) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const int8_t*>(qa) + mr * padded + k0);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) xi[m][j] = (int)(int8_t)(ww[j / 4] >> (8 * (j & 3)));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(
+                reinterpret_cast<const int16_t*>(qa) + mr * padded + k0)[v];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xi[m][8 * v + j] = (int)(int16_t)(ww[j / 2] >> (16 * (j & 1)));
+          }
+        }
+      }
+      // Every column's loads first (a column past N reads column N - 1 and
+      // is discarded), so that they are in flight together.
+      uint32_t raw[GU_R][Raw16<BITS>::W];
+      int zr[GU_R];
+      float sr[GU_R];
+#pragma unroll
+      for (int r = 0; r < GU_R; ++r) {
+        const int64_t nc = min(n0 + r, N - 1);
+        load_raw16<BITS>(B + (nc * kb + b) * blob, bs, ui * 16, raw[r]);
+        zr[r] = zero_point2<BITS, HAS_ZP>(zp + nc * zp_row_bytes, b, zp_row_bytes);
+        sr[r] = dt<SDT>::to_f32(scales[nc * kb + b]);
+      }
+#pragma unroll
+      for (int r = 0; r < GU_R; ++r) {
+        const int n = n0 + r;
+        if (n >= N) continue;                           // wave-uniform
+        int c[16];
+        decode16<BITS>(raw[r], c);
+        const int z = zr[r];
+        const float s = sr[r];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if constexpr (ACT == ACT_F) {
+            float d = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) d = fmaf(xf[m][j], (float)(c[j] - z), d);
+            acc[r][m] = fmaf(live ? d : 0.0f, s, acc[r][m]);
+          } else {
+            int d = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) d += xi[m][j] * (c[j] - z);
+            d = live ? d : 0;
+            for (int o = 1; o < (1 << ub_log2); o <<= 1) d += __shfl_xor(d, o);
+            if (live && ui == 0) {
+              if constexpr (DOTS) {
+                if (m < Mp) dots[((int64_t)m * N + n) * kb + b] = d;
+              }
+              const float sab = m < Mp ? sa[(int64_t)m * kb + b] : 0.0f;
+              acc[r][m] = fmaf((float)d, sab * s, acc[r][m]);
+            }
+          }
+        }
+      }
+    }
+  }
+  if constexpr (DOTS) return;
+#pragma unroll
+  for (int r = 0; r < GU_R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float v = wave_sum(acc[r][m]);
+      const int n = n0 + r;
+      if (lane == 0 && n < N && m < Mp) {
+        float o = v;
+        if (bias) o += dt<XDT>::to_f32(reinterpret_cast<const XT*>(bias)[n]);
+        reinterpret_cast<XT*>(Y)[(int64_t)m * N + n] = dt<XDT>::from_f32(o);
+      }
+    }
+}
+
 int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS, int MT>
+hipError_t launch_gu_m(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  using ST = typename dt<SDT>::T;
+  const int grid = (int)((a.N + 4 * GU_R - 1) / (4 * GU_R));
+  const int64_t padded = a.kb * a.block_size;
+  const int qb = ACT == ACT_I16 ? 2 : 1;
+  for (int64_t m0 = 0; m0 < a.M; m0 += MT) {
+    const int Mp = (int)std::min<int64_t>(MT, a.M - m0);
+    hipLaunchKernelGGL((generic_unit_kernel<ACT, BITS, XDT, SDT, HAS_ZP, MT, DOTS>), dim3(grid),
+                       dim3(256), 0, a.stream,
+                       ACT == ACT_F ? (const void*)((const char*)a.A + m0 * a.K * dtype_bytes(a.a_dtype))
+                                    : a.A,
+                       qa ? (const void*)((const char*)qa + m0 * padded * qb) : nullptr,
+                       sa ? sa + m0 * a.kb : nullptr, a.B, (const ST*)a.scales, a.zp, a.bias,
+                       DOTS ? nullptr : (void*)((char*)a.Y + m0 * a.N * dtype_bytes(a.a_dtype)),
+                       DOTS ? dots + m0 * a.N * a.kb : nullptr, Mp, (int)a.K, (int)a.N,
+                       (int)a.block_size, (int)a.kb, (int)a.blob, (int)a.zp_row_bytes);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS, int MT>
 hipError_t launch_gn_m(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
@@ -211,6 +446,9 @@ hipError_t launch_gn_m(const MatArgs& a, const void* qa, const float* sa, int32_
 
 template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS>
 hipError_t launch_gn_t(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
+  if (a.block_size <= GU_MAX_BS)
+    return a.M == 1 ? launch_gu_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 1>(a, qa, sa, dots)
+                    : launch_gu_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 4>(a, qa, sa, dots);
   return a.M == 1 ? launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 1>(a, qa, sa, dots)
                   : launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 4>(a, qa, sa, dots);
 }
