@@ -717,6 +717,20 @@ def bench_lowbit(qmm, dev, stream, args):
                 "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del pool
+    # 3-bit prefill on the matrix cores (operator layout).
+    c = make_matmul_case(2048, 4096, 14336, 32, 3, a_dtype="bf16", has_zp=True, seed=63).to(dev)
+    Y = torch.empty(c.M, c.N, dtype=torch.bfloat16, device=dev)
+
+    def runp(_):
+        qmm.qmm_gemm(c.A, c.B, c.scales, c.zero_points, None, Y, c.M, c.K, c.N, 32, 3, 0, stream)
+
+    for i in range(3):
+        runp(i)
+    torch.cuda.synchronize()
+    ms = _time_launches(runp, max(20, args.steps // 5), stream)
+    flop = 2.0 * c.M * c.N * c.K
+    res["b3_prefill_M2048"] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                               "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     return res
 
 

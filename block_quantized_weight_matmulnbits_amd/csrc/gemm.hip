@@ -157,9 +157,12 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int BN = 32 * TN;
-  constexpr int P = 32 / BITS;                 // codes per 32-bit word
+  static_assert(BITS != 3 || (!TL && !GI && !WF), "3-bit weights: operator layout");
+  constexpr int P = BITS == 3 ? 8 : 32 / BITS; // codes per 32-bit word (3-bit: unused)
   constexpr int HK = GBK / 2;                  // codes per thread per K-step
-  constexpr int WPT = HK / P;                  // code words per thread per K-step
+  // Code words per thread per K-step; 3-bit: the 32 codes' 2-bit plane (two
+  // words) and 1-bit plane (one word).
+  constexpr int WPT = BITS == 3 ? 3 : HK / P;
   constexpr int TM = 4;                        // MFMA row tiles per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_g[];
   uint16_t* As = lds_g;                        // [2][GBM][LDS_ROW], pieces per lds_at
@@ -189,7 +192,9 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   //   tiled layout (qmm_layout.h): codes at ((g * chunks + c) * 32 + i) *
   //     chunk_bytes + half; scale at (g * kb + b) * 32 + i; zero point at bit
   //     ((g * kb + b) * 32 + i) * bits, with n = 32 g + i and c = k / 64.
-  const int row_bytes = kb << log2_blob;
+  // Row length of the operator layout (3-bit blobs, 3 bs / 8 bytes, are not
+  // powers of two).
+  const int row_bytes = BITS == 3 ? kb * (3 << log2_bs) / 8 : kb << log2_blob;
   constexpr int CHUNK_BYTES = TKC * BITS / 8;
   const bool dq = tid < 2 * BN;                // this thread dequantizes
   const int bcol = tid >> 1;
@@ -253,7 +258,36 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   auto load_b = [&](int k0, int st) {
     const int kt = k0 + khalf;
     const int byte0 = col_code0 + (k0 >> 6) * code_step;
-    if constexpr (GI) {
+    if constexpr (BITS == 3) {
+      // Operator layout, blob of 3 bs / 8 bytes per block: the 2-bit plane
+      // (bs / 4 bytes) then the 1-bit plane (bs / 8 bytes).  bs >= 32: this
+      // thread's 32 codes are 8 bytes of the first plane and 4 of the second
+      // of one block (4-aligned: blobs of 12 bytes or more); bs = 16: two
+      // whole blocks, 12 contiguous bytes.  Past the row's last block the
+      // bytes belong to the next row or lie past the matrix (zeros); they
+      // meet zero activations.
+      const int bsz = 1 << log2_bs;
+      const int rb = ncol_ok ? ncol * row_bytes : 0;
+      const int base = rb + (kt >> log2_bs) * (3 * bsz / 8);
+      if (bsz >= 32) {
+        const int i0 = kt & (bsz - 1);
+        const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rbc, ncol_ok ? base + i0 / 4 : OOB, 0, 0);
+        cw[st][0] = lo.x;
+        cw[st][1] = lo.y;
+        cw[st][2] = __builtin_amdgcn_raw_buffer_load_b32(rbc, ncol_ok ? base + bsz / 4 + i0 / 8 : OOB,
+                                                         0, 0);
+      } else {
+        // [lo0 4 B][hi0 2 B][lo1 4 B][hi1 2 B], 2-aligned only (rows of
+        // 6 kb bytes): six 16-bit loads.
+        uint32_t h[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+          h[i] = __builtin_amdgcn_raw_buffer_load_b16(rbc, ncol_ok ? base + 2 * i : OOB, 0, 0);
+        cw[st][0] = h[0] | (h[1] << 16);
+        cw[st][1] = h[3] | (h[4] << 16);
+        cw[st][2] = h[2] | (h[5] << 16);
+      }
+    } else if constexpr (GI) {
       // Codes only; the scales and zero points are looked up per code when
       // the step is dequantized.
       if constexpr (WPT >= 4) {
@@ -267,8 +301,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
         cw[st][0] = t.x; cw[st][1] = t.y;
       }
       return;
-    }
-    if constexpr (WPT >= 4) {
+    } else if constexpr (WPT >= 4) {
 #pragma unroll
       for (int w = 0; w < WPT; w += 4) {
         const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rbc, byte0 + 4 * w, 0, 0);
@@ -289,9 +322,14 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
         scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b32(rsc, si * 4, 0, 0));
       else
         scr[st][i] = __builtin_bit_cast(ST, __builtin_amdgcn_raw_buffer_load_b16(rsc, si * 2, 0, 0));
-      if constexpr (HAS_ZP)
-        zbr[st][i] = __builtin_amdgcn_raw_buffer_load_b8(
-            rzp, ncol_ok ? (col_zb0 + b * zb_stride) >> 3 : OOB, 0, 0);
+      if constexpr (HAS_ZP) {
+        const int zo = ncol_ok ? (col_zb0 + b * zb_stride) >> 3 : OOB;
+        zbr[st][i] = __builtin_amdgcn_raw_buffer_load_b8(rzp, zo, 0, 0);
+        // A 3-bit zero point may continue into the next byte (read past the
+        // zero-point rows as zero).
+        if constexpr (BITS == 3)
+          zbr[st][i] |= __builtin_amdgcn_raw_buffer_load_b8(rzp, ncol_ok ? zo + 1 : OOB, 0, 0) << 8;
+      }
     }
   };
   // Dequantize register stage `st` (step starting at k0) into LDS buffer buf.
@@ -363,6 +401,28 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
       zs[i] = (float)z * sf[i];
     }
     uint32_t pk[HK / 2];
+    if constexpr (BITS == 3) {
+      // Code j = 2-bit plane bits 2 (j % 16) of word j / 16, plus bit j of the
+      // 1-bit plane times 4; codes 16..31 lie in the second block when bs = 16.
+      const bool two = (1 << log2_bs) < HK;
+#pragma unroll
+      for (int j = 0; j < HK; j += 2) {
+        const int bi = (two && j >= 16) ? 1 : 0;
+        const float s = bi ? sf[1] : sf[0], z = bi ? zs[1] : zs[0];
+        float q[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int jj = j + t;
+          q[t] = (float)(((cw[st][jj / 16] >> (2 * (jj % 16))) & 3u) | (((cw[st][2] >> jj) & 1u) << 2));
+        }
+        pk[j / 2] = Op::pack(fmaf(q[0], s, -z), fmaf(q[1], s, -z));
+      }
+#pragma unroll
+      for (int j = 0; j < HK / 8; ++j)
+        *reinterpret_cast<u32x4*>(&bs[lds_at(bcol, (khalf >> 3) + j)]) =
+            u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
+      return;
+    }
     // (q - z) * s = q * s - z * s: for 16-bit scales both products are
     // exact and so is the difference; one rounding to the activation dtype.
     auto dequant_word = [&](int w, float s, float z) {
@@ -635,10 +695,15 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
       const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + bn - 1) / bn);
       constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);   // double-buffered A and B
       decltype(&gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>) kern;
-      if (a.tiled) kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, true>
-                               : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, true>;
-      else kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, false>
-                       : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>;
+      if constexpr (BITS == 3) {
+        kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, false>
+                    : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>;
+      } else {
+        if (a.tiled) kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, true>
+                                 : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, true>;
+        else kern = n224 ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 7, false>
+                         : gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false>;
+      }
       const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
@@ -649,7 +714,8 @@ static hipError_t launch_gemm_t(const MatArgs& a) {
       return hipGetLastError();
     }
   }
-  return launch_rows<BITS, XDT, SDT, HAS_ZP>(a);
+  if constexpr (BITS == 3) return launch_generic_float(a);
+  else return launch_rows<BITS, XDT, SDT, HAS_ZP>(a);
 }
 
 template <int BITS, int XDT, int SDT>
@@ -760,9 +826,9 @@ hipError_t launch_gemm_mfma_gidx(const MatArgs& a) {
 
 hipError_t launch_gemm(const MatArgs& a) {
   if (a.g_idx) return launch_gidx(a);
-  if (a.bits == 3) return launch_generic_float(a);
   switch (a.bits) {
     case 2: return launch_gemm_x<2>(a);
+    case 3: return launch_gemm_x<3>(a);
     case 4: return launch_gemm_x<4>(a);
     default: return launch_gemm_x<8>(a);
   }

@@ -8,7 +8,9 @@ their scales and its int32 block dots (qmm_debug_compint8_block_dots).
 Within tol * S of the oracle: qmm_gemv (M = 1) and qmm_gemm for every
 activation dtype, small and large blocks, ragged K and N, with and without
 zero points and bias; CompInt8's output against the oracle's CompInt8 value;
-and the decode projection 4096 x 14336 (block 32) strictly.
+the decode projection 4096 x 14336 (block 32) and sampled rows of the
+M = 2048 prefill shape strictly.  The matrix-core GEMM (M > 16, 16-bit
+activations) on exact data bit for bit.
 """
 import numpy as np
 import pytest
@@ -75,6 +77,38 @@ def test_float_activations_within_tolerance(a_dtype, bs):
         Y, S = oracle_matmul(case)
         r = assert_within(gpu_float(case), Y, S, TOL[case.A.dtype], "bits3 float")
         print(f"  max |err|/S = {r:.3e}")
+
+
+@pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 1024])
+def test_matrix_core_gemm_exact_data(a_dtype, bs):
+    """M > 16 with 16-bit activations runs the matrix-core GEMM, which decodes
+    the two planes itself: small-integer activations and scale 0.25 make every
+    dequantized weight exact in bf16 / f16 and every sum exact in fp32, so the
+    result is the oracle's rounded once (ragged M, N, K % 64 != 0)."""
+    rng = np.random.default_rng(bs)
+    for i, (M, K, N) in enumerate([(17, 1032, 33), (300, 2056, 224), (1100, 264, 300)]):
+        K = max(K, bs)
+        case = case_of(M, K, N, bs, a_dtype=a_dtype, has_zp=(i != 1), has_bias=True, seed=70 + i)
+        case.A = torch.from_numpy(rng.integers(-3, 4, (M, K)).astype(np.float32)).to(case.A.dtype)
+        case.scales = torch.full_like(case.scales, 0.25)
+        case.bias = torch.from_numpy(rng.integers(-8, 9, N).astype(np.float32)).to(case.A.dtype)
+        print(f"[bits3 gemm exact] M={M} K={K} N={N} bs={bs} a={a_dtype}", flush=True)
+        Y, _ = oracle_matmul(case)
+        assert torch.equal(gpu_float(case).cpu(), torch.from_numpy(Y).to(case.A.dtype)), (M, K, N)
+
+
+def test_prefill_shape_sampled_rows():
+    """M = 2048, K = 4096, N = 14336, 3-bit block 32: every output of 32
+    sampled rows against the oracle, strictly."""
+    case = case_of(2048, 4096, 14336, 32, a_dtype="bf16", has_zp=True, seed=81)
+    y = gpu_float(case).cpu()
+    rows = np.random.default_rng(1).choice(2048, 32, replace=False)
+    rows[:2] = [0, 2047]
+    Y, S = oracle.matmul_nbits(f64(case.A)[rows], u8(case.B), f64(case.scales),
+                               u8(case.zero_points), None, case.N, case.K, 32, 3)
+    r = assert_within(y[rows], Y, S, TOL[torch.bfloat16], "bits3 prefill", strict=True)
+    print(f"  max |err|/S = {r:.3e}")
 
 
 def test_largest_block():
