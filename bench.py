@@ -671,7 +671,8 @@ def bench_lowbit(qmm, dev, stream, args):
     K=4096 N=14336, operator layout, bf16 activations: the float GEMV / GEMM
     (3-bit) at M in {1, 16}, CompInt8 (3-bit) and the int16 route (8-bit) at
     M in {1, 4, 16}.  Weights rotate through copies so each launch streams them
-    from HBM; times include the activation quantization."""
+    from HBM; times include the activation quantization.  Plus the 3-bit
+    prefill M=2048 on the matrix cores (TFLOP/s)."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
     res = {}
     for bits, route in ((3, "float"), (3, "compint8"), (8, "int16")):
