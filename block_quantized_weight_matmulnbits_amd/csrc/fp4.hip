@@ -17,10 +17,10 @@
 // global scale multiplies the result.
 //
 // fp4_gemv_kernel (M = 1): a wave owns R rows (output columns) and walks
-// each row in wave-wide 16-byte loads (1 KiB per load, contiguous); the
-// activations are staged in LDS per workgroup in pieces of 8192, and every
-// load of a piece (R rows x 4 per lane) is issued before the staging and in
-// flight before any is consumed.
+// each row in wave-wide 16-byte loads (1 KiB per load, contiguous); every
+// load of a piece (R rows x 2 per lane) is issued first, then each lane reads
+// its units' activations straight from memory (16-byte loads; the vector
+// stays in the caches, so there is no staging and no barrier).
 // A lane's 16 bytes are 32 codes: one MXFP4 block or two NVFP4 blocks.
 // fp4_rows_kernel (M > 1 without the matrix cores, or f32 activations): fp32
 // throughout, MT rows of A per pass.
@@ -36,7 +36,6 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int F4_R = 8;            // rows (output columns) per wave
 constexpr int F4_LPC = 2;          // 16-byte units per lane, row and piece
 constexpr int F4_CHUNK = 64 * F4_LPC * 32;   // activations staged per piece (4096)
 
@@ -78,6 +77,12 @@ __device__ __forceinline__ void fp4_dot32(const u32x4& v, const uint32_t* x, flo
   }
 }
 
+// Rows (output columns) per wave: fewer rows, more waves in flight (measured
+// on 4096 x 14336: MXFP4 8 -> 4 rows 11.0 -> 9.7 us, NVFP4 8 -> 2 rows
+// 13.1 -> 10.8 us, with its two scale bytes per unit).
+template <int FMT>
+constexpr int f4_rows() { return FMT == FP4_MX ? 4 : 2; }
+
 template <int XDT, int FMT>
 __global__ __launch_bounds__(256) void fp4_gemv_kernel(
     const void* __restrict__ x, const uint8_t* __restrict__ W, const uint8_t* __restrict__ scales,
@@ -85,41 +90,43 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(
     int kb) {
   constexpr int BS = FMT == FP4_MX ? 32 : 16;
   constexpr int XW = XDT == DT_F32 ? 32 : 16;          // 32-bit words of x per 32 codes
-  __shared__ uint32_t xs[F4_CHUNK / 32 * XW];
   using XT = typename dt<XDT>::T;
+  // 16-byte activation loads when every 32-code unit is wholly inside or
+  // wholly past K and x is 16-byte aligned.
+  const bool xvec = (K % 32) == 0 && (((uintptr_t)x) & 15) == 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = (blockIdx.x * 4 + wave) * F4_R;
+  const int n0 = (blockIdx.x * 4 + wave) * f4_rows<FMT>();
   const int row_bytes = kb * BS / 2;                    // a multiple of 8
   const int row_units = (row_bytes + 15) / 16;          // 16-byte units (the last may be half)
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)W, 0, N * row_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)scales, 0, N * kb, 0x00020000);
-  float acc[F4_R];
+  float acc[f4_rows<FMT>()];
 #pragma unroll
-  for (int r = 0; r < F4_R; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < f4_rows<FMT>(); ++r) acc[r] = 0.0f;
 
   for (int u0 = 0; u0 < row_units; u0 += F4_CHUNK / 32) {
-    // Every load of the piece in flight first (F4_R rows x F4_LPC units per
+    // Every load of the piece in flight first (the wave's rows x F4_LPC units per
     // lane, unit u0 + lane + 64 j; they do not depend on the staged
     // activations), then the activations staged.  Units past the row are
     // not loaded (a uniform skip when the whole wave is past it) or read
     // zeros through an out-of-range offset, and are not consumed.
-    u32x4 cv[F4_R][F4_LPC];
-    uint32_t sv[F4_R][F4_LPC], sv2[F4_R][F4_LPC];
+    u32x4 cv[f4_rows<FMT>()][F4_LPC];
+    uint32_t sv[f4_rows<FMT>()][F4_LPC], sv2[f4_rows<FMT>()][F4_LPC];
 #pragma unroll
     for (int j = 0; j < F4_LPC; ++j) {
       const int u = u0 + lane + 64 * j;
       const bool live = u < row_units;
 #pragma unroll
-      for (int r = 0; r < F4_R; ++r) {
+      for (int r = 0; r < f4_rows<FMT>(); ++r) {
         cv[r][j] = u32x4{0u, 0u, 0u, 0u};
         sv[r][j] = sv2[r][j] = 0u;
       }
       if (u0 + 64 * j >= row_units) continue;
 #pragma unroll
-      for (int r = 0; r < F4_R; ++r) {
+      for (int r = 0; r < f4_rows<FMT>(); ++r) {
         const int n = n0 + r;
         const bool ok = live && n < N;
         cv[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -131,30 +138,49 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(
           sv2[r][j] = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? sb + 1 : 0x7FFFFFF0, 0, 0);
       }
     }
-    // Stage the piece's activations (zero past K).
-    __syncthreads();
-    for (int t = threadIdx.x; t < F4_CHUNK / 32 * XW; t += 256) {
-      uint32_t v = 0;
-      if constexpr (XDT == DT_F32) {
-        const int k = u0 * 32 + t;
-        if (k < K) v = __float_as_uint(reinterpret_cast<const float*>(x)[k]);
+    // Each lane's activations for its units, read straight from memory (the
+    // vector stays in the caches; zero past K): no staging, no barrier.
+    uint32_t xv[F4_LPC][XW];
+#pragma unroll
+    for (int j = 0; j < F4_LPC; ++j) {
+      const int u = u0 + lane + 64 * j;
+      const int k0 = u * 32;
+      if (xvec) {
+        const bool in = k0 < K;
+        const u32x4* xp = reinterpret_cast<const u32x4*>(reinterpret_cast<const XT*>(x) + (in ? k0 : 0));
+#pragma unroll
+        for (int v = 0; v < XW / 4; ++v) {
+          const u32x4 t = xp[v];
+          xv[j][4 * v + 0] = in ? t.x : 0u;
+          xv[j][4 * v + 1] = in ? t.y : 0u;
+          xv[j][4 * v + 2] = in ? t.z : 0u;
+          xv[j][4 * v + 3] = in ? t.w : 0u;
+        }
       } else {
-        const int k = u0 * 32 + 2 * t;
-        const XT* xp = reinterpret_cast<const XT*>(x);
-        const uint32_t lo = k < K ? __builtin_bit_cast(uint16_t, xp[k]) : 0u;
-        const uint32_t hi = k + 1 < K ? __builtin_bit_cast(uint16_t, xp[k + 1]) : 0u;
-        v = lo | (hi << 16);
+#pragma unroll
+        for (int t = 0; t < XW; ++t) {
+          uint32_t v = 0;
+          if constexpr (XDT == DT_F32) {
+            const int k = k0 + t;
+            if (k < K) v = __float_as_uint(reinterpret_cast<const float*>(x)[k]);
+          } else {
+            const int k = k0 + 2 * t;
+            const XT* xp = reinterpret_cast<const XT*>(x);
+            const uint32_t lo = k < K ? __builtin_bit_cast(uint16_t, xp[k]) : 0u;
+            const uint32_t hi = k + 1 < K ? __builtin_bit_cast(uint16_t, xp[k + 1]) : 0u;
+            v = lo | (hi << 16);
+          }
+          xv[j][t] = v;
+        }
       }
-      xs[t] = v;
     }
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < F4_LPC; ++j) {
       const int u = u0 + lane + 64 * j;
       if (u >= row_units) break;
-      const uint32_t* xl = xs + (u - u0) * XW;
+      const uint32_t* xl = xv[j];
 #pragma unroll
-      for (int r = 0; r < F4_R; ++r) {
+      for (int r = 0; r < f4_rows<FMT>(); ++r) {
         float d[2];
         fp4_dot32<XDT>(cv[r][j], xl, d);
         if (FMT == FP4_MX) {
@@ -169,7 +195,7 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(
     }
   }
 #pragma unroll
-  for (int r = 0; r < F4_R; ++r) {
+  for (int r = 0; r < f4_rows<FMT>(); ++r) {
     const float v = wave_sum(acc[r]);
     const int n = n0 + r;
     if (lane == 0 && n < N) {
@@ -247,7 +273,7 @@ template <int XDT, int FMT>
 hipError_t launch_fp4_t(const Fp4Args& a) {
   using XT = typename dt<XDT>::T;
   if (a.M == 1) {
-    const int grid = (int)((a.N + 4 * F4_R - 1) / (4 * F4_R));
+    const int grid = (int)((a.N + 4 * f4_rows<FMT>() - 1) / (4 * f4_rows<FMT>()));
     hipLaunchKernelGGL((fp4_gemv_kernel<XDT, FMT>), dim3(grid), dim3(256), 0, a.stream, a.A, a.W,
                        a.scales, a.global_scale, a.bias, a.Y, (int)a.K, (int)a.N, (int)a.kb);
     return hipGetLastError();
