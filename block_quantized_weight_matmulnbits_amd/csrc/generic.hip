@@ -446,11 +446,13 @@ hipError_t launch_gn_m(const MatArgs& a, const void* qa, const float* sa, int32_
 
 template <int ACT, int BITS, int XDT, int SDT, bool HAS_ZP, bool DOTS>
 hipError_t launch_gn_t(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
-  if (a.block_size <= GU_MAX_BS)
+  if (ACT == ACT_I16 || a.block_size <= GU_MAX_BS)   // int16: block_size <= 128
     return a.M == 1 ? launch_gu_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 1>(a, qa, sa, dots)
                     : launch_gu_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 4>(a, qa, sa, dots);
-  return a.M == 1 ? launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 1>(a, qa, sa, dots)
-                  : launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 4>(a, qa, sa, dots);
+  if constexpr (ACT != ACT_I16)
+    return a.M == 1 ? launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 1>(a, qa, sa, dots)
+                    : launch_gn_m<ACT, BITS, XDT, SDT, HAS_ZP, DOTS, 4>(a, qa, sa, dots);
+  return hipErrorInvalidValue;
 }
 
 template <int ACT, int BITS, int XDT, bool DOTS>
@@ -476,13 +478,19 @@ hipError_t launch_gn_x(const MatArgs& a, const void* qa, const float* sa, int32_
   }
 }
 
+// Float and int8 activations reach these kernels with 3-bit weights only
+// (the other widths have their own kernels); int16 activations with any.
 template <int ACT, bool DOTS>
 hipError_t launch_gn_b(const MatArgs& a, const void* qa, const float* sa, int32_t* dots) {
-  switch (a.bits) {
-    case 2: return launch_gn_x<ACT, 2, DOTS>(a, qa, sa, dots);
-    case 3: return launch_gn_x<ACT, 3, DOTS>(a, qa, sa, dots);
-    case 4: return launch_gn_x<ACT, 4, DOTS>(a, qa, sa, dots);
-    default: return launch_gn_x<ACT, 8, DOTS>(a, qa, sa, dots);
+  if constexpr (ACT != ACT_I16) {
+    return a.bits == 3 ? launch_gn_x<ACT, 3, DOTS>(a, qa, sa, dots) : hipErrorInvalidValue;
+  } else {
+    switch (a.bits) {
+      case 2: return launch_gn_x<ACT, 2, DOTS>(a, qa, sa, dots);
+      case 3: return launch_gn_x<ACT, 3, DOTS>(a, qa, sa, dots);
+      case 4: return launch_gn_x<ACT, 4, DOTS>(a, qa, sa, dots);
+      default: return launch_gn_x<ACT, 8, DOTS>(a, qa, sa, dots);
+    }
   }
 }
 
