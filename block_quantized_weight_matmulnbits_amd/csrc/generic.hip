@@ -93,6 +93,38 @@ __device__ __forceinline__ void decode16(const uint32_t (&w)[Raw16<BITS>::W], in
   }
 }
 
+// (code - zp) of 16 codes as eight int16 pairs (codes 2v, 2v + 1 in the low
+// and high halves of pair v), for v_dot2_i32_i16 against int16 activation
+// pairs.  8-bit and 4-bit codes are moved into 16-bit lanes with byte
+// permutes; the other widths are decoded first.  |code - zp| <= 255.
+typedef short short2_t __attribute__((ext_vector_type(2)));
+template <int BITS>
+__device__ __forceinline__ void code_pairs16(const uint32_t (&w)[Raw16<BITS>::W], int z,
+                                             uint32_t (&pr)[8]) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      pr[v] = __builtin_amdgcn_perm(0u, w[v / 2], (v & 1) ? 0x0C030C02u : 0x0C010C00u);
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        pr[4 * i + b] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b);
+    }
+  } else {
+    int c[16];
+    decode16<BITS>(w, c);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) pr[v] = (uint32_t)c[2 * v] | ((uint32_t)c[2 * v + 1] << 16);
+  }
+  const short2_t zz = {(short)z, (short)z};
+#pragma unroll
+  for (int v = 0; v < 8; ++v)
+    pr[v] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(short2_t, pr[v]) - zz);
+}
+
 // Zero point of block b of a packed zero-point row of row_bytes bytes,
 // without a branch: both bytes a 3-bit value can touch are read (the second
 // clamped into the row).
@@ -228,8 +260,10 @@ __global__ __launch_bounds__(256) void generic_rows_kernel(
 // (16 codes) u0 + l of each of the wave's GU_R columns, so a wave covers 1024
 // codes of a column per pass and every lane is busy whatever the block size.
 // Each lane reads its unit's activations of MT rows straight from memory
-// (16-byte loads; the vector stays in the caches): no staging, no barrier.  Per code: (code - zp) as an integer, then
-// an fp32 FMA with the activation (float) or an integer multiply-add (int).
+// (16-byte loads; the vector stays in the caches): no staging, no barrier.
+// Per code: (code - zp) as an integer, then an fp32 FMA with the activation
+// (float) or an integer multiply-add (int8); int16 activations meet packed
+// int16 (code - zp) pairs in v_dot2_i32_i16.
 // Float: each unit's sum is scaled by its block's scale.  Integer: the
 // block's UB = bs / 16 lanes (aligned, adjacent) add their exact int32 sums
 // by XOR shuffles, and the first lane scales the block dot once.
@@ -275,6 +309,7 @@ __global__ __launch_bounds__(256) void generic_unit_kernel(
       // stays in the caches, so there is no staging and no barrier.
       float xf[MT][16];
       int xi[MT][16];
+      uint32_t xw[MT][8];          // int16: the raw activation pairs
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int64_t mr = m < Mp ? m : 0;
@@ -320,9 +355,10 @@ __global__ __launch_bounds__(256) void generic_unit_kernel(
           for (int v = 0; v < 2; ++v) {
             const u32x4 w = reinterpret_cast<const u32x4*>(
                 reinterpret_cast<const int16_t*>(qa) + mr * padded + k0)[v];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xi[m][8 * v + j] = (int)(int16_t)(ww[j / 2] >> (16 * (j & 1)));
+            xw[m][4 * v + 0] = w.x;
+            xw[m][4 * v + 1] = w.y;
+            xw[m][4 * v + 2] = w.z;
+            xw[m][4 * v + 3] = w.w;
           }
         }
       }
@@ -343,7 +379,9 @@ __global__ __launch_bounds__(256) void generic_unit_kernel(
         const int n = n0 + r;
         if (n >= N) continue;                           // wave-uniform
         int c[16];
-        decode16<BITS>(raw[r], c);
+        uint32_t pr[8];
+        if constexpr (ACT == ACT_I16) code_pairs16<BITS>(raw[r], zr[r], pr);
+        else decode16<BITS>(raw[r], c);
         const int z = zr[r];
         const float s = sr[r];
 #pragma unroll
@@ -355,8 +393,16 @@ __global__ __launch_bounds__(256) void generic_unit_kernel(
             acc[r][m] = fmaf(live ? d : 0.0f, s, acc[r][m]);
           } else {
             int d = 0;
+            if constexpr (ACT == ACT_I16) {
+              // Exact: |pair dot| < 2^24, block sums < 2^31 (bs <= 128).
 #pragma unroll
-            for (int j = 0; j < 16; ++j) d += xi[m][j] * (c[j] - z);
+              for (int v = 0; v < 8; ++v)
+                d = __builtin_amdgcn_sdot2(__builtin_bit_cast(short2_t, pr[v]),
+                                           __builtin_bit_cast(short2_t, xw[m][v]), d, false);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 16; ++j) d += xi[m][j] * (c[j] - z);
+            }
             d = live ? d : 0;
             for (int o = 1; o < (1 << ub_log2); o <<= 1) d += __shfl_xor(d, o);
             if (live && ui == 0) {
