@@ -37,6 +37,11 @@ hipError_t launch_gemv(const MatArgs& a);
 hipError_t launch_gidx(const MatArgs& a);
 // The matrix-core GEMM with per-code group lookups (gemm.hip).
 bool gemm_mfma_gidx_supported(const MatArgs& a);
+// A few rows (2 <= M <= SKINNY_MAX_M) of 16-bit activations on the matrix
+// cores, K split over the waves of a workgroup (gemm_skinny.hip).
+constexpr int64_t SKINNY_MAX_M = 64;
+bool gemm_skinny_supported(const MatArgs& a);
+hipError_t launch_gemm_skinny(const MatArgs& a);
 hipError_t launch_gemm_mfma_gidx(const MatArgs& a);
 // M = 1 on the tiled layout (gemv_tiled.hip).
 bool gemv_tiled_supported(const MatArgs& a);
