@@ -1,6 +1,6 @@
 // gemm_skinny.hip -- the matmul over block-quantized weights for a few rows of
-// 16-bit activations (2 <= M <= 64: batched decode, short prompts) on the
-// gfx950 matrix cores.
+// 16-bit activations (batched decode, short prompts: M <= 16, or up to 1024
+// workgroups of 32 x 32 outputs) on the gfx950 matrix cores.
 //
 // Y[M, N] = A[M, K] * W^T, W[n, k] = (code - zp) * scale (onnx-runtime-ep-cpu
 // matmul_nbits.rs: the batched route dequantizes then multiplies).  With few
@@ -378,7 +378,7 @@ static hipError_t launch_skinny_t(const MatArgs& a) {
   return hipGetLastError();
 }
 
-// M <= 16: one 16-row tile per workgroup; up to 64: 32-row tiles.
+// M <= 16: one 16-row tile per workgroup; more rows: 32-row tiles (grid y).
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 static hipError_t launch_skinny_m(const MatArgs& a) {
   if (a.M <= 16) return launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 1>(a);
@@ -401,7 +401,10 @@ static hipError_t launch_skinny_x(const MatArgs& a) {
 
 bool gemm_skinny_supported(const MatArgs& a) {
   const int64_t sz = a.s_dtype == DT_F32 ? 4 : 2;
-  return a.a_dtype != DT_F32 && a.bits != 3 && !a.g_idx && a.M >= 2 && a.M <= SKINNY_MAX_M &&
+  // Past the limit the 256-row kernel, whose workgroups each cover many
+  // rows, is faster: every workgroup here dequantizes its columns afresh.
+  const bool few = a.M <= 16 || ((a.M + 31) / 32) * ((a.N + 31) / 32) <= SKINNY_MAX_GROUPS;
+  return a.a_dtype != DT_F32 && a.bits != 3 && !a.g_idx && a.M >= 2 && few &&
          (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 < 0x7FFFFF00LL &&
          (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
          (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 < 0x7FFFFF00LL &&

@@ -37,9 +37,10 @@ hipError_t launch_gemv(const MatArgs& a);
 hipError_t launch_gidx(const MatArgs& a);
 // The matrix-core GEMM with per-code group lookups (gemm.hip).
 bool gemm_mfma_gidx_supported(const MatArgs& a);
-// A few rows (2 <= M <= SKINNY_MAX_M) of 16-bit activations on the matrix
-// cores, K split over the waves of a workgroup (gemm_skinny.hip).
-constexpr int64_t SKINNY_MAX_M = 64;
+// A few rows of 16-bit activations on the matrix cores, K split over the
+// waves of a workgroup (gemm_skinny.hip): M <= 16, or a grid of at most
+// SKINNY_MAX_GROUPS workgroups of 32 rows x 32 columns.
+constexpr int64_t SKINNY_MAX_GROUPS = 1024;
 bool gemm_skinny_supported(const MatArgs& a);
 hipError_t launch_gemm_skinny(const MatArgs& a);
 hipError_t launch_gemm_mfma_gidx(const MatArgs& a);

@@ -1,5 +1,6 @@
-"""GPU parity of the few-row matrix-core matmul (qmm_gemm with 2 <= M <= 64
-and bf16 / f16 activations, K % 8 == 0: the path for batched decode).
+"""GPU parity of the few-row matrix-core matmul (qmm_gemm with bf16 / f16
+activations, K % 8 == 0, and M <= 16 or at most 1024 workgroups of 32 x 32
+outputs: the path for batched decode).
 
 * Exact data (small-integer activations, power-of-two scales): the result
   equals the oracle's value rounded once to the output dtype, for every
@@ -9,9 +10,9 @@ and bf16 / f16 activations, K % 8 == 0: the path for batched decode).
   repacked one.
 * Random data within tol * S; the decode projections (K, N) = (4096, 14336)
   and (14336, 4096) at M = 16 and M = 64 strictly.
-* The edges of the route: M = 64 (the last few-row size) against M = 65
-  (the 256-row kernel) on the same rows; row m of a batch equals the same row
-  computed in another batch.
+* The edges of the route: M = 64 against M = 65 at N = 14336 (the 256-row
+  kernel) on the same rows; many rows of a narrow matrix; row m of a batch
+  equals the same row computed in another batch.
 """
 import numpy as np
 import pytest
@@ -111,12 +112,23 @@ def test_decode_projection_strict(M, K, N):
 
 
 def test_route_edge_m64_vs_m65():
-    """Rows 0..63 of an M = 65 product (256-row kernel) equal the M = 64 product
-    (few-row kernel) on exact data."""
-    case = exact_case(65, 1024, 200, 32, 4, "bf16", "bf16", True, True, seed=9)
+    """N = 14336: M = 64 takes the few-row kernel (2 x 448 workgroups), M = 65
+    the 256-row kernel (3 x 448 would pass the limit of 1024); on exact data
+    rows 0..63 agree bit for bit."""
+    case = exact_case(65, 256, 14336, 32, 4, "bf16", "bf16", True, True, seed=9)
     y65 = run(case).cpu()
     case.M, case.A = 64, case.A[:64].contiguous()
     assert torch.equal(run(case).cpu(), y65[:64])
+
+
+def test_many_rows_narrow_matrix():
+    """M = 200 on N = 100 stays on the few-row kernel (7 x 4 workgroups):
+    exact data on both layouts."""
+    case = exact_case(200, 520, 100, 64, 4, "f16", "f32", True, True, seed=21)
+    Y, _ = oracle_matmul(case)
+    expect = torch.from_numpy(Y).to(case.A.dtype)
+    assert torch.equal(run(case).cpu(), expect)
+    assert torch.equal(run(case, tiled=True).cpu(), expect)
 
 
 def test_rows_are_independent():
