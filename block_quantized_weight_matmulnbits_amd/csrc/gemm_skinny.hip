@@ -72,20 +72,21 @@ __device__ __forceinline__ void step_codes(const uint32_t* cw, int s, float* q) 
 // byte range of each tensor on both layouts -- scales [32 x kb sz, +32 kb sz)
 // (operator layout: rows n * kb; tiled: group x), zero points [x zrow, +zrow)
 // with zrow = 32 * zp_row_bytes (operator) or 4 kb bits (tiled).  With
-// slab = 1 the workgroup copies both ranges into LDS once (16-byte loads) and
+// SLAB the workgroup copies both ranges into LDS once (16-byte loads) and
 // every lookup reads LDS.
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, int MT, bool TL>
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, int MT, bool TL, bool SLAB>
 __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
-    int log2_bs, int row_bytes, int zp_row_bytes, int chunks, int zrow, int slab) {
+    int log2_bs, int row_bytes, int zp_row_bytes, int chunks, int zrow) {
   static_assert(TN == 2, "a workgroup's 32 columns are one group of the tiled layout");
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int LW = 2 * BITS;                 // code words per lane and tile (64 codes)
   constexpr int CHUNK_BYTES = TKC * BITS / 8;  // tiled layout: one column's 64 codes
   constexpr int OOB = 0x7FFFFFF0;
+  constexpr int OOB_A = 0x7FFFE000;            // activations: the launcher keeps M K 2 below
   constexpr uint32_t ZM = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
   constexpr int SZ = (int)sizeof(typename dt<SDT>::T);
   __shared__ float red[SK_WAVES / 2][MT * TN * 4][64];
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   auto scale_at = [&](int t, int b, bool ok) -> float {
     const int e = sc0[t] + b * sc_stride;
     ST v;
-    if (slab) {
+    if constexpr (SLAB) {
       v = *reinterpret_cast<const ST*>(slab_lds + (s_lo - s_al) + e * SZ);
     } else {
       const int so = ok ? s_lo + e * SZ : OOB;
@@ -147,8 +148,8 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
     return dt<SDT>::to_f32(v);
   };
   auto zp_byte = [&](int byte, bool ok) -> uint32_t {      // byte offset within the range
-    if (slab) return slab_lds[s_cnt + (z_lo - z_al) + byte];
-    return __builtin_amdgcn_raw_buffer_load_b8(rzp, ok ? z_lo + byte : OOB, 0, 0);
+    if constexpr (SLAB) return slab_lds[s_cnt + (z_lo - z_al) + byte];
+    else return __builtin_amdgcn_raw_buffer_load_b8(rzp, ok ? z_lo + byte : OOB, 0, 0);
   };
 
   f32x4 acc[MT][TN];
@@ -178,14 +179,17 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   // k = 256 st + 32 s + 8 g .. + 7 of row r, so each load reads 64
   // contiguous bytes of 16 rows.
   auto load_a = [&](int st) {
+    const bool whole = (st + 1) * SK_KSTEP <= K;   // every k of the step inside K
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int row = m0 + 16 * i + c;
+      const int base = row < M ? (row * K + st * SK_KSTEP + 8 * g) * 2 : OOB_A;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int k = st * SK_KSTEP + 32 * s + 8 * g;
-        const bool ok = row < M && k < K;      // K % 8 == 0: 8 activations all in or all out
-        ar[i][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? (row * K + k) * 2 : OOB, 0, 0);
+        // K % 8 == 0: 8 activations are all in or all out.  OOB_A + 448
+        // stays past the extent and below 2^31.
+        const bool ok = whole || st * SK_KSTEP + 32 * s + 8 * g < K;
+        ar[i][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? base + 64 * s : OOB_A, 0, 0);
       }
     }
   };
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   // The first step's loads go out before the staging copy and its barrier.
   load_codes(wave);
   load_a(wave);
-  if (slab) {
+  if constexpr (SLAB) {
     // A buffer load reads zero for every dword not wholly inside the extent,
     // so the 16 bytes that hold a tensor's last byte are read byte by byte.
     auto copy = [&](__amdgpu_buffer_rsrc_t r, int extent, int from, int count, uint8_t* to) {
@@ -360,13 +364,16 @@ static hipError_t launch_skinny_t(const MatArgs& a) {
   using ST = typename dt<SDT>::T;
   constexpr int64_t SZ = sizeof(ST);
   const dim3 grid((unsigned)((a.N + 16 * SK_TN - 1) / (16 * SK_TN)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
-  auto kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, true>
-                      : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false>;
   // Bytes of a workgroup's zero-point range; LDS for both ranges (with the
   // slack of their 16-byte aligned copies).
   const int64_t zrow = a.tiled ? a.kb * 4 * BITS : 32 * a.zp_row_bytes;
   const int64_t lds = (32 * a.kb * SZ + 15 + 15) / 16 * 16 + (HAS_ZP ? (zrow + 15 + 15) / 16 * 16 : 0);
   const bool slab = lds <= SK_SLAB_MAX;
+  decltype(&gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false, false>) kern;
+  if (slab) kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, true, true>
+                           : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false, true>;
+  else kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, true, false>
+                      : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false, false>;
   if (slab) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, SK_SLAB_MAX);
     if (e != hipSuccess) return e;
@@ -374,7 +381,7 @@ static hipError_t launch_skinny_t(const MatArgs& a) {
   hipLaunchKernelGGL(kern, grid, dim3(SK_TPB), slab ? (size_t)lds : 0, a.stream, (const uint16_t*)a.A,
                      a.B, (const ST*)a.scales, a.zp, (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M,
                      (int)a.K, (int)a.N, (int)a.kb, sk_log2(a.block_size), (int)(a.kb * a.blob),
-                     (int)a.zp_row_bytes, (int)a.chunks, (int)zrow, slab ? 1 : 0);
+                     (int)a.zp_row_bytes, (int)a.chunks, (int)zrow);
   return hipGetLastError();
 }
 
@@ -405,7 +412,7 @@ bool gemm_skinny_supported(const MatArgs& a) {
   // rows, is faster: every workgroup here dequantizes its columns afresh.
   const bool few = a.M <= 16 || ((a.M + 31) / 32) * ((a.N + 31) / 32) <= SKINNY_MAX_GROUPS;
   return a.a_dtype != DT_F32 && a.bits != 3 && !a.g_idx && a.M >= 2 && few &&
-         (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 < 0x7FFFFF00LL &&
+         (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 <= 0x7FFFE000LL &&
          (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
          (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 < 0x7FFFFF00LL &&
          (a.N + 32) * a.kb * sz < 0x7FFFFF00LL;
