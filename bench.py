@@ -67,7 +67,8 @@ def parse():
                         "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
-    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4", "lowbit"], default=None,
+    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4", "lowbit", "batched"],
+                   default=None,
                    help="time only this workload and print its object (profiling runs)")
     p.add_argument("--read-sweep", action="store_true",
                    help="only sweep the plain streaming read (bench_probe/) over launch shapes "
@@ -107,7 +108,8 @@ def main():
             torch.cuda.synchronize()
             del src, dst
         fn = {"compint8": bench_compint8, "prefill": bench_prefill, "conv": bench_conv,
-              "tiny": bench_tiny, "fp4": bench_fp4, "lowbit": bench_lowbit}[args.only]
+              "tiny": bench_tiny, "fp4": bench_fp4, "lowbit": bench_lowbit,
+              "batched": bench_batched}[args.only]
         print(json.dumps({args.only: fn(qmm, dev, stream, args)}), flush=True)
         return
     if args.copy_calibration:
@@ -732,6 +734,46 @@ def bench_lowbit(qmm, dev, stream, args):
     flop = 2.0 * c.M * c.N * c.K
     res["b3_prefill_M2048"] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
                                "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
+def bench_batched(qmm, dev, stream, args):
+    """Float (bf16) batched decode on the decode-layer weights, 4-bit asymmetric
+    bs 32 with bf16 scales, operator layout: qmm_gemv at M = 1 and qmm_gemm
+    for M = 2 .. 256 on the projections (K, N) = (4096, 14336) and
+    (14336, 4096).  Weights rotate through copies so each launch streams them
+    from HBM; bytes = codes + scales + zero points + activations + output."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    res = {}
+    for K, N in ((4096, 14336), (14336, 4096)):
+        base = make_matmul_case(1, K, N, 32, 4, a_dtype="bf16", has_zp=True, seed=70).to(dev)
+        nbytes = base.weight_bytes()
+        n_copies = max(2, -(-POOL_BYTES // nbytes))
+        pool = [(base.B, base.scales, base.zero_points)] + [
+            (base.B.clone(), base.scales.clone(), base.zero_points.clone())
+            for _ in range(n_copies - 1)]
+        for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+            A = make_matmul_case(M, K, N, 32, 4, a_dtype="bf16", seed=71 + M).A.to(dev)
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+            def run(i, A=A, Y=Y, M=M, K=K, N=N):
+                B, sc, zp = pool[i % len(pool)]
+                if M == 1:
+                    qmm.qmm_gemv(A.reshape(-1), B, sc, zp, None, Y.reshape(-1), K, N, 32, 4,
+                                 stream=stream)
+                else:
+                    qmm.qmm_gemm(A, B, sc, zp, None, Y, M, K, N, 32, 4, 0, stream)
+
+            for i in range(3):
+                run(i)
+            torch.cuda.synchronize()
+            ms = _time_launches(run, max(20, args.steps // 4), stream)
+            byts = nbytes + A.numel() * 2 + M * N * 2
+            res[f"K{K}_N{N}_M{M}"] = {
+                "us": round(ms * 1e3, 2), "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2)}
+        del pool
     return res
 
 

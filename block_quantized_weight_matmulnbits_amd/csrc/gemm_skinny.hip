@@ -35,7 +35,7 @@ namespace qmm {
 constexpr int SK_WAVES = 8;
 constexpr int SK_TPB = 64 * SK_WAVES;
 constexpr int SK_KSTEP = 256;               // K per wave step (4 lane groups x 64 codes)
-constexpr int SK_TN = 2;                    // 16-column tiles per workgroup: 32 columns
+constexpr int SK_FULL_ROUND = 256;          // workgroups that give every compute unit one
 // Scales and zero points of a workgroup's 32 columns are staged in LDS when
 // both fit in this many bytes (each range is copied from a 16-byte aligned
 // start, hence the slack); otherwise every lane loads its own.
@@ -68,19 +68,19 @@ __device__ __forceinline__ void step_codes(const uint32_t* cw, int s, float* q) 
 // the next column (or lie past the matrix and read as zero) and meet zero
 // activations.
 //
-// Scales and zero points: the 32 columns of workgroup x own one contiguous
-// byte range of each tensor on both layouts -- scales [32 x kb sz, +32 kb sz)
-// (operator layout: rows n * kb; tiled: group x), zero points [x zrow, +zrow)
-// with zrow = 32 * zp_row_bytes (operator) or 4 kb bits (tiled).  With
-// SLAB the workgroup copies both ranges into LDS once (16-byte loads) and
-// every lookup reads LDS.
+// Scales and zero points: a workgroup's columns lie in one contiguous byte
+// range of each tensor on both layouts -- operator layout: its 16 TN rows of
+// kb scales and of zp_row_bytes zero-point bytes; tiled: the 32 columns of
+// its group (kb x 32 scales, 4 kb bits bytes of zero points).  With SLAB the
+// workgroup copies both ranges into LDS once (16-byte loads) and every lookup
+// reads LDS.
 template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, int MT, bool TL, bool SLAB>
 __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
-    int log2_bs, int row_bytes, int zp_row_bytes, int chunks, int zrow) {
-  static_assert(TN == 2, "a workgroup's 32 columns are one group of the tiled layout");
+    int log2_bs, int row_bytes, int zp_row_bytes, int chunks) {
+  static_assert(TN == 1 || TN == 2, "16 or 32 columns: within one group of the tiled layout");
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int LW = 2 * BITS;                 // code words per lane and tile (64 codes)
@@ -111,10 +111,14 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   const __amdgpu_buffer_rsrc_t rzp =
       __builtin_amdgcn_make_buffer_rsrc((void*)zp, 0, HAS_ZP ? zp_extent : 0, BUF_WORD3);
 
-  // The workgroup's ranges: scales from byte s_lo, zero points from z_lo.
-  const int s_lo = blockIdx.x * 32 * kb * SZ, z_lo = blockIdx.x * zrow;
+  // The workgroup's ranges: columns from col0 (tiled: its group's first),
+  // scales from byte s_lo, zero points from z_lo.
+  const int cols = TL ? TG : 16 * TN;
+  const int col0 = TL ? n0 / TG * TG : n0;
+  const int zrow = TL ? kb * 4 * BITS : cols * zp_row_bytes;
+  const int s_lo = col0 * kb * SZ, z_lo = TL ? n0 / TG * zrow : n0 * zp_row_bytes;
   const int s_al = s_lo & ~15, z_al = z_lo & ~15;
-  const int s_cnt = (s_lo - s_al + 32 * kb * SZ + 15) & ~15;     // bytes copied
+  const int s_cnt = (s_lo - s_al + cols * kb * SZ + 15) & ~15;   // bytes copied
   const int z_cnt = HAS_ZP ? (z_lo - z_al + zrow + 15) & ~15 : 0;
 
   // Per tile: the byte offset of this lane's codes at k0 = 0 (and per 64-code
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   const int zb_stride = TL ? TG * BITS : BITS;
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    const int n = n0 + 16 * t + c, ci = 16 * t + c;       // ci: column within the 32
+    const int n = n0 + 16 * t + c, ci = n - col0;         // ci: column within the range
     col_ok[t] = n < N;
     code0[t] = TL ? ((n / TG) * chunks * TG + ci) * CHUNK_BYTES : n * row_bytes;
     sc0[t] = TL ? ci : ci * kb;
@@ -359,21 +363,22 @@ static int sk_log2(int64_t v) {
   return l;
 }
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int MT>
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, int MT>
 static hipError_t launch_skinny_t(const MatArgs& a) {
   using ST = typename dt<SDT>::T;
   constexpr int64_t SZ = sizeof(ST);
-  const dim3 grid((unsigned)((a.N + 16 * SK_TN - 1) / (16 * SK_TN)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+  const dim3 grid((unsigned)((a.N + 16 * TN - 1) / (16 * TN)), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
   // Bytes of a workgroup's zero-point range; LDS for both ranges (with the
   // slack of their 16-byte aligned copies).
-  const int64_t zrow = a.tiled ? a.kb * 4 * BITS : 32 * a.zp_row_bytes;
-  const int64_t lds = (32 * a.kb * SZ + 15 + 15) / 16 * 16 + (HAS_ZP ? (zrow + 15 + 15) / 16 * 16 : 0);
+  const int64_t cols = a.tiled ? TG : 16 * TN;
+  const int64_t zrow = a.tiled ? a.kb * 4 * BITS : cols * a.zp_row_bytes;
+  const int64_t lds = (cols * a.kb * SZ + 15 + 15) / 16 * 16 + (HAS_ZP ? (zrow + 15 + 15) / 16 * 16 : 0);
   const bool slab = lds <= SK_SLAB_MAX;
-  decltype(&gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false, false>) kern;
-  if (slab) kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, true, true>
-                           : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false, true>;
-  else kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, true, false>
-                      : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, SK_TN, MT, false, false>;
+  decltype(&gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, false>) kern;
+  if (slab) kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, true, true>
+                           : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, true>;
+  else kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, true, false>
+                      : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, false>;
   if (slab) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, SK_SLAB_MAX);
     if (e != hipSuccess) return e;
@@ -381,15 +386,20 @@ static hipError_t launch_skinny_t(const MatArgs& a) {
   hipLaunchKernelGGL(kern, grid, dim3(SK_TPB), slab ? (size_t)lds : 0, a.stream, (const uint16_t*)a.A,
                      a.B, (const ST*)a.scales, a.zp, (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M,
                      (int)a.K, (int)a.N, (int)a.kb, sk_log2(a.block_size), (int)(a.kb * a.blob),
-                     (int)a.zp_row_bytes, (int)a.chunks, (int)zrow);
+                     (int)a.zp_row_bytes, (int)a.chunks);
   return hipGetLastError();
 }
 
 // M <= 16: one 16-row tile per workgroup; more rows: 32-row tiles (grid y).
+// 32 columns per workgroup, or 16 when 32 would leave compute units idle.
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 static hipError_t launch_skinny_m(const MatArgs& a) {
-  if (a.M <= 16) return launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 1>(a);
-  return launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 2>(a);
+  const int64_t row_tiles = a.M <= 16 ? 1 : (a.M + 31) / 32;
+  const bool narrow = row_tiles * ((a.N + 31) / 32) < SK_FULL_ROUND;
+  if (a.M <= 16) return narrow ? launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 1, 1>(a)
+                               : launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 2, 1>(a);
+  return narrow ? launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 1, 2>(a)
+                : launch_skinny_t<BITS, XDT, SDT, HAS_ZP, 2, 2>(a);
 }
 
 template <int BITS, int XDT>
