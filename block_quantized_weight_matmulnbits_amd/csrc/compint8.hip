@@ -246,10 +246,10 @@ __global__ __launch_bounds__(CI8_THREADS) void compint8_kernel(
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (vec) {
-          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb[r], uc * 16, 0, 0);
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb[r], uc * 16, 0, BUF_STREAM);
           cw[r][0] = t.x; cw[r][1] = t.y; cw[r][2] = t.z; cw[r][3] = t.w;
         } else {
-          cw[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rb[r], uc * 4, 0, 0);
+          cw[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rb[r], uc * 4, 0, BUF_STREAM);
           cw[r][1] = cw[r][2] = cw[r][3] = 0;
         }
         if constexpr (sizeof(ST) == 4)

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(CS_MAXW * 64) void compint8_small_kernel(
 
   struct Slot { u32x4 cw; uint32_t sw, zw; };
   auto issue = [&](Slot& sl, int j) {
-    sl.cw = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, 0);
+    sl.cw = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, BUF_STREAM);
     const int b = min((lane_k + j * CPL * TKC) >> log2_bs, kb - 1);
     const int si = (g * kb + b) * TG + gcol;
     sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (si * SZ) & ~3, 0, 0);

@@ -166,12 +166,12 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   auto issue = [&](CtSlot& sl, int j) {
     const int c = c_lo + j;
     if constexpr (LB == 16)
-      sl.code = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + c * (TG * CB), 0, 0);
+      sl.code = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + c * (TG * CB), 0, BUF_STREAM);
     else if constexpr (LB == 8) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane_code + c * (TG * CB), 0, 0);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane_code + c * (TG * CB), 0, BUF_STREAM);
       sl.code = u32x4{v.x, v.y, 0u, 0u};
     } else {
-      sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * (TG * CB), 0, 0),
+      sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * (TG * CB), 0, BUF_STREAM),
                       0u, 0u, 0u};
     }
     if constexpr (!STAGE) sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);

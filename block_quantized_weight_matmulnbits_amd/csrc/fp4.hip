@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void fp4_gemv_kernel(
         const int n = n0 + r;
         const bool ok = live && n < N;
         cv[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
-            rw, ok ? n * row_bytes + u * 16 : 0x7FFFFFF0, 0, 0);
+            rw, ok ? n * row_bytes + u * 16 : 0x7FFFFFF0, 0, BUF_STREAM);
         // MXFP4: one scale per unit; NVFP4: two (bytes 2u and 2u + 1).
         const int sb = n * kb + (FMT == FP4_MX ? u : 2 * u);
         sv[r][j] = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? sb : 0x7FFFFFF0, 0, 0);

@@ -290,10 +290,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
       Slot<UW, ST_> sl[D];
       auto issue = [&](Slot<UW, ST_>& q, int r, int u) {
         if constexpr (VEC) {
-          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb[r], u * 16, 0, 0);
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb[r], u * 16, 0, BUF_STREAM);
           q.cw[0] = t.x; q.cw[1] = t.y; q.cw[2] = t.z; q.cw[3] = t.w;
         } else {
-          q.cw[0] = __builtin_amdgcn_raw_buffer_load_b32(rb[r], u * 4, 0, 0);
+          q.cw[0] = __builtin_amdgcn_raw_buffer_load_b32(rb[r], u * 4, 0, BUF_STREAM);
         }
         const int blk = (u * UW) >> blob_words_log2;
         q.blk = blk;

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
     const int ub0 = (g * kb + ((c_lo * TKC) >> log2_bs)) * TG;
     const int ubs = ((CPL * TKC) >> log2_bs) * TG;
     auto issue = [&](TSlot& sl, int j) {
-      sl.cw = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, 0);
+      sl.cw = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, BUF_STREAM);
       const int ub = LINB ? ub0 + j * ubs
                           : (g * kb + (((c_lo + j * CPL) * TKC) >> log2_bs)) * TG;
       sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, ub * SZ + lane_soff, 0, 0);
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void gemv_tiled_kernel(
     } else {
       // Exact fp32 path: every code times the activation read from memory.
       for (int j = 0; j < nloads; ++j) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + 4096 * j, 0, BUF_STREAM);
         const int ub = (g * kb + (((c_lo + j * CPL) * TKC) >> log2_bs)) * TG;
         const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(rs, ub * SZ + lane_soff, 0, 0);
         float sc;

@@ -69,14 +69,15 @@ struct Raw16 {
 template <int BITS>
 __device__ __forceinline__ void load_raw16(const uint8_t* __restrict__ blk, int bs, int i0,
                                            uint32_t (&w)[Raw16<BITS>::W]) {
+  // Codes are read once: non-temporal loads.
   if constexpr (BITS == 3) {
     const uint16_t* lo = reinterpret_cast<const uint16_t*>(blk + i0 / 4);
-    w[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-    w[1] = *reinterpret_cast<const uint16_t*>(blk + bs / 4 + i0 / 8);
+    w[0] = (uint32_t)__builtin_nontemporal_load(lo) | ((uint32_t)__builtin_nontemporal_load(lo + 1) << 16);
+    w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(blk + bs / 4 + i0 / 8));
   } else {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + i0 * BITS / 8);
 #pragma unroll
-    for (int i = 0; i < Raw16<BITS>::W; ++i) w[i] = p[i];
+    for (int i = 0; i < Raw16<BITS>::W; ++i) w[i] = __builtin_nontemporal_load(p + i);
   }
 }
 template <int BITS>

@@ -16,6 +16,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Cache policy of buffer loads of data read once (the packed codes streamed by
+// the M = 1 kernels): the non-temporal bit of gfx950's buffer-load cache
+// policy.  A plain read of the decode layer's gate|up bytes ran at 5.9 TB/s
+// with it and 5.6 without; the tiled GEMV's gate|up launch went from 16.6 to
+// 15.1-15.5 us.  (The few-row matrix-core kernel, whose 8 waves read adjacent
+// pieces of each column, measured 2-7 % slower with it and does not use it;
+// nor do the scale and zero-point loads, which neighbouring waves share.)
+constexpr int BUF_STREAM = 2;
+
 // Storage type and exact widening / rounding narrowing of each float dtype.
 template <int DT> struct dt;
 template <> struct dt<DT_F32> {
