@@ -45,7 +45,15 @@ constexpr int SK_SLAB_MAX = 64 * 1024;
 // fp32 values.
 template <int BITS>
 __device__ __forceinline__ void step_codes(const uint32_t* cw, int s, float* q) {
-  if constexpr (BITS == 8) {
+  if constexpr (BITS == 3) {
+    // cw[0..3]: the 64 codes' 2-bit plane fields in code order, cw[4..5]:
+    // their 1-bit plane bits (see load_codes); code i of sub-step s is
+    // field 8 s + i plus 4 times bit 8 s + i.
+    const uint32_t lo = cw[s >> 1] >> (16 * (s & 1));
+    const uint32_t hi = cw[4 + (s >> 2)] >> (8 * (s & 3));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (float)(((lo >> (2 * i)) & 3u) | (((hi >> i) & 1u) << 2));
+  } else if constexpr (BITS == 8) {
     word_codes_f32<8>(cw[2 * s], q);
     word_codes_f32<8>(cw[2 * s + 1], q + 4);
   } else if constexpr (BITS == 4) {
@@ -81,12 +89,15 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
     int log2_bs, int row_bytes, int zp_row_bytes, int chunks) {
   static_assert(TN == 1 || TN == 2, "16 or 32 columns: within one group of the tiled layout");
+  static_assert(BITS != 3 || !TL, "3-bit weights: operator layout");
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int LW = 2 * BITS;                 // code words per lane and tile (64 codes)
   constexpr int CHUNK_BYTES = TKC * BITS / 8;  // tiled layout: one column's 64 codes
   constexpr int OOB = 0x7FFFFFF0;
-  constexpr int OOB_A = 0x7FFFE000;            // activations: the launcher keeps M K 2 below
+  // Past every extent (the launcher keeps them at most this) with room for
+  // the constant offsets added to it below 2^31.
+  constexpr int OOB_A = 0x7FFFE000;
   constexpr uint32_t ZM = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
   constexpr int SZ = (int)sizeof(typename dt<SDT>::T);
   __shared__ float red[SK_WAVES / 2][MT * TN * 4][64];
@@ -119,7 +130,8 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   const int s_lo = col0 * kb * SZ, z_lo = TL ? n0 / TG * zrow : n0 * zp_row_bytes;
   const int s_al = s_lo & ~15, z_al = z_lo & ~15;
   const int s_cnt = (s_lo - s_al + cols * kb * SZ + 15) & ~15;   // bytes copied
-  const int z_cnt = HAS_ZP ? (z_lo - z_al + zrow + 15) & ~15 : 0;
+  // 3-bit: a block's 4-byte zero-point window may reach 3 bytes past a row.
+  const int z_cnt = HAS_ZP ? (z_lo - z_al + zrow + (BITS == 3 ? 4 : 0) + 15) & ~15 : 0;
 
   // Per tile: the byte offset of this lane's codes at k0 = 0 (and per 64-code
   // chunk), the index of its first scale and bit of its first zero point
@@ -171,11 +183,49 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
     const int chunk = k0 >> 6;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const int off = k0 < kpad && col_ok[t] ? code0[t] + chunk * code_chunk : OOB;
+      const bool ok = k0 < kpad && col_ok[t];
+      if constexpr (BITS == 3) {
+        // Operator layout, blob of 3 bs / 8 bytes: the 2-bit plane (bs / 4
+        // bytes) then the 1-bit plane (bs / 8 bytes).  The lane's 64 codes
+        // go to cw[0..3] (2-bit fields) and cw[4..5] (bits), in code order.
+        const int bsz = 1 << log2_bs;
+        if (bsz >= 64) {
+          // One block: 16 bytes of the first plane, 8 of the second.
+          const int base = code0[t] + (k0 >> log2_bs) * (3 * bsz / 8);
+          const int i0 = k0 & (bsz - 1);
+          const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rbc, ok ? base + i0 / 4 : OOB_A, 0, 0);
+          const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(rbc, ok ? base + bsz / 4 + i0 / 8 : OOB_A, 0, 0);
+          cw[t][0] = lo.x; cw[t][1] = lo.y; cw[t][2] = lo.z; cw[t][3] = lo.w;
+          cw[t][4] = hi.x; cw[t][5] = hi.y;
+        } else {
+          // 2 (bs 32) or 4 (bs 16) whole blocks: 24 contiguous bytes.
+          const int base = ok ? code0[t] + 3 * (k0 / 8) : OOB_A;
+          if (bsz == 32) {
+            // [plane 2: 8][plane 1: 4] twice, 4-byte aligned.
+            const u32x2 a0 = __builtin_amdgcn_raw_buffer_load_b64(rbc, base, 0, 0);
+            const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b32(rbc, base + 8, 0, 0);
+            const u32x2 a1 = __builtin_amdgcn_raw_buffer_load_b64(rbc, base + 12, 0, 0);
+            const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b32(rbc, base + 20, 0, 0);
+            cw[t][0] = a0.x; cw[t][1] = a0.y; cw[t][2] = a1.x; cw[t][3] = a1.y;
+            cw[t][4] = b0; cw[t][5] = b1;
+          } else {
+            // [plane 2: 4][plane 1: 2] four times, 2-byte aligned.
+            uint32_t h[12];
 #pragma unroll
-      for (int v = 0; v < LW; v += 4) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rbc, off + 4 * v, 0, 0);
-        cw[t][v] = x.x; cw[t][v + 1] = x.y; cw[t][v + 2] = x.z; cw[t][v + 3] = x.w;
+            for (int i = 0; i < 12; ++i) h[i] = __builtin_amdgcn_raw_buffer_load_b16(rbc, base + 2 * i, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cw[t][j] = h[3 * j] | (h[3 * j + 1] << 16);
+            cw[t][4] = h[2] | (h[5] << 16);
+            cw[t][5] = h[8] | (h[11] << 16);
+          }
+        }
+      } else {
+        const int off = ok ? code0[t] + chunk * code_chunk : OOB_A;
+#pragma unroll
+        for (int v = 0; v < LW; v += 4) {
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rbc, off + 4 * v, 0, 0);
+          cw[t][v] = x.x; cw[t][v + 1] = x.y; cw[t][v + 2] = x.z; cw[t][v + 3] = x.w;
+        }
       }
     }
   };
@@ -190,8 +240,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
       const int base = row < M ? (row * K + st * SK_KSTEP + 8 * g) * 2 : OOB_A;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        // K % 8 == 0: 8 activations are all in or all out.  OOB_A + 448
-        // stays past the extent and below 2^31.
+        // K % 8 == 0: 8 activations are all in or all out.
         const bool ok = whole || st * SK_KSTEP + 32 * s + 8 * g < K;
         ar[i][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? base + 64 * s : OOB_A, 0, 0);
       }
@@ -217,7 +266,14 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
         if (d > 0 && d >= nbl) break;
         const int bd = min(b0 + d, kb - 1);
         sd[d] = scale_at(t, bd, ok);
-        if constexpr (HAS_ZP) {
+        if constexpr (HAS_ZP && BITS == 3) {
+          // 3-bit zero points may straddle bytes: the 4 bytes from the
+          // first block's hold every block's (at most 7 + 4 * 3 bits).
+          if (d == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zb |= zp_byte((zb0[t] >> 3) + ((b0 * 3) >> 3) + i, ok) << (8 * i);
+          }
+        } else if constexpr (HAS_ZP) {
           if (TL) {
             const int bit = zb0[t] + bd * zb_stride;
             zb |= ((zp_byte(bit >> 3, ok) >> (bit & 7)) & ZM) << (8 * d);
@@ -236,7 +292,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
         else if (d == 3) sv = sd[3];
         uint32_t z = 1u << (BITS - 1);
         if constexpr (HAS_ZP) {
-          if (TL) z = (zb >> (8 * d)) & ZM;
+          if (TL && BITS != 3) z = (zb >> (8 * d)) & ZM;
           else z = (zb >> (((b0 * BITS) & 7) + d * BITS)) & ZM;
         }
         sfq[t][j] = sv;
@@ -372,13 +428,20 @@ static hipError_t launch_skinny_t(const MatArgs& a) {
   // slack of their 16-byte aligned copies).
   const int64_t cols = a.tiled ? TG : 16 * TN;
   const int64_t zrow = a.tiled ? a.kb * 4 * BITS : cols * a.zp_row_bytes;
-  const int64_t lds = (cols * a.kb * SZ + 15 + 15) / 16 * 16 + (HAS_ZP ? (zrow + 15 + 15) / 16 * 16 : 0);
+  const int64_t zslack = BITS == 3 ? 4 : 0;
+  const int64_t lds = (cols * a.kb * SZ + 15 + 15) / 16 * 16 + (HAS_ZP ? (zrow + zslack + 15 + 15) / 16 * 16 : 0);
   const bool slab = lds <= SK_SLAB_MAX;
   decltype(&gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, false>) kern;
-  if (slab) kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, true, true>
-                           : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, true>;
-  else kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, true, false>
-                      : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, false>;
+  if constexpr (BITS == 3) {      // operator layout only
+    kern = slab ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, true>
+                : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, false>;
+  } else if (slab) {
+    kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, true, true>
+                   : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, true>;
+  } else {
+    kern = a.tiled ? gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, true, false>
+                   : gemm_skinny_kernel<BITS, XDT, SDT, HAS_ZP, TN, MT, false, false>;
+  }
   if (slab) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, SK_SLAB_MAX);
     if (e != hipSuccess) return e;
@@ -421,16 +484,18 @@ bool gemm_skinny_supported(const MatArgs& a) {
   // Past the limit the 256-row kernel, whose workgroups each cover many
   // rows, is faster: every workgroup here dequantizes its columns afresh.
   const bool few = a.M <= 16 || ((a.M + 31) / 32) * ((a.N + 31) / 32) <= SKINNY_MAX_GROUPS;
-  return a.a_dtype != DT_F32 && a.bits != 3 && !a.g_idx && a.M >= 2 && few &&
-         (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 <= 0x7FFFE000LL &&
-         (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
-         (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 < 0x7FFFFF00LL &&
-         (a.N + 32) * a.kb * sz < 0x7FFFFF00LL;
+  constexpr int64_t LIM = 0x7FFFE000LL;       // every buffer extent (OOB_A in the kernel)
+  return a.a_dtype != DT_F32 && !(a.bits == 3 && a.tiled) && !a.g_idx && a.M >= 2 && few &&
+         (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 && a.M * a.K * 2 <= LIM &&
+         (a.N + 32) * a.kb * a.blob + 256 <= LIM &&
+         (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 <= LIM &&
+         (a.N + 32) * a.kb * sz <= LIM && (a.N + 32) * (a.zp_row_bytes + 4) <= LIM;
 }
 
 hipError_t launch_gemm_skinny(const MatArgs& a) {
   switch (a.bits) {
     case 2: return launch_skinny_x<2>(a);
+    case 3: return launch_skinny_x<3>(a);
     case 4: return launch_skinny_x<4>(a);
     default: return launch_skinny_x<8>(a);
   }

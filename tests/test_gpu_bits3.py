@@ -9,8 +9,8 @@ Within tol * S of the oracle: qmm_gemv (M = 1) and qmm_gemm for every
 activation dtype, small and large blocks, ragged K and N, with and without
 zero points and bias; CompInt8's output against the oracle's CompInt8 value;
 the decode projection 4096 x 14336 (block 32) and sampled rows of the
-M = 2048 prefill shape strictly.  The matrix-core GEMM (M > 16, 16-bit
-activations) on exact data bit for bit.
+M = 2048 prefill shape strictly.  The matrix-core kernels (few-row and
+256-row, 16-bit activations) on exact data bit for bit.
 """
 import numpy as np
 import pytest
@@ -82,12 +82,14 @@ def test_float_activations_within_tolerance(a_dtype, bs):
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("bs", [16, 32, 64, 128, 1024])
 def test_matrix_core_gemm_exact_data(a_dtype, bs):
-    """M > 16 with 16-bit activations runs the matrix-core GEMM, which decodes
-    the two planes itself: small-integer activations and scale 0.25 make every
-    dequantized weight exact in bf16 / f16 and every sum exact in fp32, so the
-    result is the oracle's rounded once (ragged M, N, K % 64 != 0)."""
+    """16-bit activations run the matrix-core kernels, which decode the two
+    planes themselves: the few-row kernel for the first two shapes, the
+    256-row kernel for the last (35 x 32 workgroups of 32 x 32 outputs, past
+    the few-row limit of 1024).  Small-integer activations and scale 0.25 make
+    every dequantized weight exact in bf16 / f16 and every sum exact in fp32,
+    so the result is the oracle's rounded once (ragged M, N, K % 64 != 0)."""
     rng = np.random.default_rng(bs)
-    for i, (M, K, N) in enumerate([(17, 1032, 33), (300, 2056, 224), (1100, 264, 300)]):
+    for i, (M, K, N) in enumerate([(17, 1032, 33), (300, 2056, 224), (1100, 264, 1000)]):
         K = max(K, bs)
         case = case_of(M, K, N, bs, a_dtype=a_dtype, has_zp=(i != 1), has_bias=True, seed=70 + i)
         case.A = torch.from_numpy(rng.integers(-3, 4, (M, K)).astype(np.float32)).to(case.A.dtype)

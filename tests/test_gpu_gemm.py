@@ -1,13 +1,19 @@
 """GPU parity of the batched / prefill matmul (qmm_gemm, M > 1).
 
+qmm_gemm routes by shape (16-bit activations, K % 8 == 0): the few-row
+kernel when M <= 16 or its grid of 32 x 32-output workgroups has at most
+1024 of them (tests/test_gpu_skinny.py covers it in depth), else the 256-row
+matrix-core kernel with 64-, 128-, 224- or 256-column tiles; f32 activations
+and K % 8 != 0 take the fp32 row kernel.  Here:
+
 * Exact data (small-integer activations, power-of-two scales): every
   dequantized weight is representable in bf16/f16 and every partial sum is
   exact in fp32, so the result must equal the oracle's value rounded once to
-  the output dtype -- on the MFMA path and the fp32 fallback, with ragged
-  M, N and K.
-* Random data within tol * S (the MFMA path rounds each dequantized weight
-  to the activation dtype; for bf16 that is within tolerance statistically,
-  on K >= 512).
+  the output dtype -- on every route and every column-tile width of the
+  256-row kernel, with ragged M, N and K, on both layouts.
+* Random data within tol * S (the matrix-core kernels round each dequantized
+  weight to the activation dtype; for bf16 that is within tolerance
+  statistically, on K >= 512).
 * The full prefill workload (M = 2048, K = 4096, N = 14336), every output of
   a sample of rows.
 """
@@ -59,8 +65,8 @@ def exact_case(M, K, N, bs, bits, a_dtype, seed):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("bs", [16, 32, 64, 128])
 def test_exact_data_ragged_shapes(a_dtype, bits, bs):
-    # (M, K, N): K % 8 == 0 takes the MFMA path for 16-bit activations when
-    # M > 16; the others take the fp32 fallback.
+    # (M, K, N): 16-bit activations with K % 8 == 0 take the few-row kernel
+    # (small grids); K % 8 != 0 and f32 activations the fp32 row kernel.
     for i, (M, K, N) in enumerate([(2, 64, 7), (17, 96, 33), (33, 1000, 300), (300, 256, 257),
                                    (40, 257, 65), (260, 512, 520)]):
         case = exact_case(M, K, N, bs, bits, a_dtype, seed=1000 * bits + bs + i)
@@ -85,36 +91,51 @@ def test_random_data_within_tolerance(a_dtype, bits):
         print(f"  max |err|/S = {r:.3e}")
 
 
-def test_224_column_tiles_ragged():
-    """N a multiple of 224 (the 224-column tile kernels) with ragged M and K:
-    exact data bit for bit, random data within tolerance, on both layouts."""
+def sampled_rows_within_tolerance(case, y, rows, what):
+    """The oracle on a sample of rows (each over all of K and N)."""
+    A = f64(case.A)[rows]
+    Y, S = oracle.matmul_nbits(A, u8(case.B), f64(case.scales), u8(case.zero_points),
+                               f64(case.bias), case.N, case.K, case.block_size, case.bits)
+    return assert_within(y[rows], Y, S, TOL[case.A.dtype], what)
+
+
+@pytest.mark.parametrize("M,K,N,tile", [(2048, 72, 2100, 128), (2048, 64, 4480, 224),
+                                        (2100, 72, 4704, 224), (2048, 64, 4100, 256)])
+def test_column_tile_widths_exact(M, K, N, tile):
+    """Grids past the few-row limit: the 256-row kernel with 128-, 224- and
+    256-column tiles (64-column ones: test_large_m_ragged), ragged M, N, K,
+    exact data bit for bit on both layouts."""
+    case = exact_case(M, K, N, 32, 4, "bf16", seed=77 + N)
+    print(f"[gemm {tile}-column tiles exact] M={M} K={K} N={N}", flush=True)
+    Y, _ = oracle_matmul(case)
+    expect = torch.from_numpy(Y).to(case.A.dtype)
+    assert torch.equal(run_gemm(case).cpu(), expect), (M, K, N)
+    assert torch.equal(run_gemm_tiled(case).cpu(), expect), ("tiled", M, K, N)
+
+
+def test_224_column_tiles_random_sampled_rows():
+    """Random data on 224-column tiles (M = 2048, N = 4480, K = 1032): 24
+    sampled rows within tolerance; the repacked layout gives the same bits."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
-    for i, (M, K, N) in enumerate([(17, 64, 224), (300, 264, 448), (520, 1000, 672),
-                                   (257, 72, 224)]):
-        case = exact_case(M, K, N, 32, 4, "bf16", seed=77 + i)
-        print(f"[gemm 224 exact] M={M} K={K} N={N}", flush=True)
-        Y, _ = oracle_matmul(case)
-        expect = torch.from_numpy(Y).to(case.A.dtype)
-        assert torch.equal(run_gemm(case).cpu(), expect), (M, K, N)
-        assert torch.equal(run_gemm_tiled(case).cpu(), expect), ("tiled", M, K, N)
-    for i, (M, K, N) in enumerate([(257, 4096, 448), (600, 1032, 224)]):
-        case = make_matmul_case(M, K, N, 32, 4, a_dtype="bf16", has_zp=True, has_bias=True,
-                                seed=90 + i)
-        print(f"[gemm 224 random] M={M} K={K} N={N}", flush=True)
-        Y, S = oracle_matmul(case)
-        y = run_gemm(case)
-        r = assert_within(y, Y, S, TOL[case.A.dtype], "gemm 224 random")
-        print(f"  max |err|/S = {r:.3e}")
-        assert torch.equal(run_gemm_tiled(case), y), ("tiled", M, K, N)
+    case = make_matmul_case(2048, 1032, 4480, 32, 4, a_dtype="bf16", has_zp=True, has_bias=True,
+                            seed=91)
+    print(f"[gemm 224 random] M={case.M} K={case.K} N={case.N}", flush=True)
+    y = run_gemm(case)
+    rows = np.random.default_rng(1).choice(case.M, 24, replace=False)
+    rows[:2] = [0, case.M - 1]
+    r = sampled_rows_within_tolerance(case, y.cpu(), rows, "gemm 224 random")
+    print(f"  max |err|/S = {r:.3e}")
+    assert torch.equal(run_gemm_tiled(case), y)
 
 
 @pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("bs", [16, 32, 64, 128])
 def test_large_m_ragged(a_dtype, bits, bs):
-    """M >= 1024 (several rounds of 256-row tiles, a partial last tile):
-    exact data bit for bit on both layouts, with ragged N and K (K % 64 != 0)."""
-    for i, (M, K, N) in enumerate([(1024, 200, 224), (1100, 264, 300), (1537, 1000, 112)]):
+    """M >= 1024 past the few-row limit (several 256-row tiles, a partial
+    last tile; 64-column tiles): exact data bit for bit on both layouts, with
+    ragged N and K (K % 64 != 0)."""
+    for i, (M, K, N) in enumerate([(1024, 72, 1200), (1537, 136, 700)]):
         case = exact_case(M, K, N, bs, bits, a_dtype, seed=3000 + 10 * bits + bs + i)
         print(f"[gemm large-M exact] M={M} K={K} N={N} bs={bs} bits={bits} a={a_dtype}", flush=True)
         Y, _ = oracle_matmul(case)
