@@ -1,5 +1,6 @@
-// compint8_tiled.hip -- CompInt8 (accuracy_level 4) on the tiled weight
-// layout (qmm_layout.h) with the int8 matrix cores of gfx950.
+// compint8_tiled.hip -- CompInt8 (accuracy_level 4) with the int8 matrix
+// cores of gfx950, on the tiled weight layout (qmm_layout.h) and, for M >= 2,
+// on the operator's layout.
 //
 // Definition (onnx-runtime-ep-cpu matmul_nbits.rs: quantize_activation_signed,
 // int4_dot_row_scalar, int8_row): with qa / sa the int8 activations and their
@@ -22,9 +23,13 @@
 // Work split: a wave owns a slice of 16 columns (half a 32-column group) and
 // a share of the blocks of K; a workgroup holds CS slices x S shares and adds
 // the shares through LDS.  Each chunk costs the wave one load of its codes
-// (the 16 columns' bytes of a chunk are 8 * BITS * 16 contiguous bytes) and
-// one 16-byte load of activations per lane (rows past M read zeros from past
-// the buffer's extent), then two MFMAs.
+// (tiled: the 16 columns' bytes of a chunk are 8 * BITS * 16 contiguous
+// bytes; operator layout (OPL): 8 * BITS bytes of each column's row) and one
+// 16-byte load of activations per lane (rows past M read zeros from past the
+// buffer's extent), then two MFMAs.  On the operator layout the scales and
+// zero points are read with loads of their own width (rows of kb scales and
+// of whole zero-point bytes need not fill 32-bit words: a buffer load zeroes
+// a dword not wholly inside the extent).
 #include "qmm_device.h"
 #include "qmm_internal.h"
 #include "qmm_layout.h"
@@ -107,13 +112,13 @@ struct CtSlot {
 // banks, and its waves read them there (rows past Mp as zeros, by a select);
 // otherwise every wave loads its rows from memory with each chunk.  The CS
 // column slices of the workgroup share the staged rows.
-template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE>
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE, bool OPL>
 __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
     const typename dt<YDT>::T* __restrict__ bias, typename dt<YDT>::T* __restrict__ Y,
     int32_t* __restrict__ dots, int Mp, int N, int kb, int Kp, int chunks, int log2_cpb,
-    int n_slices, int CS, int S) {
+    int n_slices, int CS, int S, int row_bytes, int zp_row_bytes) {
   using G = CtGeom<BITS>;
   using ST = typename dt<SDT>::T;
   constexpr int CB = G::CB, LB = G::LB;
@@ -146,13 +151,15 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
 
   const int groups = (N + TG - 1) / TG;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)codes, 0, groups * chunks * TG * CB, RSRC3);
+      (void*)codes, 0, OPL ? N * row_bytes : groups * chunks * TG * CB, RSRC3);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)qa, 0, Mp * Kp, RSRC3);
+  // No scales (the block-dot export on the operator layout): every scale
+  // load is out of range and reads zero.
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)scales, 0, groups * kb * TG * SZ, RSRC3);
+      (void*)scales, 0, scales ? (OPL ? N * kb : groups * kb * TG) * SZ : 0, RSRC3);
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)zps, 0, HAS_ZP ? groups * kb * TG * BITS / 8 : 0, RSRC3);
+      (void*)zps, 0, HAS_ZP ? (OPL ? N * zp_row_bytes : groups * kb * TG * BITS / 8) : 0, RSRC3);
   // Blocks of this wave's share (whole blocks, so no block is split).
   const int bps = (kb + S - 1) / S;
   const int b_lo = s * bps;
@@ -161,23 +168,40 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   const int c_lo = b_lo * cpb;
   const int nch = max(0, (b_hi - b_lo) * cpb);
 
-  const int lane_code = (grp * chunks * TG + col) * CB + g * LB;
+  // Codes of chunk c: lane_code + c * code_step.  Columns past N read zeros
+  // (tiled: the group's padding; operator layout: past the extent).
+  const int lane_code = OPL ? n * row_bytes + g * LB : (grp * chunks * TG + col) * CB + g * LB;
+  const int code_step = OPL ? CB : TG * CB;
+  // Scale entry of block b: sc_base + b * sc_step; zero-point bit: zb_base +
+  // b * zb_step.
+  const int sc_base = OPL ? n * kb : grp * kb * TG + col, sc_step = OPL ? 1 : TG;
+  const int zb_base = OPL ? n * zp_row_bytes * 8 : (grp * kb * TG + col) * BITS;
+  const int zb_step = OPL ? BITS : TG * BITS;
   const int lane_act = rowA * Kp + g * 16;
   auto issue = [&](CtSlot& sl, int j) {
     const int c = c_lo + j;
     if constexpr (LB == 16)
-      sl.code = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + c * (TG * CB), 0, BUF_STREAM);
+      sl.code = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + c * code_step, 0, BUF_STREAM);
     else if constexpr (LB == 8) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane_code + c * (TG * CB), 0, BUF_STREAM);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane_code + c * code_step, 0, BUF_STREAM);
       sl.code = u32x4{v.x, v.y, 0u, 0u};
     } else {
-      sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * (TG * CB), 0, BUF_STREAM),
+      sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * code_step, 0, BUF_STREAM),
                       0u, 0u, 0u};
     }
     if constexpr (!STAGE) sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);
-    const int si = (grp * kb + (c >> log2_cpb)) * TG + col;
-    sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (si * SZ) & ~3, 0, 0);
-    if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, ((si * BITS) >> 5) * 4, 0, 0);
+    const int b = c >> log2_cpb;
+    const int si = sc_base + b * sc_step;
+    const int zbit = zb_base + b * zb_step;
+    if constexpr (OPL) {
+      // The value itself (shifted back to bit 0 of the word on use).
+      if constexpr (SZ == 4) sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, si * 4, 0, 0);
+      else sl.sw = __builtin_amdgcn_raw_buffer_load_b16(rs, si * 2, 0, 0);
+      if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b8(rz, zbit >> 3, 0, 0);
+    } else {
+      sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (si * SZ) & ~3, 0, 0);
+      if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, ((zbit) >> 5) * 4, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -214,12 +238,13 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     asum = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones, asum, 0, 0, 0);
     if (((j + 1) & (cpb - 1)) == 0) {
       const int b = b_lo + (j >> log2_cpb);
-      const int si = (grp * kb + b) * TG + col;
+      const int si = sc_base + b * sc_step;
+      const int zbit = zb_base + b * zb_step;
       float sc;
       if constexpr (SZ == 4) sc = __uint_as_float(sl.sw);
-      else sc = bits16_to_f32<SDT>((uint16_t)(sl.sw >> ((si & 1) * 16)));
+      else sc = bits16_to_f32<SDT>((uint16_t)(OPL ? sl.sw : sl.sw >> ((si & 1) * 16)));
       int z = 1 << (BITS - 1);
-      if constexpr (HAS_ZP) z = (int)((sl.zw >> ((si * BITS) & 31)) & m);
+      if constexpr (HAS_ZP) z = (int)((sl.zw >> (zbit & (OPL ? 7 : 31))) & m);
       const f32x4 s4 = *reinterpret_cast<const f32x4*>(saT + b * 16 + 4 * g);
       const int zo = z - OFF;
 #pragma unroll
@@ -278,7 +303,7 @@ template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE>
 hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
   const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
                                   a.zp != nullptr);
-  const int chunks = (int)tg.chunks;
+  const int chunks = (int)tg.chunks;             // kb * bs / 64 on either layout
   const int log2_cpb = __builtin_ctz((unsigned)(a.block_size / TKC));
   const int n_slices = (int)tg.groups * 2;
   const int Kp = (int)(a.kb * a.block_size);
@@ -292,7 +317,8 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   while (CS * S < maxw && (a.kb + 2 * S - 1) / (2 * S) >= 2) S *= 2;
   const int rows = (int)std::min<int64_t>(16, a.M);
   const size_t lds = ct_lds(a.kb, Kp, CS, S, STAGE, rows);
-  auto kern = compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE>;
+  auto kern = a.tiled ? compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, false>
+                      : compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true>;
   if (lds > 64 * 1024) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)CT_STAGE_LDS_MAX);
     if (e != hipSuccess) return e;
@@ -303,10 +329,11 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
     const int Mp = (int)std::min<int64_t>(16, a.M - m0);
     hipLaunchKernelGGL(kern, dim3(grid),
                        dim3(CS * S * 64), lds, a.stream, qa + m0 * Kp, sa + m0 * a.kb,
-                       a.B + tg.codes_off, (const uint8_t*)a.scales, a.zp, (const YT*)a.bias,
-                       DOTS ? nullptr : (YT*)a.Y + m0 * a.N,
+                       a.B + (a.tiled ? tg.codes_off : 0), (const uint8_t*)a.scales, a.zp,
+                       (const YT*)a.bias, DOTS ? nullptr : (YT*)a.Y + m0 * a.N,
                        DOTS ? dots + m0 * a.N * a.kb : nullptr, Mp, (int)a.N, (int)a.kb, Kp,
-                       chunks, log2_cpb, n_slices, CS, S);
+                       chunks, log2_cpb, n_slices, CS, S, (int)(a.kb * a.blob),
+                       (int)a.zp_row_bytes);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -362,11 +389,16 @@ hipError_t launch_b(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
 
 bool compint8_tiled_supported(const MatArgs& a) {
   // Whole blocks of 64-code chunks; LDS for the activation scales; 32-bit
-  // offsets.
+  // offsets (operator layout: the code rows, the scale rows and the
+  // zero-point rows of N + 32 columns, the slices' padding).
   const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
                                   a.zp != nullptr);
-  return a.block_size >= TKC && (a.kb * 16 + 8 * 256) * 4 <= 64 * 1024 &&
-         tg.total < 0x7FFFFF00LL && 16 * a.kb * a.block_size < 0x7FFFFF00LL;
+  const bool fits = a.tiled ? tg.total < 0x7FFFFF00LL
+                            : (a.N + 32) * a.kb * a.blob < 0x7FFFFF00LL &&
+                                  (a.N + 32) * a.kb * 4 < 0x7FFFFF00LL &&
+                                  (a.N + 32) * a.zp_row_bytes * 8 < 0x7FFFFF00LL;
+  return a.bits != 3 && a.block_size >= TKC && (a.kb * 16 + 8 * 256) * 4 <= 64 * 1024 && fits &&
+         16 * a.kb * a.block_size < 0x7FFFFF00LL;
 }
 
 hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa) {

@@ -277,7 +277,8 @@ int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t
   hipError_t e = launch_quantize_a(a, qa, sa);
   if (e == hipSuccess) {
     if (a.bits == 3) e = launch_generic_int(a, qa, 1, sa, nullptr);
-    else e = a.tiled ? launch_compint8_tiled(a, qa, sa) : launch_compint8(a, qa, sa);
+    else if (a.tiled || (a.M >= 2 && compint8_tiled_supported(a))) e = launch_compint8_tiled(a, qa, sa);
+    else e = launch_compint8(a, qa, sa);
   }
   return hip_status(e, fn);
 }
@@ -611,8 +612,9 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
   if (e == hipSuccess) e = qmm::launch_quantize_a(a, qa, sa);
   if (e == hipSuccess) {
     if (a.bits == 3) e = qmm::launch_generic_int(a, qa, 1, sa, dots);
-    else e = a.tiled ? qmm::launch_compint8_tiled_dots(a, qa, sa, dots)
-                     : qmm::launch_compint8_dots(a, qa, sa, dots);
+    else if (a.tiled || (a.M >= 2 && qmm::compint8_tiled_supported(a)))
+      e = qmm::launch_compint8_tiled_dots(a, qa, sa, dots);
+    else e = qmm::launch_compint8_dots(a, qa, sa, dots);
   }
   return hip_status(e, "qmm_debug_compint8_block_dots");
 }
