@@ -1,26 +1,23 @@
-// gemm.hip -- batched / prefill matmul over block-quantized weights for gfx950.
+// gemm.hip -- batched / prefill matmul over block-quantized weights for gfx950:
+// the routing of qmm_gemm, the 256-row matrix-core kernel's 224- and
+// 256-column instances (template in gemm_mfma.h; 64- and 128-column ones in
+// gemm_narrow.hip), its group-index and FP4 variants, and the fp32 row
+// kernel.
 //
 // Y[M, N] = A[M, K] * W^T with W[n, k] = (code - zp) * scale (onnx-runtime-ep-cpu
 // matmul_nbits.rs: the batched route dequantizes then multiplies; here the
-// weight is dequantized tile by tile inside the kernel and never written to
+// weight is dequantized tile by tile inside the kernels and never written to
 // memory).
 //
-// gemm_mfma_kernel (bf16 / f16 activations): a workgroup of 8 waves computes a
-// 256 x BN tile of Y (BN = 224 or 256), each wave 64 x BN/2 as 4 x BN/32
-// v_mfma_f32_16x16x32_{bf16,f16} tiles accumulated in fp32.  Per K-step of
-// 64: the A tile is copied to LDS, the B tile is dequantized once for the
-// whole workgroup (each thread 32 codes of one column: unpack, subtract the
-// zero point, multiply by the block scale in fp32, round to the activation
-// dtype) and stored to LDS; then every wave reads its operand fragments from
-// LDS.  LDS rows are 128 bytes with their 16-byte pieces XOR-permuted by the
-// row (lds_at), so the 16 rows of a fragment read fall in distinct bank
-// groups.  Loads of A and of the codes go through buffer descriptors whose
-// extents end at M, K and N, so ragged edges read zeros.
-//
-// gemm_rows_kernel (fallback: f32 activations, small M, unaligned operands):
-// fp32 throughout -- each wave owns R output columns, stages MT rows of A in
-// LDS as fp32 and accumulates exact (code - zp) * x products per block in fp32
-// before scaling.
+// Routes (launch_gemm): group indices -> gidx.hip; 16-bit activations with
+// K % 8 == 0 -> the few-row kernel (gemm_skinny.hip) when M <= 16 or its
+// grid has at most 1024 workgroups, else gemm_mfma_kernel with the narrowest
+// column tile whose grid still fits one round of the compute units (64 / 128
+// columns) or 224 / 256 columns; otherwise (f32 activations, K % 8 != 0,
+// offsets past 2^31) gemm_rows_kernel, fp32 throughout -- each wave owns R
+// output columns, stages MT rows of A in LDS as fp32 and accumulates exact
+// (code - zp) * x products per block in fp32 before scaling (3-bit weights:
+// the generic kernel).
 #include <algorithm>
 #include <type_traits>
 

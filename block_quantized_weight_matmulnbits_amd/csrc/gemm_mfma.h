@@ -3,6 +3,18 @@
 // by gemm.hip (224- and 256-column tiles, group indices, FP4) and
 // gemm_narrow.hip (64- and 128-column tiles), so that the two instantiation
 // sets compile in parallel.
+//
+// A workgroup of 8 waves computes a 256 x BN tile of Y, each wave 64 x BN/2
+// as 4 x BN/32 v_mfma_f32_16x16x32_{bf16,f16} tiles accumulated in fp32.
+// Per K-step of 64: the A tile goes from memory straight into LDS, the B
+// tile is dequantized once for the whole workgroup (each thread 32 codes of
+// one column: unpack, subtract the zero point, multiply by the block scale in
+// fp32, round to the activation dtype) and stored to LDS; then every wave
+// reads its operand fragments from LDS.  LDS rows are 128 bytes with their
+// 16-byte pieces XOR-permuted by the row (lds_at), so the 16 rows of a
+// fragment read fall in distinct bank groups.  Loads of A and of the codes
+// go through buffer descriptors whose extents end at M, K and N, so ragged
+// edges read zeros.
 #pragma once
 
 #include <algorithm>
