@@ -625,8 +625,9 @@ def bench_compint8(qmm, dev, stream, args):
 
 def bench_fp4(qmm, dev, stream, args):
     """Block-scaled FP4 weights (MXFP4 / NVFP4), bf16 activations: the decode
-    GEMV on a 4096 x 14336 projection (weights rotating through copies, so
-    they stream from HBM) and the prefill GEMM M=2048 K=4096 N=14336."""
+    GEMV and batched decode at M = 16 on a 4096 x 14336 projection (weights
+    rotating through copies, so they stream from HBM) and the prefill GEMM
+    M=2048 K=4096 N=14336."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
     res = {}
     for fmt in ("mxfp4", "nvfp4"):
@@ -641,6 +642,18 @@ def bench_fp4(qmm, dev, stream, args):
             qmm.qmm_gemm_fp4(c.A, W, S, c.fmt, c.global_scale, None, y, 1, c.K, c.N, stream)
 
         ms = _time_launches(run, max(20, args.steps), stream)
+        a16 = make_fp4_case(16, 4096, 14336, fmt, a_dtype="bf16", seed=43).A.to(dev)
+        y16 = torch.empty(16, c.N, dtype=torch.bfloat16, device=dev)
+
+        def run16(i, c=c, pool=pool, a16=a16, y16=y16):
+            W, S = pool[i % len(pool)]
+            qmm.qmm_gemm_fp4(a16, W, S, c.fmt, c.global_scale, None, y16, 16, c.K, c.N, stream)
+
+        for i in range(3):
+            run16(i)
+        torch.cuda.synchronize()
+        ms16 = _time_launches(run16, max(20, args.steps // 4), stream)
+        b16 = nbytes + 15 * c.K * 2 + 15 * c.N * 2
         del pool
         p = make_fp4_case(2048, 4096, 14336, fmt, a_dtype="bf16", seed=42).to(dev)
         Y = torch.empty(p.M, p.N, dtype=torch.bfloat16, device=dev)
@@ -658,6 +671,9 @@ def bench_fp4(qmm, dev, stream, args):
             "gemv_K4096_N14336": {"us": round(ms * 1e3, 3), "bytes": nbytes,
                                   "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                   "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "batched_M16_K4096_N14336": {"us": round(ms16 * 1e3, 3), "bytes": b16,
+                                         "GBps": round(b16 / (ms16 * 1e-3) / 1e9, 1),
+                                         "frac_hbm": round(b16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "prefill_M2048_K4096_N14336": {"ms": round(msp, 4),
                                            "tflops": round(flop / (msp * 1e-3) / 1e12, 2),
                                            "frac_bf16_peak": round(

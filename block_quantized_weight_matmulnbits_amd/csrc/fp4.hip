@@ -278,6 +278,7 @@ hipError_t launch_fp4_t(const Fp4Args& a) {
                        a.scales, a.global_scale, a.bias, a.Y, (int)a.K, (int)a.N, (int)a.kb);
     return hipGetLastError();
   }
+  if (gemm_skinny_fp4_supported(a)) return launch_gemm_skinny_fp4(a);
   if (gemm_mfma_fp4_supported(a)) return launch_gemm_mfma_fp4(a);
   constexpr int MT = 8;
   const int grid = (int)((a.N + 7) / 8);

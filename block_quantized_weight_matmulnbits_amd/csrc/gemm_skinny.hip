@@ -82,14 +82,21 @@ __device__ __forceinline__ void step_codes(const uint32_t* cw, int s, float* q) 
 // its group (kb x 32 scales, 4 kb bits bytes of zero points).  With SLAB the
 // workgroup copies both ranges into LDS once (16-byte loads) and every lookup
 // reads LDS.
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, int MT, bool TL, bool SLAB>
+//
+// WF: block-scaled FP4 weights (1 + FP4_MX or 1 + FP4_NV; operator layout,
+// BITS = 4, no zero points): codes are E2M1 values, scales one E8M0 / E4M3
+// byte per block, and the sums are multiplied by gscale.  Each weight,
+// e2m1 * scale, has at most 6 significant bits, so its rounding to the
+// activation dtype is exact.
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, int MT, bool TL, bool SLAB, int WF = 0>
 __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int K, int N, int kb,
-    int log2_bs, int row_bytes, int zp_row_bytes, int chunks) {
+    int log2_bs, int row_bytes, int zp_row_bytes, int chunks, float gscale) {
   static_assert(TN == 1 || TN == 2, "16 or 32 columns: within one group of the tiled layout");
   static_assert(BITS != 3 || !TL, "3-bit weights: operator layout");
+  static_assert(!WF || (BITS == 4 && !TL && !HAS_ZP), "FP4 weights: operator layout");
   using Op = MfmaOp<XDT>;
   using ST = typename dt<SDT>::T;
   constexpr int LW = 2 * BITS;                 // code words per lane and tile (64 codes)
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   // the constant offsets added to it below 2^31.
   constexpr int OOB_A = 0x7FFFE000;
   constexpr uint32_t ZM = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
-  constexpr int SZ = (int)sizeof(typename dt<SDT>::T);
+  constexpr int SZ = WF ? 1 : (int)sizeof(typename dt<SDT>::T);   // bytes per scale
   __shared__ float red[SK_WAVES / 2][MT * TN * 4][64];
   extern __shared__ __attribute__((aligned(16))) uint8_t slab_lds[];
 
@@ -153,6 +160,11 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
   // Scale (as fp32) and zero point of block b of tile t.
   auto scale_at = [&](int t, int b, bool ok) -> float {
     const int e = sc0[t] + b * sc_stride;
+    if constexpr (WF) {
+      const uint32_t byte = SLAB ? (uint32_t)slab_lds[(s_lo - s_al) + e]
+                                 : __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? s_lo + e : OOB, 0, 0);
+      return fp4_scale(byte, WF - 1);
+    }
     ST v;
     if constexpr (SLAB) {
       v = *reinterpret_cast<const ST*>(slab_lds + (s_lo - s_al) + e * SZ);
@@ -290,7 +302,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
         if (d == 1) sv = sd[1];
         else if (d == 2) sv = sd[2];
         else if (d == 3) sv = sd[3];
-        uint32_t z = 1u << (BITS - 1);
+        uint32_t z = WF ? 0u : 1u << (BITS - 1);
         if constexpr (HAS_ZP) {
           if (TL && BITS != 3) z = (zb >> (8 * d)) & ZM;
           else z = (zb >> (((b0 * BITS) & 7) + d * BITS)) & ZM;
@@ -326,7 +338,18 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         float q[8];
-        step_codes<BITS>(cw[t], s, q);
+        if constexpr (WF) {
+          // Byte j of the word: E2M1 values of codes 2j (low nibble), 2j + 1.
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          const f2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t][s], 1.0f, 0);
+          const f2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t][s], 1.0f, 1);
+          const f2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t][s], 1.0f, 2);
+          const f2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[t][s], 1.0f, 3);
+          q[0] = c0.x; q[1] = c0.y; q[2] = c1.x; q[3] = c1.y;
+          q[4] = c2.x; q[5] = c2.y; q[6] = c3.x; q[7] = c3.y;
+        } else {
+          step_codes<BITS>(cw[t], s, q);
+        }
         const float sv = sfq[t][s >> 1], zv = zsq[t][s >> 1];
         u32x4 pk;
         pk.x = Op::pack(fmaf(q[0], sv, -zv), fmaf(q[1], sv, -zv));
@@ -405,7 +428,7 @@ __global__ __launch_bounds__(SK_TPB, 2) void gemm_skinny_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + 16 * i + 4 * g + e;
-        if (m < M) Y[(int64_t)m * N + n] = Op::round(acc[i][t][e] + bv);
+        if (m < M) Y[(int64_t)m * N + n] = Op::round((WF ? acc[i][t][e] * gscale : acc[i][t][e]) + bv);
       }
   }
 }
@@ -449,7 +472,7 @@ static hipError_t launch_skinny_t(const MatArgs& a) {
   hipLaunchKernelGGL(kern, grid, dim3(SK_TPB), slab ? (size_t)lds : 0, a.stream, (const uint16_t*)a.A,
                      a.B, (const ST*)a.scales, a.zp, (const uint16_t*)a.bias, (uint16_t*)a.Y, (int)a.M,
                      (int)a.K, (int)a.N, (int)a.kb, sk_log2(a.block_size), (int)(a.kb * a.blob),
-                     (int)a.zp_row_bytes, (int)a.chunks);
+                     (int)a.zp_row_bytes, (int)a.chunks, 1.0f);
   return hipGetLastError();
 }
 
@@ -490,6 +513,50 @@ bool gemm_skinny_supported(const MatArgs& a) {
          (a.N + 32) * a.kb * a.blob + 256 <= LIM &&
          (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 <= LIM &&
          (a.N + 32) * a.kb * sz <= LIM && (a.N + 32) * (a.zp_row_bytes + 4) <= LIM;
+}
+
+// FP4 weights: the operator-layout 4-bit geometry with blocks of 32 (MXFP4)
+// or 16 (NVFP4), one scale byte per block, no zero points.
+template <int XDT, int WF, int TN, int MT>
+static hipError_t launch_skinny_fp4_t(const Fp4Args& f) {
+  const int64_t bs = (WF - 1) == FP4_MX ? 32 : 16;
+  const dim3 grid((unsigned)((f.N + 16 * TN - 1) / (16 * TN)), (unsigned)((f.M + 16 * MT - 1) / (16 * MT)));
+  const int64_t lds = (16 * TN * f.kb + 15 + 15) / 16 * 16;
+  const bool slab = lds <= SK_SLAB_MAX;
+  auto kern = slab ? gemm_skinny_kernel<4, XDT, DT_BF16, false, TN, MT, false, true, WF>
+                   : gemm_skinny_kernel<4, XDT, DT_BF16, false, TN, MT, false, false, WF>;
+  if (slab) {
+    const hipError_t e = ensure_dynamic_lds((const void*)kern, SK_SLAB_MAX);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(SK_TPB), slab ? (size_t)lds : 0, f.stream, (const uint16_t*)f.A,
+                     f.W, (const uint16_t*)f.scales, (const uint8_t*)nullptr, (const uint16_t*)f.bias,
+                     (uint16_t*)f.Y, (int)f.M, (int)f.K, (int)f.N, (int)f.kb, sk_log2(bs),
+                     (int)(f.kb * bs / 2), 0, 0, f.global_scale);
+  return hipGetLastError();
+}
+
+template <int XDT, int WF>
+static hipError_t launch_skinny_fp4_m(const Fp4Args& f) {
+  const int64_t row_tiles = f.M <= 16 ? 1 : (f.M + 31) / 32;
+  const bool narrow = row_tiles * ((f.N + 31) / 32) < SK_FULL_ROUND;
+  if (f.M <= 16) return narrow ? launch_skinny_fp4_t<XDT, WF, 1, 1>(f) : launch_skinny_fp4_t<XDT, WF, 2, 1>(f);
+  return narrow ? launch_skinny_fp4_t<XDT, WF, 1, 2>(f) : launch_skinny_fp4_t<XDT, WF, 2, 2>(f);
+}
+
+bool gemm_skinny_fp4_supported(const Fp4Args& f) {
+  const int64_t bs = f.format == FP4_MX ? 32 : 16;
+  const bool few = f.M <= 16 || ((f.M + 31) / 32) * ((f.N + 31) / 32) <= SKINNY_MAX_GROUPS;
+  constexpr int64_t LIM = 0x7FFFE000LL;
+  return f.a_dtype != DT_F32 && f.M >= 2 && few && (f.K % 8) == 0 && ((uintptr_t)f.A & 15) == 0 &&
+         f.M * f.K * 2 <= LIM && (f.N + 32) * f.kb * (bs / 2) + 256 <= LIM && (f.N + 32) * f.kb <= LIM;
+}
+
+hipError_t launch_gemm_skinny_fp4(const Fp4Args& f) {
+  const bool f16 = f.a_dtype == DT_F16;
+  if (f.format == FP4_MX)
+    return f16 ? launch_skinny_fp4_m<DT_F16, 1 + FP4_MX>(f) : launch_skinny_fp4_m<DT_BF16, 1 + FP4_MX>(f);
+  return f16 ? launch_skinny_fp4_m<DT_F16, 1 + FP4_NV>(f) : launch_skinny_fp4_m<DT_BF16, 1 + FP4_NV>(f);
 }
 
 hipError_t launch_gemm_skinny(const MatArgs& a) {

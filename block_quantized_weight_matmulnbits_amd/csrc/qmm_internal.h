@@ -88,6 +88,9 @@ hipError_t launch_fp4(const Fp4Args& a);
 // The matrix-core GEMM on FP4 weights (gemm.hip): 16-bit activations, M > 16.
 bool gemm_mfma_fp4_supported(const Fp4Args& a);
 hipError_t launch_gemm_mfma_fp4(const Fp4Args& a);
+// FP4 weights on the few-row kernel (gemm_skinny.hip), the same routing rule.
+bool gemm_skinny_fp4_supported(const Fp4Args& a);
+hipError_t launch_gemm_skinny_fp4(const Fp4Args& a);
 
 // int8 convolution (validated NHWC / OHWI problem).
 struct ConvArgs {

@@ -2,8 +2,9 @@
 
 rlx-cpu quant.rs (dequant_matmul_nvfp4, lowp_dequantize): w = e2m1(code) *
 block scale (* global scale).  MXFP4 (E8M0 per 32) and NVFP4 (E4M3 per 16),
-f32 / bf16 / f16 activations, M = 1 (the GEMV), small M (fp32 rows) and
-M > 16 (matrix cores for 16-bit activations), ragged K and N.  Exact data
+f32 / bf16 / f16 activations, M = 1 (the GEMV), the few-row and 256-row
+matrix-core kernels for 16-bit activations, the fp32 row kernel (f32, K % 8
+!= 0), ragged K and N.  Exact data
 (small-integer activations, power-of-two scales) must equal the oracle's
 value rounded once to the output dtype; random data is within tol * S
 (strictly on a decode-size projection).  Every E2M1 code and every scale
@@ -62,7 +63,11 @@ def test_exact_data_bit_for_bit(fmt, a_dtype):
     value rounded once."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_fp4_case
     rng = np.random.default_rng(7)
-    for i, (M, K, N) in enumerate([(1, 256, 40), (5, 300, 17), (40, 512, 300)]):
+    # M = 1: the GEMV; K % 8 != 0 and f32: the fp32 row kernel; (40, 512,
+    # 300): the few-row kernel; (1100, 256, 1000): the 256-row kernel (35 x 32
+    # workgroups of 32 x 32 outputs, past the few-row limit).
+    for i, (M, K, N) in enumerate([(1, 256, 40), (5, 300, 17), (40, 512, 300),
+                                   (1100, 256, 1000)]):
         case = make_fp4_case(M, K, N, fmt, a_dtype=a_dtype, has_bias=True, seed=i)
         case.A = torch.from_numpy(rng.integers(-3, 4, (M, K)).astype(np.float32)).to(case.A.dtype)
         kb = case.scales.shape[1]
