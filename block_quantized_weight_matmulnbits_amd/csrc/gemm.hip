@@ -145,13 +145,18 @@ static hipError_t launch_rows(const MatArgs& a) {
 }
 
 // Every buffer offset of the MFMA kernel must fit in 31 bits.
-static bool mfma_fits(const MatArgs& a) {
+// Shapes the 256-row kernel takes: 16-bit activations, K % 8 == 0, A 16-byte
+// aligned, every byte offset below 2^31 (with a column tile's slack past N).
+static bool mfma_shape_fits(const MatArgs& a) {
   const int64_t sz = a.s_dtype == DT_F32 ? 4 : 2;
-  return a.a_dtype != DT_F32 && a.M > 16 && (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 &&
+  return a.a_dtype != DT_F32 && (a.K % 8) == 0 && ((uintptr_t)a.A & 15) == 0 &&
          a.M * a.K * 2 < 0x7FFFFF00LL && (a.N + 32) * a.kb * a.blob + 256 < 0x7FFFFF00LL &&
          (a.N + 32) * (a.chunks + 2) * 64 * a.bits / 8 < 0x7FFFFF00LL &&
-         (a.N + 32) * a.kb * sz < 0x7FFFFF00LL && a.K * 4 < 0x7FFFFF00LL;
+         (a.N + 256) * a.kb * sz < 0x7FFFFF00LL && (a.N + 256) * a.zp_row_bytes < 0x7FFFFF00LL &&
+         a.K * 4 < 0x7FFFFF00LL;
 }
+
+static bool mfma_fits(const MatArgs& a) { return a.M > 16 && mfma_shape_fits(a); }
 
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 static hipError_t launch_gemm_t(const MatArgs& a) {
@@ -201,8 +206,8 @@ template <int BITS, int XDT, int SDT, bool HAS_ZP>
 static hipError_t launch_gidx_t(const MatArgs& a) {
   using ST = typename dt<SDT>::T;
   const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
-  constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);
-  auto kern = gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false, true>;
+  constexpr size_t lds = mfma_lds_bytes<GBN>();
+  auto kern = gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, 8, false, 1>;
   const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
@@ -231,7 +236,18 @@ static hipError_t launch_gidx_x(const MatArgs& a) {
   return a.a_dtype == DT_F16 ? launch_gidx_s<BITS, DT_F16>(a) : launch_gidx_s<BITS, DT_BF16>(a);
 }
 
-bool gemm_mfma_gidx_supported(const MatArgs& a) { return !a.tiled && mfma_fits(a); }
+// Group indices: the tabled kernel (gidx_mfma.hip) for M >= 2 when its
+// table fits in LDS beside the 64-column tiles, else, for M > 16, the
+// 256-column kernel with lookups in memory.
+// (Its group indices are read 16 bytes at a time: 16-byte aligned.)
+static bool gidx_table_fits(const MatArgs& a, int bn) {
+  return ((uintptr_t)a.g_idx & 15) == 0 &&
+         (bn == 64 ? mfma_lds_bytes<64>() : mfma_lds_bytes<128>()) + gidx_table_bytes(a, bn) <= LDS_MAX;
+}
+
+bool gemm_mfma_gidx_supported(const MatArgs& a) {
+  return !a.tiled && a.M >= 2 && mfma_shape_fits(a) && (a.M > 16 || gidx_table_fits(a, 64));
+}
 
 // FP4 weights on the matrix cores: the 4-bit operator-layout geometry with
 // blocks of 32 (MXFP4) or 16 (NVFP4) and one scale byte per block.
@@ -252,8 +268,8 @@ template <int XDT, int WF>
 static hipError_t launch_fp4_mfma_t(const Fp4Args& f) {
   const MatArgs a = fp4_as_mat(f);
   const int tiles_m = (int)((a.M + GBM - 1) / GBM), tiles_n = (int)((a.N + GBN - 1) / GBN);
-  constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);
-  auto kern = gemm_mfma_kernel<4, XDT, DT_BF16, false, 8, false, false, WF>;
+  constexpr size_t lds = mfma_lds_bytes<GBN>();
+  auto kern = gemm_mfma_kernel<4, XDT, DT_BF16, false, 8, false, 0, WF>;
   const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GEMM_TPB), lds, a.stream,
@@ -272,6 +288,12 @@ hipError_t launch_gemm_mfma_fp4(const Fp4Args& f) {
 }
 
 hipError_t launch_gemm_mfma_gidx(const MatArgs& a) {
+  const int tiles_m = (int)((a.M + GBM - 1) / GBM);
+  // 128-column tiles when their table fits and their grid still fills the
+  // compute units, else 64.
+  if (gidx_table_fits(a, 128) && tiles_m * ((a.N + 127) / 128) >= GEMM_FULL_ROUND)
+    return launch_gidx_staged(a, tiles_m, 4);
+  if (gidx_table_fits(a, 64)) return launch_gidx_staged(a, tiles_m, 2);
   switch (a.bits) {
     case 2: return launch_gidx_x<2>(a);
     case 4: return launch_gidx_x<4>(a);

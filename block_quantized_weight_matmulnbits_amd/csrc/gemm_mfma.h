@@ -64,18 +64,28 @@ __device__ __forceinline__ int lds_at(int r, int p) {
 // out-of-range offsets or harmless in-range addresses), so the compiler's
 // waits on the load counter stay exact.
 // ---------------------------------------------------------------------------
+// LDS bytes of the kernel's double-buffered A (256 rows) and B (BN rows)
+// tiles.
+template <int BN>
+constexpr size_t mfma_lds_bytes() {
+  return (size_t)(2 * STAGE + 2 * BN * LDS_ROW) * sizeof(uint16_t);
+}
+
 constexpr int GEMM_WAVES = 8;
 constexpr int GEMM_TPB = 64 * GEMM_WAVES;
 
 // GI: group indices (operator layout only): code k of a column takes the
 // scale and zero point of group g_idx[k] (clamped into 0..kb-1) instead of
-// its block's, looked up per code during the dequantization.
+// its block's, looked up per code during the dequantization -- GI = 1 from
+// memory; GI = 2 from a table of the tile's columns built in LDS after the
+// operand tiles (mfma_lds_bytes), with the step's group indices loaded with
+// its codes.
 // WF: block-scaled FP4 weights (1 + FP4_MX or 1 + FP4_NV; operator layout,
 // BITS = 4, no zero points): codes are E2M1 values (v_cvt_scalef32_pk_f32_fp4
 // with a unit scale), scales are one E8M0 / E4M3 byte per block, and the
 // result is multiplied by gscale.  Each weight, e2m1 * scale, has at most 6
 // significant bits, so its rounding to the activation dtype is exact.
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL, bool GI = false, int WF = 0>
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int TN, bool TL, int GI = 0, int WF = 0>
 __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
@@ -94,9 +104,12 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   // words) and 1-bit plane (one word).
   constexpr int WPT = BITS == 3 ? 3 : HK / P;
   constexpr int TM = 4;                        // MFMA row tiles per wave
+  constexpr int BSTRIDE = BN * LDS_ROW;        // one B tile, in 16-bit elements
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_g[];
   uint16_t* As = lds_g;                        // [2][GBM][LDS_ROW], pieces per lds_at
   uint16_t* Bs = lds_g + 2 * STAGE;            // [2][BN][LDS_ROW], pieces per lds_at
+  // GI = 2: the table of the BN columns' scales and zero points.
+  uint8_t* gslab = reinterpret_cast<uint8_t*>(lds_g + 2 * STAGE + 2 * BSTRIDE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,6 +175,16 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   ST scr[2][2];                      // scales of the (at most 2) blocks of 32 codes
   uint32_t sc8[2][2];                // WF: their scale bytes
   uint32_t zbr[2][2];                // zero-point bytes of those blocks
+  // GI = 2: every thread dequantizes: TPC threads per column, HKG codes
+  // each (8 for 64-column tiles, 16 for 128), with their group indices.
+  constexpr int TPC = GEMM_TPB / BN, HKG = GBK / TPC;
+  constexpr int WG2 = (HKG * BITS + 31) / 32;    // code words (2-bit, 8 codes: a half word)
+  constexpr int TSTRIDE = BN + 1;                // table row, in entries (see the prologue)
+  const int gcol = tid / TPC, gk = (tid % TPC) * HKG;
+  const bool gok = n0 + gcol < N;
+  const int gcode0 = gok ? (n0 + gcol) * row_bytes + gk * BITS / 8 : 0;
+  uint32_t cg2[GI == 2 ? 2 : 1][GI == 2 ? WG2 : 1];
+  int gir[GI == 2 ? 2 : 1][GI == 2 ? HKG : 1];
 
   // The A tile goes from memory straight into LDS buffer buf (buffer loads
   // with the LDS flag, no registers, no LDS write instructions): load i of
@@ -217,6 +240,28 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
         cw[st][1] = h[3] | (h[4] << 16);
         cw[st][2] = h[2] | (h[5] << 16);
       }
+    } else if constexpr (GI == 2) {
+      // This thread's HKG codes and their group indices (the codes of a
+      // column are contiguous, so adjacent threads read adjacent bytes).
+      const int kg = k0 + gk;
+#pragma unroll
+      for (int i = 0; i < HKG; i += 4) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rgi, (kg + i) * 4, 0, 0);
+        gir[st][i] = (int)t.x; gir[st][i + 1] = (int)t.y; gir[st][i + 2] = (int)t.z; gir[st][i + 3] = (int)t.w;
+      }
+      const int cb = gok ? gcode0 + (k0 >> 6) * CHUNK_BYTES : OOB;
+      if constexpr (HKG * BITS == 16) {
+        cg2[st][0] = __builtin_amdgcn_raw_buffer_load_b16(rbc, cb, 0, 0);
+      } else if constexpr (HKG * BITS == 32) {
+        cg2[st][0] = __builtin_amdgcn_raw_buffer_load_b32(rbc, cb, 0, 0);
+      } else if constexpr (HKG * BITS == 64) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbc, cb, 0, 0);
+        cg2[st][0] = t.x; cg2[st][1] = t.y;
+      } else {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rbc, cb, 0, 0);
+        cg2[st][0] = t.x; cg2[st][1] = t.y; cg2[st][2] = t.z; cg2[st][3] = t.w;
+      }
+      return;
     } else if constexpr (GI) {
       // Codes only; the scales and zero points are looked up per code when
       // the step is dequantized.
@@ -264,8 +309,33 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   };
   // Dequantize register stage `st` (step starting at k0) into LDS buffer buf.
   auto store_b = [&](int k0, int st, int buf) {
+    uint16_t* bs = Bs + buf * BSTRIDE;
+    if constexpr (GI == 2) {
+      // Per code: its group (past K: group 0, meeting zero activations),
+      // then this column's table entry {s, z * s} of that group.
+      constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+      constexpr int PW = 32 / BITS;
+      const f32x2* tab = reinterpret_cast<const f32x2*>(gslab) + gcol;
+      uint32_t pk[HKG / 2];
+#pragma unroll
+      for (int j = 0; j < HKG; j += 2) {
+        float w2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int i = j + t;
+          const f32x2 e = tab[min(max(gir[st][i], 0), kb - 1) * TSTRIDE];
+          const float q = (float)((cg2[st][i / PW] >> ((i % PW) * BITS)) & zm);
+          w2[t] = fmaf(q, e.x, -e.y);
+        }
+        pk[j / 2] = Op::pack(w2[0], w2[1]);
+      }
+#pragma unroll
+      for (int j = 0; j < HKG / 8; ++j)
+        *reinterpret_cast<u32x4*>(&bs[lds_at(gcol, (gk >> 3) + j)]) =
+            u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
+      return;
+    }
     if (!dq) return;
-    uint16_t* bs = Bs + buf * STAGE;
     const int kt = k0 + khalf;
     if constexpr (GI) {
       // Per code k = kt + i: g = g_idx[k] (zero past K, where the activations
@@ -401,7 +471,7 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   auto mfma_step = [&](int buf) {
     const uint16_t* as = As + buf * STAGE;
-    const uint16_t* bs = Bs + buf * STAGE;
+    const uint16_t* bs = Bs + buf * BSTRIDE;
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 32) {
       typename Op::V af[TM];
@@ -444,6 +514,47 @@ __global__ __launch_bounds__(GEMM_TPB) void gemm_mfma_kernel(
   load_a(0, 0);
   load_b(0, 0);
   load_b(GBK, 1);
+  if constexpr (GI == 2) {
+    // Table of the tile's BN columns, entry (g, c) at g * (BN + 1) + c: the
+    // scale of group g of column n0 + c and its product with the zero point,
+    // both in fp32 (the product rounded as the other paths round it).  Lanes
+    // take adjacent columns, so the table is written without bank conflicts;
+    // a wave reads it at BN / TPC adjacent columns times TPC groups, which
+    // the odd row length spreads over the banks.  Past N the loads read
+    // zeros.
+    constexpr int GPP = GEMM_TPB / BN;         // groups per pass
+    constexpr uint32_t zm = (BITS == 8) ? 0xFFu : ((1u << BITS) - 1u);
+    const int c = tid % BN;
+    const int sc0 = (n0 + c) * kb, zr0 = (n0 + c) * zp_row_bytes;
+    f32x2* tab = reinterpret_cast<f32x2*>(gslab);
+    for (int gb = tid / BN; gb < kb; gb += 8 * GPP) {
+      uint32_t sv[8], zv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = gb + u * GPP;
+        const bool ok = g < kb;
+        if constexpr (sizeof(ST) == 4)
+          sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, ok ? (sc0 + g) * 4 : OOB, 0, 0);
+        else
+          sv[u] = __builtin_amdgcn_raw_buffer_load_b16(rsc, ok ? (sc0 + g) * 2 : OOB, 0, 0);
+        zv[u] = HAS_ZP ? __builtin_amdgcn_raw_buffer_load_b8(rzp, ok ? zr0 + ((g * BITS) >> 3) : OOB, 0, 0)
+                       : 0u;
+      }
+      // Unconditional stores (groups past kb go to the spare row kb), so
+      // that the loads above stay ahead of every use instead of being sunk
+      // into a branch per group.
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = gb + u * GPP;
+        float sf;
+        if constexpr (sizeof(ST) == 4) sf = __builtin_bit_cast(float, sv[u]);
+        else sf = dt<SDT>::to_f32(__builtin_bit_cast(ST, (uint16_t)sv[u]));
+        const uint32_t z = HAS_ZP ? (zv[u] >> ((g * BITS) & 7)) & zm : 1u << (BITS - 1);
+        tab[min(g, kb) * TSTRIDE + c] = f32x2{sf, (float)z * sf};
+      }
+    }
+    __syncthreads();
+  }
   store_b(0, 0, 0);
   __syncthreads();
   // The two orders are two copies of the loop (one wave-uniform branch
@@ -485,6 +596,18 @@ inline int ilog2i(int64_t v) {
   return l;
 }
 
+// Group indices with a staged table (GI = 2): LDS bytes of the table of a
+// BN-column workgroup, 8 bytes per group and column (rows of BN + 1; one
+// spare row).
+inline size_t gidx_table_bytes(const MatArgs& a, int bn) { return (size_t)(a.kb + 1) * (bn + 1) * 8; }
+
+// The staged group-index kernel (GI = 2) with 64-column (tn = 2) or
+// 128-column (tn = 4) tiles (gidx_mfma.hip).
+hipError_t launch_gidx_staged(const MatArgs& a, int tiles_m, int tn);
+
+// LDS available to one workgroup.
+constexpr size_t LDS_MAX = 160 * 1024;
+
 // Workgroups that fill the chip once (one per compute unit).
 constexpr int GEMM_FULL_ROUND = 256;
 
@@ -497,7 +620,7 @@ hipError_t launch_mfma_tn(const MatArgs& a, int tiles_m) {
   using ST = typename dt<SDT>::T;
   constexpr int BN = 32 * TN;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
-  constexpr size_t lds = 4 * STAGE * sizeof(uint16_t);   // double-buffered A and B
+  constexpr size_t lds = mfma_lds_bytes<BN>();   // double-buffered A and B
   decltype(&gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, TN, false>) kern;
   if constexpr (BITS == 3) kern = gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, TN, false>;
   else kern = a.tiled ? gemm_mfma_kernel<BITS, XDT, SDT, HAS_ZP, TN, true>

@@ -174,3 +174,45 @@ def test_out_of_range_entries_are_clamped_not_faulting():
         clamped = np.clip(bad, 0, kb - 1).astype(np.int32)
         entry = "gemv" if M == 1 else "gemm"
         assert torch.equal(run(case, bad, entry), run(case, clamped, entry))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_every_route_exact(bits):
+    """Exact data on each route of qmm_gemm with group indices and 16-bit
+    activations: the tabled matrix-core kernel with 128-column tiles (grid of
+    at least 256 workgroups, table of at most 63 groups) and with 64-column
+    tiles (M = 2, M = 16, ragged N), the 256-column kernel with lookups in
+    memory (M > 16, a table of 160 groups does not fit in LDS), the row
+    kernel (M <= 16, same), and a group-index array that is not 16-byte
+    aligned (the tabled kernel reads it 16 bytes at a time)."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    rng = np.random.default_rng(77 + bits)
+    cases = [("table128", 520, 264, 11000, 32, "bf16", "f32"),
+             ("table64 M2", 2, 1032, 300, 64, "f16", "f16"),
+             ("table64 M16", 16, 776, 97, 16, "bf16", "bf16"),
+             ("memory", 40, 2560, 130, 16, "bf16", "f16"),
+             ("rows", 8, 2560, 70, 16, "f16", "bf16"),
+             ("unaligned", 24, 512, 200, 32, "bf16", "bf16")]
+    for i, (name, M, K, N, bs, a_dtype, s_dtype) in enumerate(cases):
+        case = make_matmul_case(M, K, N, bs, bits, a_dtype=a_dtype, s_dtype=s_dtype,
+                                has_zp=i % 2 == 0, has_bias=True, seed=500 + i)
+        case.A = torch.from_numpy(rng.integers(-3, 4, (M, K)).astype(np.float32)).to(case.A.dtype)
+        kb = case.k_blocks
+        case.scales = torch.from_numpy(
+            2.0 ** rng.integers(-4, 0, (N, kb)).astype(np.float32)).to(case.scales.dtype)
+        case.bias = torch.from_numpy(rng.integers(-8, 9, N).astype(np.float32)).to(case.A.dtype)
+        g = gidx_pattern("act_order", K, bs, kb, rng)
+        print(f"[gidx route] {name}: M={M} K={K} N={N} bs={bs} bits={bits} a={a_dtype} "
+              f"s={s_dtype}", flush=True)
+        Y, _ = oracle_y(case, g)
+        expect = torch.from_numpy(Y).to(case.A.dtype)
+        if name == "unaligned":
+            c = case.to(DEV)
+            gd = torch.from_numpy(np.concatenate([[0], g]).astype(np.int32)).to(DEV)[1:]
+            y = torch.empty(M, N, dtype=c.A.dtype, device=DEV)
+            qmm().qmm_gemm(c.A, c.B, c.scales, c.zero_points, c.bias, y, M, K, N, bs, bits,
+                           g_idx=gd)
+            torch.cuda.synchronize()
+        else:
+            y = run(case, g)
+        assert torch.equal(y.cpu(), expect), name
