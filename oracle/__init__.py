@@ -16,8 +16,9 @@ Every function cites the passage of the web pages it follows:
   ``int4_dot_row_scalar`` / ``int8_row``.
 * "rlx-cpu quant.rs" -- ``exec_q_mat_mul`` (int32 accumulate, requantize,
   clamp), the ``QConv2d`` attribute set, ``dequant_matmul_nvfp4`` and the
-  low-precision scaled-GEMM reference (``lowp_dequantize``,
-  ``lowp_scaled_matmul``) for block-scaled FP4 weights.
+  low-precision scaled-GEMM reference (``lowp_compute_scales``,
+  ``lowp_quantize``, ``lowp_dequantize``, ``lowp_scaled_matmul``): FP8 / FP6 /
+  FP4 codes with per-tensor, MX (E8M0 per 32) or NVFP4 (E4M3 per 16) scales.
 * "MNN ConvInt8TiledExecutor.cpp" -- zero-point padding of the im2col and the
   clamp defaults.
 
@@ -83,14 +84,30 @@ def _load():
             "oracle_compint8_matmul": [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp],
             "oracle_conv_int8": [vp, vp, vp, vp, f32, f32, i32, i32, i32, i32, i32, i32,
                                  i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp],
+            "oracle_lowp_decode": [i32, ctypes.c_uint],
+            "oracle_lowp_max_finite": [i32],
+            "oracle_lowp_encode": [i32, ctypes.c_double],
+            "oracle_f32_to_e8m0": [f32],
+            "oracle_lowp_snap_scale": [i32, f32],
+            "oracle_lowp_compute_scales": [vp, i32, i32, i64, i64, vp],
+            "oracle_lowp_store_scales": [vp, i32, i64, vp],
+            "oracle_lowp_read_scales": [vp, i32, i64, vp],
+            "oracle_lowp_quantize": [vp, vp, i32, i32, i64, i64, vp],
+            "oracle_lowp_dequantize": [vp, vp, i32, i32, i64, i64, vp],
+            "oracle_lowp_scaled_matmul": [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp,
+                                          vp],
         }
         for name, argtypes in sig.items():
             fn = getattr(_lib, name)
             fn.argtypes = argtypes
             fn.restype = None
         _lib.oracle_check_g_idx.restype = i64
-        for name in ("oracle_e2m1", "oracle_e8m0", "oracle_e4m3"):
+        for name in ("oracle_e2m1", "oracle_e8m0", "oracle_e4m3", "oracle_lowp_decode",
+                     "oracle_lowp_max_finite"):
             getattr(_lib, name).restype = ctypes.c_double
+        _lib.oracle_lowp_encode.restype = ctypes.c_uint
+        _lib.oracle_f32_to_e8m0.restype = ctypes.c_uint
+        _lib.oracle_lowp_snap_scale.restype = f32
     return _lib
 
 
@@ -321,6 +338,108 @@ def fp4_matmul(A, W, scales, fmt, global_scale, bias, N, K):
                               FP4_FORMATS[fmt], float(global_scale), _ptr(_c(bias, np.float64)),
                               M, N, K, _ptr(Y), _ptr(S))
     return Y, S
+
+
+# -- Low-precision scaled GEMM ([RLX] quant.rs: lowp_* reference) -------------
+
+LOWP_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m3": 2, "e3m2": 3, "e2m1": 4}
+LOWP_LAYOUTS = {"tensor": 0, "mx": 1, "nvfp4": 2}
+LOWP_BLOCK = {"mx": 32, "nvfp4": 16}
+
+
+def _fmt(f):
+    return LOWP_FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _lay(l):
+    return LOWP_LAYOUTS[l] if isinstance(l, str) else int(l)
+
+
+def lowp_decode(fmt, code):
+    """Value of one code of an element format (e4m3, e5m2, e2m3, e3m2, e2m1)."""
+    return _load().oracle_lowp_decode(_fmt(fmt), int(code))
+
+
+def lowp_encode(fmt, v):
+    """Code of the finite value nearest to v (ties to even, saturating)."""
+    return int(_load().oracle_lowp_encode(_fmt(fmt), float(v)))
+
+
+def lowp_max_finite(fmt):
+    return _load().oracle_lowp_max_finite(_fmt(fmt))
+
+
+def f32_to_e8m0(s):
+    return int(_load().oracle_f32_to_e8m0(float(np.float32(s))))
+
+
+def lowp_snap_scale(layout, s):
+    return float(_load().oracle_lowp_snap_scale(_lay(layout), float(np.float32(s))))
+
+
+def lowp_nblk(cols, layout):
+    return 1 if _lay(layout) == 0 else -(-cols // LOWP_BLOCK[["tensor", "mx", "nvfp4"][_lay(layout)]])
+
+
+def lowp_compute_scales(x, fmt, layout):
+    """Raw float32 scales of x [rows, cols] (lowp_compute_scales)."""
+    x = _c(np.atleast_2d(x), np.float32)
+    rows, cols = x.shape
+    out = np.empty(1 if _lay(layout) == 0 else rows * lowp_nblk(cols, layout), np.float32)
+    _load().oracle_lowp_compute_scales(_ptr(x), _fmt(fmt), _lay(layout), rows, cols, _ptr(out))
+    return out if _lay(layout) == 0 else out.reshape(rows, -1)
+
+
+def lowp_store_scales(scales, layout):
+    """Stored form of raw scales: float32 (per tensor) or one byte each."""
+    s = _c(np.ravel(scales), np.float32)
+    out = np.empty(1, np.float32) if _lay(layout) == 0 else np.empty(s.size, np.uint8)
+    _load().oracle_lowp_store_scales(_ptr(s), _lay(layout), s.size, _ptr(out))
+    return out if _lay(layout) == 0 else out.reshape(np.shape(scales))
+
+
+def lowp_read_scales(stored, layout):
+    """Raw float32 scales from their stored form (lowp_read_scales)."""
+    st = np.ascontiguousarray(stored)
+    n = 1 if _lay(layout) == 0 else st.size
+    out = np.empty(n, np.float32)
+    _load().oracle_lowp_read_scales(_ptr(st), _lay(layout), n, _ptr(out))
+    return out if _lay(layout) == 0 else out.reshape(np.shape(stored))
+
+
+def lowp_quantize(x, scales, fmt, layout):
+    """Codes [rows, cols] (one per byte) of x with raw scales (lowp_quantize)."""
+    x = _c(np.atleast_2d(x), np.float32)
+    rows, cols = x.shape
+    out = np.empty((rows, cols), np.uint8)
+    _load().oracle_lowp_quantize(_ptr(x), _ptr(_c(scales, np.float32)), _fmt(fmt), _lay(layout),
+                                 rows, cols, _ptr(out))
+    return out
+
+
+def lowp_dequantize(codes, scales, fmt, layout):
+    codes = _c(np.atleast_2d(codes), np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), np.float64)
+    _load().oracle_lowp_dequantize(_ptr(codes), _ptr(_c(scales, np.float32)), _fmt(fmt),
+                                   _lay(layout), rows, cols, _ptr(out))
+    return out
+
+
+def lowp_scaled_matmul(lhs, rhs, lhs_scales, rhs_scales, bias, layout, lhs_fmt, rhs_fmt):
+    """out = dequant(lhs) . dequant(rhs)^T (+ bias) in float64 and S = sum |a b|
+    (lowp_scaled_matmul; lhs [m, k], rhs [n, k] codes, raw float32 scales)."""
+    lhs = _c(np.atleast_2d(lhs), np.uint8)
+    rhs = _c(np.atleast_2d(rhs), np.uint8)
+    m, k = lhs.shape
+    n = rhs.shape[0]
+    out = np.empty((m, n), np.float64)
+    S = np.empty((m, n), np.float64)
+    _load().oracle_lowp_scaled_matmul(_ptr(lhs), _ptr(rhs), _ptr(_c(lhs_scales, np.float32)),
+                                      _ptr(_c(rhs_scales, np.float32)), _ptr(_c(bias, np.float64)),
+                                      m, n, k, _lay(layout), _fmt(lhs_fmt), _fmt(rhs_fmt),
+                                      _ptr(out), _ptr(S))
+    return out, S
 
 
 # -- O5 int8 conv --------------------------------------------------------------

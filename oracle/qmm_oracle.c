@@ -478,6 +478,204 @@ EXPORT void oracle_fp4_matmul(const double *A, const uint8_t *W,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Low-precision scaled GEMM ([RLX] quant.rs, its FP8/FP6/FP4 scaled-GEMM    */
+/* reference: lowp_compute_scales, lowp_quantize, lowp_scaled_matmul,         */
+/* lowp_dequantize, lowp_snap_scale, lowp_read_scales).                       */
+/* One code per byte (its low bits), rows K-last, out = lhs . rhs^T (TN).     */
+/* Element formats (fmt), decoded from their published definitions (OCP 8-bit */
+/* floating point and OCP Microscaling formats):                              */
+/*   0 E4M3: bias 7, 3 mantissa bits, S.1111.111 nan, no inf, max 448.        */
+/*   1 E5M2: bias 15, 2 mantissa bits, exponent 31: inf (m = 0) or nan,       */
+/*           max 57344.                                                       */
+/*   2 E2M3 (FP6): bias 1, 3 mantissa bits, no inf or nan, max 7.5.           */
+/*   3 E3M2 (FP6): bias 3, 2 mantissa bits, no inf or nan, max 28.            */
+/*   4 E2M1 (FP4): bias 1, 1 mantissa bit, no inf or nan, max 6.              */
+/* Exponent field 0 is subnormal: m / 2^mbits * 2^(1 - bias).                 */
+/* Scale layouts (layout): 0 per tensor (one f32 per operand), 1 MX (one E8M0 */
+/* byte per 32 elements along K), 2 NVFP4 (one E4M3 byte per 16 along K).     */
+/* The codec itself is not printed on the pages; its readings:               */
+/*   encode: the finite value of the format nearest to v, ties to the code    */
+/*   with the even mantissa; beyond the largest finite value: that value     */
+/*   (saturation, inf included); nan: the format's nan (E4M3 0x7F, E5M2      */
+/*   0x7F) or 0 where it has none; the sign of v is kept on zero.            */
+/*   f32_to_e8m0: the 8 exponent bits of the binary32 value (the power of two */
+/*   at or below a normal value; 0 for zero and subnormals; 255 for inf and  */
+/*   nan).                                                                    */
+/* ------------------------------------------------------------------------ */
+static const int LOWP_EBITS[5] = {4, 5, 2, 3, 2};
+static const int LOWP_MBITS[5] = {3, 2, 3, 2, 1};
+static const int LOWP_BIAS[5] = {7, 15, 1, 3, 1};
+
+static int lowp_bits(int fmt) { return 1 + LOWP_EBITS[fmt] + LOWP_MBITS[fmt]; }
+
+/* Nan or inf code (not a finite value). */
+static int lowp_special(int fmt, unsigned c) {
+    unsigned e = (c >> LOWP_MBITS[fmt]) & ((1u << LOWP_EBITS[fmt]) - 1);
+    unsigned m = c & ((1u << LOWP_MBITS[fmt]) - 1);
+    if (fmt == 0) return e == 15 && m == 7;
+    if (fmt == 1) return e == 31;
+    return 0;
+}
+
+EXPORT double oracle_lowp_decode(int fmt, unsigned code) {
+    int mb = LOWP_MBITS[fmt], eb = LOWP_EBITS[fmt], bias = LOWP_BIAS[fmt];
+    unsigned c = code & ((1u << lowp_bits(fmt)) - 1);
+    int sign = (c >> (eb + mb)) & 1;
+    int e = (int)((c >> mb) & ((1u << eb) - 1));
+    int m = (int)(c & ((1u << mb) - 1));
+    double v;
+    if (fmt == 0 && e == 15 && m == 7) return NAN;
+    if (fmt == 1 && e == 31) v = m == 0 ? INFINITY : NAN;
+    else if (e == 0) v = ldexp((double)m / (1 << mb), 1 - bias);
+    else v = ldexp(1.0 + (double)m / (1 << mb), e - bias);
+    return sign ? -v : v;
+}
+
+EXPORT double oracle_lowp_max_finite(int fmt) {
+    static const double mx[5] = {448.0, 57344.0, 7.5, 28.0, 6.0};
+    return mx[fmt];
+}
+
+EXPORT unsigned oracle_lowp_encode(int fmt, double v) {
+    int bits = lowp_bits(fmt);
+    unsigned signbit = 1u << (bits - 1);
+    if (isnan(v)) return (fmt == 0 || fmt == 1) ? 0x7Fu : 0u;
+    unsigned sgn = signbit(v) ? signbit : 0u;
+    double a = fabs(v);
+    if (a > oracle_lowp_max_finite(fmt)) a = oracle_lowp_max_finite(fmt);  /* saturation */
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned c = 0; c < signbit; ++c) {          /* the non-negative codes */
+        if (lowp_special(fmt, c)) continue;
+        double d = fabs(oracle_lowp_decode(fmt, c) - a);
+        if (d < best_d || (d == best_d && (c & 1u) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best | sgn;
+}
+
+EXPORT unsigned oracle_f32_to_e8m0(float s) {
+    uint32_t u;
+    memcpy(&u, &s, 4);
+    return (u >> 23) & 0xFFu;
+}
+
+static int lowp_block(int layout) { return layout == 1 ? 32 : 16; }
+
+/* lowp_snap_scale: the value the layout can store nearest (by its reading)   */
+/* to s.                                                                      */
+EXPORT float oracle_lowp_snap_scale(int layout, float s) {
+    if (layout == 0) return s;
+    if (layout == 1) return (float)oracle_e8m0(oracle_f32_to_e8m0(s));
+    return (float)oracle_lowp_decode(0, oracle_lowp_encode(0, (double)s));
+}
+
+/* lowp_compute_scales: raw f32 scales of x [rows, cols] (per tensor: one;    */
+/* else [rows, nblk]): amax / max_finite (1 where amax is 0), snapped.        */
+EXPORT void oracle_lowp_compute_scales(const float *x, int fmt, int layout, int64_t rows,
+                                       int64_t cols, float *out) {
+    float maxf = (float)oracle_lowp_max_finite(fmt);
+    if (layout == 0) {
+        float amax = 0.0f;
+        for (int64_t i = 0; i < rows * cols; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        out[0] = amax > 0.0f ? amax / maxf : 1.0f;
+        return;
+    }
+    int64_t bs = lowp_block(layout), nblk = n_blocks(cols, bs);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nblk; ++b) {
+            float amax = 0.0f;
+            for (int64_t c = b * bs; c < cols && c < (b + 1) * bs; ++c)
+                amax = fmaxf(amax, fabsf(x[r * cols + c]));
+            out[r * nblk + b] = oracle_lowp_snap_scale(layout, amax > 0.0f ? amax / maxf : 1.0f);
+        }
+}
+
+/* Stored scale bytes of raw scales (ScaledQuantScale): per tensor the f32   */
+/* itself, MX the E8M0 byte, NVFP4 the E4M3 byte.                             */
+EXPORT void oracle_lowp_store_scales(const float *scales, int layout, int64_t n, void *out) {
+    if (layout == 0) {
+        memcpy(out, scales, 4);
+        return;
+    }
+    uint8_t *o = (uint8_t *)out;
+    for (int64_t i = 0; i < n; ++i)
+        o[i] = (uint8_t)(layout == 1 ? oracle_f32_to_e8m0(scales[i])
+                                     : oracle_lowp_encode(0, (double)scales[i]));
+}
+
+/* lowp_read_scales: decoded raw scales from stored bytes. */
+EXPORT void oracle_lowp_read_scales(const void *stored, int layout, int64_t n, float *out) {
+    if (layout == 0) {
+        memcpy(out, stored, 4);
+        return;
+    }
+    const uint8_t *b = (const uint8_t *)stored;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (float)(layout == 1 ? oracle_e8m0(b[i]) : oracle_lowp_decode(0, b[i]));
+}
+
+static float lowp_scale_at(int layout, const float *scales, int64_t row, int64_t col,
+                           int64_t nblk) {
+    if (layout == 0) return scales[0];
+    return scales[row * nblk + col / lowp_block(layout)];
+}
+
+/* lowp_quantize: code = encode(x / s) with the binary32 quotient (0 where s  */
+/* is 0).                                                                     */
+EXPORT void oracle_lowp_quantize(const float *x, const float *scales, int fmt, int layout,
+                                 int64_t rows, int64_t cols, uint8_t *out) {
+    int64_t nblk = layout == 0 ? 1 : n_blocks(cols, lowp_block(layout));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float s = lowp_scale_at(layout, scales, r, c, nblk);
+            float v = s != 0.0f ? x[r * cols + c] / s : 0.0f;
+            out[r * cols + c] = (uint8_t)oracle_lowp_encode(fmt, (double)v);
+        }
+}
+
+/* lowp_dequantize: decode(code) * scale, in double. */
+EXPORT void oracle_lowp_dequantize(const uint8_t *codes, const float *scales, int fmt,
+                                   int layout, int64_t rows, int64_t cols, double *out) {
+    int64_t nblk = layout == 0 ? 1 : n_blocks(cols, lowp_block(layout));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = oracle_lowp_decode(fmt, codes[r * cols + c]) *
+                                (double)lowp_scale_at(layout, scales, r, c, nblk);
+}
+
+/* lowp_scaled_matmul: out[i, j] = sum_p a(i, p) b(j, p) (+ bias[j]) with     */
+/* a = decode(lhs) * lhs scale, b = decode(rhs) * rhs scale, in double; S the */
+/* sum of |a b| (+ |bias|).                                                   */
+EXPORT void oracle_lowp_scaled_matmul(const uint8_t *lhs, const uint8_t *rhs,
+                                      const float *ls, const float *rs, const double *bias,
+                                      int64_t m, int64_t n, int64_t k, int layout,
+                                      int lfmt, int rfmt, double *out, double *S) {
+    int64_t nblk = layout == 0 ? 1 : n_blocks(k, lowp_block(layout));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t p = 0; p < k; ++p) {
+                double a = oracle_lowp_decode(lfmt, lhs[i * k + p]) *
+                           (double)lowp_scale_at(layout, ls, i, p, nblk);
+                double b = oracle_lowp_decode(rfmt, rhs[j * k + p]) *
+                           (double)lowp_scale_at(layout, rs, j, p, nblk);
+                acc += a * b;
+                mag += fabs(a * b);
+            }
+            if (bias) {
+                acc += bias[j];
+                mag += fabs(bias[j]);
+            }
+            out[i * n + j] = acc;
+            if (S) S[i * n + j] = mag;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O5 int8 convolution with requantization.                                   */
 /* acc = bias[oc] + sum over taps and input channels of                       */
 /*       (x - in_zp) * w, an out-of-bounds tap reading x = in_zp             */
