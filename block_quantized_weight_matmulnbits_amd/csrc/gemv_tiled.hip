@@ -476,11 +476,13 @@ hipError_t launch_z(const MatArgs& a, const TiledGeom& tg) {
   const int chunks = (int)tg.chunks;
   const int n_oct = (int)tg.groups * (TG / OCT);
   // Octets per workgroup: one workgroup per compute unit where there are
-  // enough octets; then shares of K until a workgroup has 8 waves (two per
-  // SIMD), keeping at least two wave loads per share.
+  // enough octets; then, for one or two octets, shares of K up to 4 waves,
+  // keeping at least two wave loads per share (measured at K = 4096: N = 4096
+  // 5.0 µs with two shares against 6.4 with one; N = 6144, three octets,
+  // 6.1 µs with one share against 6.6 with two).
   const int O = std::min(MAX_WAVES, std::max(1, (n_oct + 255) / 256));
   int S = 1;
-  while (O * S * 2 <= MAX_WAVES && O * S < 4 && chunks >= 2 * (2 * S) * G::CPL) S *= 2;
+  while (O * S * 2 <= 4 && chunks >= 2 * (2 * S) * G::CPL) S *= 2;
   // More shares while the workgroup's threads cannot stage the activations
   // in their two first passes (every further pass is a dependent load).
   const int pc = std::min(chunks, PIECE_CHUNKS);

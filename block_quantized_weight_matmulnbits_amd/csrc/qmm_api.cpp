@@ -451,6 +451,40 @@ int qmm_gemm_fp4(const void* A, int a_dtype, const uint8_t* W, const uint8_t* sc
   return hip_status(qmm::launch_fp4(a), fn);
 }
 
+int qmm_lowp_matmul(const uint8_t* lhs, const uint8_t* rhs, const void* lhs_scales,
+                    const void* rhs_scales, const float* bias, float* out, int64_t m, int64_t n,
+                    int64_t k, int layout, int lhs_format, int rhs_format, void* stream) {
+  const char* fn = "qmm_lowp_matmul";
+  if (layout < QMM_LOWP_PER_TENSOR || layout > QMM_LOWP_NVFP4)
+    return fail(QMM_ERR_INVALID_ARG, "%s: layout=%d is not a qmm_lowp_layout. How to fix: pass "
+                "QMM_LOWP_PER_TENSOR, QMM_LOWP_MX (E8M0 per 32) or QMM_LOWP_NVFP4 (E4M3 per 16).",
+                fn, layout);
+  for (int f : {lhs_format, rhs_format})
+    if (f < QMM_LOWP_E4M3 || f > QMM_LOWP_E2M1)
+      return fail(QMM_ERR_INVALID_ARG, "%s: format=%d is not a qmm_lowp_format. How to fix: pass "
+                  "QMM_LOWP_E4M3, _E5M2, _E2M3, _E3M2 or _E2M1.", fn, f);
+  if (n <= 0 || k <= 0 || m < 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: n and k must be positive and m >= 0 (got m=%lld "
+                "n=%lld k=%lld).", fn, (long long)m, (long long)n, (long long)k);
+  if (rhs == nullptr || lhs_scales == nullptr || rhs_scales == nullptr ||
+      (m > 0 && (lhs == nullptr || out == nullptr)))
+    return fail(QMM_ERR_INVALID_ARG, "%s: lhs, rhs, both scale tensors and out must be non-null "
+                "device pointers (bias may be NULL).", fn);
+  if (!aligned(out, 4) || !aligned(bias, 4) || (layout == QMM_LOWP_PER_TENSOR &&
+      (!aligned(lhs_scales, 4) || !aligned(rhs_scales, 4))))
+    return fail(QMM_ERR_INVALID_ARG, "%s: out, bias and f32 scales must be 4-byte aligned.", fn);
+  if (m * k + 64 > INT32_MAX || n * k + 64 > INT32_MAX)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: m * k or n * k (%lld, %lld) reaches 2^31, past the "
+                "kernels' 32-bit offsets. How to fix: split the matmul along m or n.", fn,
+                (long long)(m * k), (long long)(n * k));
+  if (m == 0) return QMM_OK;
+  qmm::LowpArgs a;
+  a.lhs = lhs; a.rhs = rhs; a.lsc = lhs_scales; a.rsc = rhs_scales; a.bias = bias; a.out = out;
+  a.m = m; a.n = n; a.k = k; a.layout = layout; a.lfmt = lhs_format; a.rfmt = rhs_format;
+  a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_lowp_matmul(a), fn);
+}
+
 int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,
                float in_scale, float out_scale, int in_zp, int out_zp, int clamp_min,
                int clamp_max, int Nb, int H, int W, int C, int Co, int KH, int KW, int stride_h,

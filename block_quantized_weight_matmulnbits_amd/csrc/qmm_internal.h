@@ -92,6 +92,21 @@ hipError_t launch_gemm_mfma_fp4(const Fp4Args& a);
 bool gemm_skinny_fp4_supported(const Fp4Args& a);
 hipError_t launch_gemm_skinny_fp4(const Fp4Args& a);
 
+// Low-precision scaled GEMM (validated problem; lowp.hip).
+struct LowpArgs {
+  const uint8_t* lhs = nullptr;   // [m, k] codes, one per byte
+  const uint8_t* rhs = nullptr;   // [n, k] codes
+  const void* lsc = nullptr;      // per tensor: one f32; MX / NVFP4: [m, nblk] bytes
+  const void* rsc = nullptr;      // per tensor: one f32; MX / NVFP4: [n, nblk] bytes
+  const float* bias = nullptr;    // [n] or null
+  float* out = nullptr;           // [m, n]
+  int64_t m = 0, n = 0, k = 0;
+  int layout = 0;                 // 0 per tensor, 1 MX (E8M0 / 32), 2 NVFP4 (E4M3 / 16)
+  int lfmt = 0, rfmt = 0;         // 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1
+  hipStream_t stream = nullptr;
+};
+hipError_t launch_lowp_matmul(const LowpArgs& a);
+
 // int8 convolution (validated NHWC / OHWI problem).
 struct ConvArgs {
   const int8_t* X = nullptr;

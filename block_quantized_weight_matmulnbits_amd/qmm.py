@@ -38,6 +38,8 @@ _SIGS = {
     "qmm_gemm": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i32,
                   _i32, _i32, _vp], _i32),
     "qmm_compint8_workspace_size": ([_i64, _i64, _i32], _sz),
+    "qmm_lowp_matmul": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
+                        _i32),
     "qmm_gemm_compint8": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
                            _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
@@ -358,3 +360,19 @@ def qmm_debug_compint8_block_dots(A, B, zero_points, M, K, N, block_size, bits, 
                                              _ptr(workspace),
                                              workspace.numel() * workspace.element_size(),
                                              _stream(stream)))
+
+
+LOWP_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m3": 2, "e3m2": 3, "e2m1": 4}
+LOWP_LAYOUTS = {"tensor": 0, "mx": 1, "nvfp4": 2}
+
+
+def qmm_lowp_matmul(lhs, rhs, lhs_scales, rhs_scales, bias, out, m, n, k, layout, lhs_format,
+                    rhs_format, stream=None):
+    """out[m, n] (f32) = decoded, scaled lhs [m, k] times rhs [n, k]^T (+ bias);
+    layout "tensor" / "mx" / "nvfp4", formats "e4m3" / "e5m2" / "e2m3" /
+    "e3m2" / "e2m1" (or their qmm_lowp_* integers)."""
+    lay = LOWP_LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    lf = LOWP_FORMATS[lhs_format] if isinstance(lhs_format, str) else int(lhs_format)
+    rf = LOWP_FORMATS[rhs_format] if isinstance(rhs_format, str) else int(rhs_format)
+    _check(lib.qmm_lowp_matmul(_ptr(lhs), _ptr(rhs), _ptr(lhs_scales), _ptr(rhs_scales),
+                               _ptr(bias), _ptr(out), m, n, k, lay, lf, rf, _stream(stream)))

@@ -244,6 +244,42 @@ int qmm_gemm_fp4(const void *A, int a_dtype, const uint8_t *W,
                  void *stream);
 
 /*
+ * Low-precision scaled GEMM (rlx-cpu quant.rs: the FP8 / FP6 / FP4
+ * scaled-GEMM reference lowp_scaled_matmul and lowp_read_scales), TN:
+ *   out[i, j] = sum_p a(i, p) * b(j, p)  (+ bias[j]),  fp32 accumulate
+ *   a(i, p) = decode(lhs[i, p]) * lhs_scale(i, p)
+ *   b(j, p) = decode(rhs[j, p]) * rhs_scale(j, p)
+ *   lhs [m, k], rhs [n, k]   uint8, one code per byte in its low bits
+ *                            (rows K-last)
+ *   lhs_scales, rhs_scales   by layout:
+ *     QMM_LOWP_PER_TENSOR    one f32 each (device memory)
+ *     QMM_LOWP_MX            [m, ceil(k/32)] / [n, ceil(k/32)] E8M0 bytes
+ *                            (2^(e-127); 255 is nan)
+ *     QMM_LOWP_NVFP4         [m, ceil(k/16)] / [n, ceil(k/16)] E4M3 bytes
+ *   bias [n] f32 (may be NULL), out [m, n] f32
+ * Element formats (OCP FP8 and Microscaling definitions; exponent 0 is
+ * subnormal): E4M3 (bias 7, S.1111.111 nan, max 448), E5M2 (bias 15, IEEE
+ * inf / nan, max 57344), E2M3 (FP6, bias 1, max 7.5), E3M2 (FP6, bias 3,
+ * max 28), E2M1 (FP4, bias 1, max 6).  The two operands may differ in
+ * format.  Per tensor and MX run on gfx950's block-scaled matrix-core
+ * instruction; NVFP4 decodes to bf16 (exact) for the bf16 one.  Errors:
+ * QMM_ERR_INVALID_ARG for an unknown format or layout, null pointers or
+ * non-positive n or k; QMM_ERR_UNSUPPORTED when m * k or n * k reaches 2^31.
+ * m = 0 is a no-op.
+ */
+typedef enum qmm_lowp_format {
+  QMM_LOWP_E4M3 = 0, QMM_LOWP_E5M2 = 1, QMM_LOWP_E2M3 = 2, QMM_LOWP_E3M2 = 3, QMM_LOWP_E2M1 = 4
+} qmm_lowp_format;
+typedef enum qmm_lowp_layout {
+  QMM_LOWP_PER_TENSOR = 0, QMM_LOWP_MX = 1, QMM_LOWP_NVFP4 = 2
+} qmm_lowp_layout;
+
+int qmm_lowp_matmul(const uint8_t *lhs, const uint8_t *rhs, const void *lhs_scales,
+                    const void *rhs_scales, const float *bias, float *out, int64_t m,
+                    int64_t n, int64_t k, int layout, int lhs_format, int rhs_format,
+                    void *stream);
+
+/*
  * A step: a fixed sequence of matmul calls (say the projections of one
  * decode step) recorded once and replayed as one HIP graph.  The pages find
  * the decode step's cost outside the kernels -- per-operator dispatch and

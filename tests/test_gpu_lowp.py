@@ -1,0 +1,171 @@
+"""GPU parity of the low-precision scaled GEMM (qmm_lowp_matmul) against the
+oracle (rlx-cpu quant.rs: lowp_scaled_matmul, lowp_read_scales).
+
+* Exact data: element values from {0, 0.5, 1, 1.5, 2, 3, 4, 6} (in every
+  format), scales 2^-1..2^1 (and 1.5 for NVFP4), so every product and partial
+  sum is exact in fp32: the output equals the oracle's value, for all 25
+  format pairs, the three scale layouts, ragged m / n and k (a partial last
+  block, k not a multiple of 16, k below one step).
+* Random codes of every format (nan and inf codes excluded) with random
+  scales, within the bound of the instruction's arithmetic: the
+  block-scaled matrix-core instruction adds the products of each aligned
+  group of 8 elements of K in a fixed-point sum aligned to the group's
+  largest product, cut 2^-14 below it (measured on gfx950: with 448 * 448
+  at k = 0, a product of 4 at k = 1..7 is dropped, at k = 8 it is kept), and
+  the group sums in fp32.  Bound, with a factor 2 on the cut (its position
+  relative to a product's own exponent) and one more cut unit for the group
+  sum: |gpu - oracle| <= 8 * 2^-12 * sum_g max_g |a b| + (k / 8 + 16) *
+  2^-24 * S, S = sum |a b| + |bias|.
+* The MXFP4 x MXFP4 prefill shape (m 2048, k 4096, n 14336) on sampled rows
+  and columns; rows are independent of the batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMTS = ["e4m3", "e5m2", "e2m3", "e3m2", "e2m1"]
+LAYOUTS = ["tensor", "mx", "nvfp4"]
+VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def qmm():
+    from block_quantized_weight_matmulnbits_amd import qmm as q
+    return q
+
+
+def codes_of(values, fmt):
+    table = {v: oracle.lowp_encode(fmt, v) for v in set(np.ravel(values).tolist())}
+    return np.vectorize(lambda v: table[v])(values).astype(np.uint8)
+
+
+def stored_scales(rng, rows, nb, layout, exact):
+    """Stored scales and their raw float32 values."""
+    if layout == "tensor":
+        st = np.array([rng.choice([0.5, 1.0, 2.0]) if exact else rng.uniform(0.01, 3.0)],
+                      np.float32)
+    elif layout == "mx":
+        st = rng.integers(126, 129, (rows, nb)) if exact else rng.integers(110, 140, (rows, nb))
+        st = st.astype(np.uint8)
+    else:
+        pool = [0.5, 1.0, 1.5, 2.0] if exact else None
+        if exact:
+            st = codes_of(rng.choice(pool, (rows, nb)), "e4m3")
+        else:
+            st = rng.integers(0x18, 0x60, (rows, nb)).astype(np.uint8)
+    return st, oracle.lowp_read_scales(st, layout)
+
+
+def run(lhs, rhs, ls, rs, bias, m, n, k, layout, lf, rf):
+    out = torch.empty(m, n, dtype=torch.float32, device=DEV)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    qmm().qmm_lowp_matmul(t(lhs), t(rhs), t(ls), t(rs), t(bias), out, m, n, k, layout, lf, rf)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def nblocks(k, layout):
+    return 1 if layout == "tensor" else -(-k // (32 if layout == "mx" else 16))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("lf", FMTS)
+def test_exact_data_every_format_pair(layout, lf):
+    for rf in FMTS:
+        for i, (m, n, k) in enumerate([(37, 45, 200), (130, 129, 256), (5, 200, 40), (3, 7, 5)]):
+            rng = np.random.default_rng(1000 * FMTS.index(lf) + 10 * FMTS.index(rf) + i)
+            sign = lambda shape: np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+            lv = rng.choice(VALUES, (m, k)) * sign((m, k))
+            rv = rng.choice(VALUES, (n, k)) * sign((n, k))
+            lhs, rhs = codes_of(lv, lf), codes_of(rv, rf)
+            nb = nblocks(k, layout)
+            lst, lsr = stored_scales(rng, m, nb, layout, True)
+            rst, rsr = stored_scales(rng, n, nb, layout, True)
+            bias = rng.integers(-4, 5, n).astype(np.float32) if i % 2 == 0 else None
+            print(f"[lowp exact] {layout} {lf} x {rf} m={m} n={n} k={k}", flush=True)
+            want, _ = oracle.lowp_scaled_matmul(lhs, rhs, lsr, rsr, bias, layout, lf, rf)
+            got = run(lhs, rhs, lst, rst, bias, m, n, k, layout, lf, rf)
+            assert np.array_equal(got, want.astype(np.float32)), (layout, lf, rf, m, n, k)
+
+
+def hw_bound(lhs, rhs, lsr, rsr, layout, lf, rf, S):
+    """Per-output error bound of the instruction's arithmetic (module doc)."""
+    a = np.abs(oracle.lowp_dequantize(lhs, lsr, lf, layout))
+    b = np.abs(oracle.lowp_dequantize(rhs, rsr, rf, layout))
+    k = a.shape[1]
+    kp = -(-k // 8) * 8
+    a = np.pad(a, ((0, 0), (0, kp - k))).reshape(a.shape[0], 1, kp // 8, 8)
+    b = np.pad(b, ((0, 0), (0, kp - k))).reshape(1, b.shape[0], kp // 8, 8)
+    gmax = (a * b).max(axis=3).sum(axis=2)
+    return 8 * 2.0 ** -12 * gmax + (k / 8 + 16) * 2.0 ** -24 * S
+
+
+def finite_random_codes(rng, shape, fmt):
+    bits = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}[fmt]
+    c = rng.integers(0, 1 << bits, shape).astype(np.uint8)
+    if fmt == "e4m3":
+        c[(c & 0x7F) == 0x7F] = 0x7E
+    if fmt == "e5m2":
+        c[(c & 0x7C) == 0x7C] = 0x7B
+    return c
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_random_codes_within_tolerance(layout):
+    for i, (lf, rf) in enumerate([(a, b) for a in FMTS for b in FMTS]):
+        rng = np.random.default_rng(7 + i)
+        m, n, k = [(64, 96, 1024), (33, 17, 300), (128, 256, 512)][i % 3]
+        lhs, rhs = finite_random_codes(rng, (m, k), lf), finite_random_codes(rng, (n, k), rf)
+        nb = nblocks(k, layout)
+        lst, lsr = stored_scales(rng, m, nb, layout, False)
+        rst, rsr = stored_scales(rng, n, nb, layout, False)
+        bias = rng.standard_normal(n).astype(np.float32)
+        want, S = oracle.lowp_scaled_matmul(lhs, rhs, lsr, rsr, bias, layout, lf, rf)
+        got = run(lhs, rhs, lst, rst, bias, m, n, k, layout, lf, rf)
+        err = np.abs(got - want)
+        bound = hw_bound(lhs, rhs, lsr, rsr, layout, lf, rf, S)
+        print(f"[lowp random] {layout} {lf} x {rf} m={m} n={n} k={k}: max err/S "
+              f"{float(np.max(err / S)):.2e}, max err/bound {float(np.max(err / bound)):.3f}",
+              flush=True)
+        assert np.all(err <= bound), (layout, lf, rf)
+
+
+def test_prefill_shape_mxfp4_sampled():
+    """m 2048, k 4096, n 14336, E2M1 x E2M1 with MX scales: 8 sampled rows (the
+    first and last included) against the oracle on 1024 sampled columns."""
+    rng = np.random.default_rng(3)
+    m, n, k = 2048, 14336, 4096
+    lhs = rng.integers(0, 16, (m, k)).astype(np.uint8)
+    rhs = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    lst = rng.integers(118, 124, (m, k // 32)).astype(np.uint8)
+    rst = rng.integers(118, 124, (n, k // 32)).astype(np.uint8)
+    got = run(lhs, rhs, lst, rst, None, m, n, k, "mx", "e2m1", "e2m1")
+    rows = np.array([0, 1, 517, 1024, 1500, 2000, 2046, 2047])
+    cols = np.sort(rng.choice(n, 1024, replace=False))
+    cols[0], cols[-1] = 0, n - 1
+    want, S = oracle.lowp_scaled_matmul(lhs[rows], rhs[cols], oracle.lowp_read_scales(lst[rows], "mx"),
+                                        oracle.lowp_read_scales(rst[cols], "mx"), None, "mx",
+                                        "e2m1", "e2m1")
+    bound = hw_bound(lhs[rows], rhs[cols], oracle.lowp_read_scales(lst[rows], "mx"),
+                     oracle.lowp_read_scales(rst[cols], "mx"), "mx", "e2m1", "e2m1", S)
+    assert np.all(np.abs(got[np.ix_(rows, cols)] - want) <= bound)
+
+
+def test_rows_are_independent_and_m_zero_is_a_no_op():
+    rng = np.random.default_rng(5)
+    m, n, k = 300, 200, 512
+    lhs, rhs = finite_random_codes(rng, (m, k), "e4m3"), finite_random_codes(rng, (n, k), "e2m1")
+    lst = rng.integers(120, 130, (m, k // 32)).astype(np.uint8)
+    rst = rng.integers(120, 130, (n, k // 32)).astype(np.uint8)
+    full = run(lhs, rhs, lst, rst, None, m, n, k, "mx", "e4m3", "e2m1")
+    part = run(lhs[140:150], rhs, lst[140:150], rst, None, 10, n, k, "mx", "e4m3", "e2m1")
+    assert np.array_equal(full[140:150], part)
+    out = torch.full((1, n), 7.0, device=DEV)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    qmm().qmm_lowp_matmul(t(lhs[:1]), t(rhs), t(lst[:1]), t(rst), None, out, 0, n, k, "mx",
+                          "e4m3", "e2m1")
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
