@@ -485,6 +485,37 @@ int qmm_lowp_matmul(const uint8_t* lhs, const uint8_t* rhs, const void* lhs_scal
   return hip_status(qmm::launch_lowp_matmul(a), fn);
 }
 
+int qmm_lowp_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int format,
+                      int layout, uint8_t* codes, void* scales, void* stream) {
+  const char* fn = "qmm_lowp_quantize";
+  if (layout < QMM_LOWP_PER_TENSOR || layout > QMM_LOWP_NVFP4)
+    return fail(QMM_ERR_INVALID_ARG, "%s: layout=%d is not a qmm_lowp_layout. How to fix: pass "
+                "QMM_LOWP_PER_TENSOR, QMM_LOWP_MX or QMM_LOWP_NVFP4.", fn, layout);
+  if (format < QMM_LOWP_E4M3 || format > QMM_LOWP_E2M1)
+    return fail(QMM_ERR_INVALID_ARG, "%s: format=%d is not a qmm_lowp_format. How to fix: pass "
+                "QMM_LOWP_E4M3, _E5M2, _E2M3, _E3M2 or _E2M1.", fn, format);
+  if (dtype_size(x_dtype) == 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: x_dtype=%d is not a qmm_dtype. How to fix: pass "
+                "QMM_F32, QMM_F16 or QMM_BF16.", fn, x_dtype);
+  if (cols <= 0 || rows < 0)
+    return fail(QMM_ERR_INVALID_ARG, "%s: cols must be positive and rows >= 0 (got rows=%lld "
+                "cols=%lld).", fn, (long long)rows, (long long)cols);
+  if (rows > 0 && (x == nullptr || codes == nullptr || scales == nullptr))
+    return fail(QMM_ERR_INVALID_ARG, "%s: x, codes and scales must be non-null device "
+                "pointers.", fn);
+  if (!aligned(x, dtype_size(x_dtype)) || (layout == QMM_LOWP_PER_TENSOR && !aligned(scales, 4)))
+    return fail(QMM_ERR_INVALID_ARG, "%s: x must be aligned to its element size and a per-tensor "
+                "scale to 4 bytes.", fn);
+  if (rows * cols + 64 > INT32_MAX)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: rows * cols (%lld) reaches 2^31. How to fix: quantize "
+                "in row slices.", fn, (long long)(rows * cols));
+  if (rows == 0) return QMM_OK;
+  qmm::LowpQuantArgs a;
+  a.x = x; a.codes = codes; a.scales = scales; a.rows = rows; a.cols = cols;
+  a.x_dtype = x_dtype; a.fmt = format; a.layout = layout; a.stream = (hipStream_t)stream;
+  return hip_status(qmm::launch_lowp_quantize(a), fn);
+}
+
 int qconv_int8(const int8_t* X, const int8_t* Wt, const int32_t* bias, const float* w_scale,
                float in_scale, float out_scale, int in_zp, int out_zp, int clamp_min,
                int clamp_max, int Nb, int H, int W, int C, int Co, int KH, int KW, int stride_h,

@@ -106,6 +106,15 @@ struct LowpArgs {
   hipStream_t stream = nullptr;
 };
 hipError_t launch_lowp_matmul(const LowpArgs& a);
+struct LowpQuantArgs {
+  const void* x = nullptr;        // [rows, cols] x_dtype
+  uint8_t* codes = nullptr;       // [rows, cols]
+  void* scales = nullptr;         // per tensor: one f32; else [rows, nblk] bytes
+  int64_t rows = 0, cols = 0;
+  int x_dtype = 0, fmt = 0, layout = 0;
+  hipStream_t stream = nullptr;
+};
+hipError_t launch_lowp_quantize(const LowpQuantArgs& a);
 
 // int8 convolution (validated NHWC / OHWI problem).
 struct ConvArgs {

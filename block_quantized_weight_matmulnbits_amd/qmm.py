@@ -40,6 +40,7 @@ _SIGS = {
     "qmm_compint8_workspace_size": ([_i64, _i64, _i32], _sz),
     "qmm_lowp_matmul": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp],
                         _i32),
+    "qmm_lowp_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp], _i32),
     "qmm_gemm_compint8": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
                            _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "qmm_gemm_compint8_noalloc": ([_vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
@@ -376,3 +377,12 @@ def qmm_lowp_matmul(lhs, rhs, lhs_scales, rhs_scales, bias, out, m, n, k, layout
     rf = LOWP_FORMATS[rhs_format] if isinstance(rhs_format, str) else int(rhs_format)
     _check(lib.qmm_lowp_matmul(_ptr(lhs), _ptr(rhs), _ptr(lhs_scales), _ptr(rhs_scales),
                                _ptr(bias), _ptr(out), m, n, k, lay, lf, rf, _stream(stream)))
+
+
+def qmm_lowp_quantize(x, codes, scales, rows, cols, fmt, layout, stream=None):
+    """codes [rows, cols] uint8 and scales (one f32 per tensor, else
+    [rows, ceil(cols / bs)] bytes) of x [rows, cols] (f32 / f16 / bf16)."""
+    lay = LOWP_LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    f = LOWP_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    _check(lib.qmm_lowp_quantize(_ptr(x), _dt(x), rows, cols, f, lay, _ptr(codes), _ptr(scales),
+                                 _stream(stream)))

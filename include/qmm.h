@@ -280,6 +280,27 @@ int qmm_lowp_matmul(const uint8_t *lhs, const uint8_t *rhs, const void *lhs_scal
                     void *stream);
 
 /*
+ * The operand producer of qmm_lowp_matmul (rlx-cpu quant.rs:
+ * lowp_compute_scales with lowp_snap_scale and the stored forms of
+ * ScaledQuantScale, then lowp_quantize), for x [rows, cols] in x_dtype
+ * (f32, f16, bf16; 16-bit values are taken exactly as binary32):
+ *   scale  per tensor: amax(|x|) / max_finite(format) (1 if amax is 0),
+ *          written as one f32; MX / NVFP4: the same per block of 32 / 16
+ *          along cols, snapped (E8M0: the binary32 exponent field; NVFP4:
+ *          the nearest E4M3) and written as [rows, ceil(cols / bs)] bytes
+ *   codes  [rows, cols] uint8: encode(x / scale) with the binary32 quotient
+ *          (0 where the scale is 0): the nearest finite value of the format,
+ *          ties to the even mantissa, saturating past the largest finite
+ *          value, nan to the format's nan (E4M3 / E5M2 0x7F) or 0
+ * Maxima skip nan.  Per tensor runs four kernels on `stream` (the scale
+ * slot holds amax in between).  Errors: QMM_ERR_INVALID_ARG for an unknown
+ * format, layout or dtype, null pointers or non-positive cols;
+ * QMM_ERR_UNSUPPORTED when rows * cols reaches 2^31.  rows = 0 is a no-op.
+ */
+int qmm_lowp_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int format,
+                      int layout, uint8_t *codes, void *scales, void *stream);
+
+/*
  * A step: a fixed sequence of matmul calls (say the projections of one
  * decode step) recorded once and replayed as one HIP graph.  The pages find
  * the decode step's cost outside the kernels -- per-operator dispatch and
