@@ -18,14 +18,17 @@
 // since an element has at most 4 significant bits and an E4M3 scale 4 -- and
 // the bf16 matrix-core instruction accumulates in fp32.
 //
-// Tiles: a workgroup of 4 waves (2 x 2) owns 128 x 128 outputs, each wave
-// 64 x 64 as 4 x 4 MFMA tiles; per K-step of 128 every thread loads four
-// 16-byte pieces of each operand (16 codes of one row), packs them to the
-// instruction's operand width (8, 6 or 4 bits per code; bf16 values for
-// NVFP4) and stores them to LDS in fragment order: fragment (row tile t,
-// K-group g, row r) -- the 32 elements lane 16 g + r of a wave reads -- so
-// a wave's fragment read is one contiguous run.  Double-buffered; the next
-// step's pieces are loaded into registers while this step's MFMAs run.
+// Tiles: a workgroup of 4 or 8 waves (2 x 2 or 4 x 2) owns 128 x 128 or
+// 256 x 128 outputs, each wave 64 x 64 as 4 x 4 MFMA tiles; per K-step of
+// 128 every thread loads 16-byte pieces of each operand (16 codes of one
+// row), packs them to the instruction's operand width (8, 6 or 4 bits per
+// code; bf16 values for NVFP4) and stores them to LDS in fragment order:
+// fragment (row tile t, K-group g, row r) -- the 32 elements lane 16 g + r of
+// a wave reads -- so a wave's fragment read is one contiguous run.  LDS is
+// double-buffered and the pieces are loaded into registers two steps ahead.
+// Measured (m 2048, k 4096, n 14336): the MFMAs are not the bound (removing
+// them changes the time by under 15 %); the byte-per-code operand loads and
+// the pack-and-store into LDS are, behind one barrier per step.
 #include <type_traits>
 
 #include "lowp.h"
@@ -40,6 +43,26 @@ constexpr int LT = 128;      // tile rows and columns
 constexpr int LK = 128;      // K per step
 constexpr int LTPB = 256;    // 4 waves
 constexpr int LOWP_OOB = 0x7FFFFFF0;
+
+// Output tile of workgroup b.  Workgroups are dispatched round robin over the
+// 8 XCDs (b % 8), each with its own L2.  With the plain order (consecutive
+// workgroups take consecutive M tiles of one N tile) every XCD keeps its
+// rows of lhs in L2 but reads all of rhs through the fabric; when the grid
+// splits evenly, XCD x instead owns M tiles of group x % 4 (a quarter of
+// lhs) and N tiles of half x / 4 (half of rhs), walking its M tiles fastest,
+// so its lhs rows stay in L2 and each rhs tile crosses the fabric to only 4
+// XCDs: half the fabric traffic of the plain order.
+__device__ __forceinline__ void lowp_tile(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if ((tiles_m & 3) == 0 && (tiles_n & 1) == 0) {
+    const int x = b & 7, q = b >> 3;
+    const int gm = tiles_m >> 2;                   // M tiles per group
+    tm = (x & 3) * gm + q % gm;
+    tn = (x >> 2) * (tiles_n >> 1) + q / gm;
+  } else {
+    tm = b % tiles_m;
+    tn = b / tiles_m;
+  }
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -90,22 +113,34 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int row, int r
 
 // ---------------------------------------------------------------------------
 // Per tensor (LAYOUT 0) and MX (LAYOUT 1): the block-scaled instruction.
+// WM waves along M (2: 128-row tiles, 256 threads; 4: 256-row tiles, 512
+// threads), 2 along N; each wave 64 x 64.  SS (MX with k % 128 == 0 and
+// 4-byte aligned scales): a step's scale bytes -- 4 blocks of each tile row,
+// one 32-bit word -- are loaded by one thread per row with the codes and
+// staged in LDS beside them; otherwise each lane loads its bytes.
 // ---------------------------------------------------------------------------
-template <int LF, int RF, int LAYOUT, bool VEC>
-__global__ __launch_bounds__(LTPB) void lowp_mfma_kernel(
+template <int LF, int RF, int LAYOUT, bool VEC, int WM, bool SS>
+__global__ __launch_bounds__(128 * WM) void lowp_mfma_kernel(
     const uint8_t* __restrict__ lhs, const uint8_t* __restrict__ rhs,
     const void* __restrict__ lsc, const void* __restrict__ rsc, const float* __restrict__ bias,
     float* __restrict__ out, int m, int n, int k, int tiles_m) {
+  constexpr int TPB = 128 * WM, LTM = 64 * WM;
+  constexpr int RPP = TPB / 8;                      // tile rows per load pass
+  constexpr int PA = LTM / RPP, PB = LT / RPP;      // passes: A, B
   constexpr int LS = slot_bytes<LF>(), RS = slot_bytes<RF>();
-  constexpr int LST = LT * LK / 32 * LS, RST = LT * LK / 32 * RS;   // stage bytes
+  constexpr int LST = LTM * LK / 32 * LS, RST = LT * LK / 32 * RS;   // stage bytes
+  constexpr int SROWS = LTM + LT;                   // staged scale words per step
+  constexpr int SW = (SROWS + TPB - 1) / TPB;       // scale words per thread
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_l[];
-  uint8_t* As = lds_l;                    // [2][LST]
-  uint8_t* Bs = lds_l + 2 * LST;          // [2][RST]
+  uint8_t* As = lds_l;                              // [2][LST]
+  uint8_t* Bs = lds_l + 2 * LST;                    // [2][RST]
+  uint32_t* Ss = reinterpret_cast<uint32_t*>(lds_l + 2 * LST + 2 * RST);   // [2][SROWS]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
-  const int m0 = tile_m * LT, n0 = tile_n * LT;
+  int tile_m, tile_n;
+  lowp_tile(blockIdx.x, tiles_m, (int)gridDim.x / tiles_m, tile_m, tile_n);
+  const int m0 = tile_m * LTM, n0 = tile_n * LT;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int nblk = (k + 31) / 32;
 
@@ -116,63 +151,88 @@ __global__ __launch_bounds__(LTPB) void lowp_mfma_kernel(
   const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)rsc, 0, LAYOUT == 1 ? n * nblk : 0, BUF_WORD3);
 
-  // Thread t loads, in pass p, 16 codes of tile row 32 p + t / 8 at K offset
-  // 16 c, c = t % 8.  The instruction's lane groups g = 0..3 hold, for FP6
-  // and FP4 operands, K 32 g .. 32 g + 31 (piece c: group c / 2, half c % 2),
-  // and for FP8 operands K 16 g .. 16 g + 15 in their first four registers
-  // and 64 + 16 g .. 64 + 16 g + 15 in the other four (piece c: group c % 4,
-  // half c / 4).  Either way the block scale of K 32 b .. 32 b + 31 is the
-  // one lane group b passes (measured on gfx950 with one-hot operands).
+  // Thread t loads, in pass p, 16 codes of tile row RPP p + t / 8 at K
+  // offset 16 c, c = t % 8.  The instruction's lane groups g = 0..3 hold, for
+  // FP6 and FP4 operands, K 32 g .. 32 g + 31 (piece c: group c / 2, half
+  // c % 2), and for FP8 operands K 16 g .. 16 g + 15 in their first four
+  // registers and 64 + 16 g .. 64 + 16 g + 15 in the other four (piece c:
+  // group c % 4, half c / 4).  Either way the block scale of K 32 b ..
+  // 32 b + 31 is the one lane group b passes (measured on gfx950 with
+  // one-hot operands).
   const int lrow = tid >> 3, lkk = (tid & 7) * 16;
   auto piece_slot = [&](int bits, int& g, int& half) {
     const int c = tid & 7;
     g = bits == 8 ? (c & 3) : (c >> 1);
     half = bits == 8 ? (c >> 2) : (c & 1);
   };
-  u32x4 pa[4], pb[4];
-  auto load = [&](int k0) {
+  // Two register stages (stage = step parity): the codes of step s + 2 are
+  // loaded while step s multiplies and step s + 1 is packed into LDS.
+  u32x4 pa[2][PA], pb[2][PB];
+  uint32_t sw[2][SW];
+  auto load = [&](int k0, int st) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      pa[p] = load16<VEC>(rl, m0 + 32 * p + lrow, m, k0 + lkk, k);
-      pb[p] = load16<VEC>(rh, n0 + 32 * p + lrow, n, k0 + lkk, k);
+    for (int p = 0; p < PA; ++p) pa[st][p] = load16<VEC>(rl, m0 + RPP * p + lrow, m, k0 + lkk, k);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) pb[st][p] = load16<VEC>(rh, n0 + RPP * p + lrow, n, k0 + lkk, k);
+    if constexpr (SS) {
+#pragma unroll
+      for (int i = 0; i < SW; ++i) {
+        const int r = tid + i * TPB;
+        const bool isa = r < LTM;
+        const int row = isa ? m0 + r : n0 + r - LTM;
+        const bool ok = r < SROWS && row < (isa ? m : n);
+        const int off = ok ? row * nblk + k0 / 32 : LOWP_OOB;
+        sw[st][i] = isa ? __builtin_amdgcn_raw_buffer_load_b32(rls, off, 0, 0)
+                        : __builtin_amdgcn_raw_buffer_load_b32(rrs, off, 0, 0);
+      }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int st) {
+    int g, half;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int row = 32 * p + lrow;
-      int g, half;
+    for (int p = 0; p < PA; ++p) {
+      const int row = RPP * p + lrow;
       piece_slot(LowpFmt<LF>::BITS, g, half);
       const int fa = ((row >> 4) * 4 + g) * 16 + (row & 15);
       uint32_t o[4];
-      pack16<LF>(pa[p], o);
+      pack16<LF>(pa[st][p], o);
       uint32_t* da = reinterpret_cast<uint32_t*>(As + buf * LST + fa * LS + half * (2 * LowpFmt<LF>::BITS));
 #pragma unroll
       for (int j = 0; j < LowpFmt<LF>::BITS / 2; ++j) da[j] = o[j];
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int row = RPP * p + lrow;
       piece_slot(LowpFmt<RF>::BITS, g, half);
       const int fb = ((row >> 4) * 4 + g) * 16 + (row & 15);
-      pack16<RF>(pb[p], o);
+      uint32_t o[4];
+      pack16<RF>(pb[st][p], o);
       uint32_t* db = reinterpret_cast<uint32_t*>(Bs + buf * RST + fb * RS + half * (2 * LowpFmt<RF>::BITS));
 #pragma unroll
       for (int j = 0; j < LowpFmt<RF>::BITS / 2; ++j) db[j] = o[j];
     }
+    if constexpr (SS) {
+#pragma unroll
+      for (int i = 0; i < SW; ++i)
+        if (tid + i * TPB < SROWS) Ss[buf * SROWS + tid + i * TPB] = sw[st][i];
+    }
   };
-  // The E8M0 byte of this lane's block for row tile i of the wave (127, a
-  // unit scale, per tensor and past the last block).
-  uint32_t sa[4], sb[4];
-  auto load_scales = [&](int k0) {
+  // Without staging: the E8M0 byte of this lane's block for row tile i of
+  // the wave (127, a unit scale, per tensor and past the last block).
+  uint32_t sa[2][4], sb[2][4];
+  auto load_scales = [&](int k0, int st) {
     const int blk = k0 / 32 + (lane >> 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (LAYOUT == 1) {
+      if constexpr (LAYOUT == 1 && !SS) {
         const int ra = m0 + wm + 16 * i + (lane & 15), rb = n0 + wn + 16 * i + (lane & 15);
-        sa[i] = blk < nblk ? __builtin_amdgcn_raw_buffer_load_b8(rls, ra < m ? ra * nblk + blk : LOWP_OOB, 0, 0)
-                           : 127u;
-        sb[i] = blk < nblk ? __builtin_amdgcn_raw_buffer_load_b8(rrs, rb < n ? rb * nblk + blk : LOWP_OOB, 0, 0)
-                           : 127u;
+        sa[st][i] = blk < nblk ? __builtin_amdgcn_raw_buffer_load_b8(rls, ra < m ? ra * nblk + blk : LOWP_OOB, 0, 0)
+                               : 127u;
+        sb[st][i] = blk < nblk ? __builtin_amdgcn_raw_buffer_load_b8(rrs, rb < n ? rb * nblk + blk : LOWP_OOB, 0, 0)
+                               : 127u;
       } else {
-        sa[i] = 127u;
-        sb[i] = 127u;
+        sa[st][i] = 127u;
+        sb[st][i] = 127u;
       }
     }
   };
@@ -197,32 +257,52 @@ __global__ __launch_bounds__(LTPB) void lowp_mfma_kernel(
   };
 
   const int nsteps = (k + LK - 1) / LK;
-  load(0);
-  load_scales(0);
-  store(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
+  // Step s (register stage and LDS buffer s & 1 = ST): load step s + 2 into
+  // stage ST, multiply buffer ST, pack stage ST ^ 1 (step s + 1) into buffer
+  // ST ^ 1.  Loads past the last step read nothing (zero pieces).
+  auto step = [&](int s, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
     uint32_t csa[4], csb[4];
+    if constexpr (SS) {
+      const int sh = 8 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { csa[i] = sa[i]; csb[i] = sb[i]; }
-    if (s + 1 < nsteps) {
-      load((s + 1) * LK);
-      load_scales((s + 1) * LK);
+      for (int i = 0; i < 4; ++i) {
+        csa[i] = Ss[ST * SROWS + wm + 16 * i + (lane & 15)] >> sh;
+        csb[i] = Ss[ST * SROWS + LTM + wn + 16 * i + (lane & 15)] >> sh;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { csa[i] = sa[ST][i]; csb[i] = sb[ST][i]; }
+    }
+    if (s + 2 < nsteps) {
+      load((s + 2) * LK, ST);
+      load_scales((s + 2) * LK, ST);
     }
     v8i b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frag(Bs + buf * RST, RS, (wn >> 4) + j);
+    for (int j = 0; j < 4; ++j) b[j] = frag(Bs + ST * RST, RS, (wn >> 4) + j);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const v8i a = frag(As + buf * LST, LS, (wm >> 4) + i);
+      const v8i a = frag(As + ST * LST, LS, (wm >> 4) + i);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             a, b[j], acc[i][j], LF, RF, 0, (int)csa[i], 0, (int)csb[j]);
     }
-    if (s + 1 < nsteps) store(buf ^ 1);
+    if (s + 1 < nsteps) store(ST ^ 1, ST ^ 1);
     __syncthreads();
+  };
+  load(0, 0);
+  load_scales(0, 0);
+  if (nsteps > 1) {
+    load(LK, 1);
+    load_scales(LK, 1);
+  }
+  store(0, 0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
   }
 
   // Per tensor: the product of the two f32 scales.
@@ -261,7 +341,8 @@ __global__ __launch_bounds__(LTPB) void lowp_nvfp4_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  int tile_m, tile_n;
+  lowp_tile(blockIdx.x, tiles_m, (int)gridDim.x / tiles_m, tile_m, tile_n);
   const int m0 = tile_m * LT, n0 = tile_n * LT;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int nblk = (k + 15) / 16;
@@ -377,15 +458,36 @@ hipError_t launch_pair(const LowpArgs& a) {
                        (const uint8_t*)a.rsc, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tiles_m);
     return hipGetLastError();
   }
-  const size_t lds = 2 * (size_t)LT * LK / 32 * (slot_bytes<LF>() + slot_bytes<RF>());
-  decltype(&lowp_mfma_kernel<LF, RF, 0, true>) kern;
-  if (a.layout == 0) kern = vec ? lowp_mfma_kernel<LF, RF, 0, true> : lowp_mfma_kernel<LF, RF, 0, false>;
-  else kern = vec ? lowp_mfma_kernel<LF, RF, 1, true> : lowp_mfma_kernel<LF, RF, 1, false>;
-  const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, block, lds, a.stream, a.lhs, a.rhs, a.lsc, a.rsc, a.bias, a.out,
-                     (int)a.m, (int)a.n, (int)a.k, tiles_m);
-  return hipGetLastError();
+  // 256-row tiles when their grid still fills the chip, else 128.
+  const int tiles_m4 = (int)((a.m + 255) / 256);
+  const bool wide = (int64_t)tiles_m4 * tiles_n >= 256;
+  const bool ss = a.layout == 1 && (a.k % 128) == 0 && ((uintptr_t)a.lsc & 3) == 0 &&
+                  ((uintptr_t)a.rsc & 3) == 0;
+  auto go = [&](auto wm_tag, auto ss_tag) {
+    constexpr int WM = decltype(wm_tag)::value;
+    constexpr bool SS = decltype(ss_tag)::value;
+    const int tm = WM == 4 ? tiles_m4 : tiles_m;
+    const size_t lds = 2 * (size_t)LK / 32 * (64 * WM * slot_bytes<LF>() + LT * slot_bytes<RF>()) +
+                       (SS ? 2 * (size_t)(64 * WM + LT) * 4 : 0);
+    decltype(&lowp_mfma_kernel<LF, RF, 0, true, WM, SS>) kern;
+    if constexpr (WM == 2 && !SS) {
+      // The byte-load fallback (k % 16 != 0 or unaligned codes) only here.
+      if (a.layout == 0) kern = vec ? lowp_mfma_kernel<LF, RF, 0, true, 2, false> : lowp_mfma_kernel<LF, RF, 0, false, 2, false>;
+      else kern = vec ? lowp_mfma_kernel<LF, RF, 1, true, 2, false> : lowp_mfma_kernel<LF, RF, 1, false, 2, false>;
+    } else {
+      kern = a.layout == 0 ? lowp_mfma_kernel<LF, RF, 0, true, WM, SS> : lowp_mfma_kernel<LF, RF, 1, true, WM, SS>;
+    }
+    const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(tm * tiles_n), dim3(128 * WM), lds, a.stream, a.lhs, a.rhs, a.lsc,
+                       a.rsc, a.bias, a.out, (int)a.m, (int)a.n, (int)a.k, tm);
+    return hipGetLastError();
+  };
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  if (!vec) return go(I2{}, std::false_type{});
+  if (wide) return ss ? go(I4{}, std::true_type{}) : go(I4{}, std::false_type{});
+  return ss ? go(I2{}, std::true_type{}) : go(I2{}, std::false_type{});
 }
 
 template <int LF>

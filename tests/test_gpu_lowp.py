@@ -231,3 +231,26 @@ def test_quantize_then_matmul(layout):
     # pipeline, not a bound of the method).
     rel = np.abs(got - x @ w.T).max() / np.abs(x @ w.T).max()
     assert rel < 0.5, rel
+
+
+@pytest.mark.parametrize("lf,rf", [("e2m1", "e2m1"), ("e4m3", "e2m1"), ("e5m2", "e3m2")])
+def test_tile_and_scale_routes_exact_sampled(lf, rf):
+    """Exact data on each route of the block-scaled kernel: 256-row tiles
+    (grid of at least 256 workgroups) and 128-row tiles, MX scale words staged
+    in LDS (k % 128 == 0) or loaded per lane, per-tensor scales; 12 sampled
+    rows (first and last included) against the oracle on all columns."""
+    for i, (m, n, k, layout) in enumerate([(1100, 8000, 200, "mx"), (1100, 8000, 256, "mx"),
+                                           (1100, 8000, 256, "tensor"), (300, 500, 384, "mx")]):
+        rng = np.random.default_rng(40 + i)
+        sign = lambda shape: np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+        lhs = codes_of(rng.choice(VALUES, (m, k)) * sign((m, k)), lf)
+        rhs = codes_of(rng.choice(VALUES, (n, k)) * sign((n, k)), rf)
+        nb = nblocks(k, layout)
+        lst, lsr = stored_scales(rng, m, nb, layout, True)
+        rst, rsr = stored_scales(rng, n, nb, layout, True)
+        print(f"[lowp route] {lf} x {rf} {layout} m={m} n={n} k={k}", flush=True)
+        got = run(lhs, rhs, lst, rst, None, m, n, k, layout, lf, rf)
+        rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 10, replace=False)]))
+        want, _ = oracle.lowp_scaled_matmul(lhs[rows], rhs, lsr if layout == "tensor" else lsr[rows],
+                                            rsr, None, layout, lf, rf)
+        assert np.array_equal(got[rows], want.astype(np.float32)), (m, n, k, layout)
