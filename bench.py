@@ -30,6 +30,8 @@ import torch
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA
+FP4_PEAK_TFLOPS = 10066.3      # MI355X dense fp4 / fp6 MFMA
 POOL_BYTES = 640 << 20         # rotating weight pool, > 2x the Infinity Cache
 COPY_CAL_BYTES = 256 << 20     # plain copy used to scale the HBM byte counters
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
@@ -67,7 +69,8 @@ def parse():
                         "scaling the FETCH_SIZE / WRITE_SIZE counters of profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
-    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4", "lowbit", "batched"],
+    p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4", "lowbit", "batched",
+                                      "lowp"],
                    default=None,
                    help="time only this workload and print its object (profiling runs)")
     p.add_argument("--read-sweep", action="store_true",
@@ -109,7 +112,7 @@ def main():
             del src, dst
         fn = {"compint8": bench_compint8, "prefill": bench_prefill, "conv": bench_conv,
               "tiny": bench_tiny, "fp4": bench_fp4, "lowbit": bench_lowbit,
-              "batched": bench_batched}[args.only]
+              "batched": bench_batched, "lowp": bench_lowp}[args.only]
         print(json.dumps({args.only: fn(qmm, dev, stream, args)}), flush=True)
         return
     if args.copy_calibration:
@@ -352,6 +355,7 @@ def main():
     out["conv_int8"] = bench_conv(qmm, dev, stream, args)
     out["fp4"] = bench_fp4(qmm, dev, stream, args)
     out["lowbit"] = bench_lowbit(qmm, dev, stream, args)
+    out["lowp"] = bench_lowp(qmm, dev, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
@@ -680,6 +684,72 @@ def bench_fp4(qmm, dev, stream, args):
                                                flop / (msp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         }
         del p, Y
+    return res
+
+
+def bench_lowp(qmm, dev, stream, args):
+    """Low-precision scaled GEMM (qmm_lowp_matmul) on the prefill shape
+    m=2048, k=4096, n=14336: operands produced by qmm_lowp_quantize from
+    seeded normal activations and weights (the weights once, before timing;
+    the activations' quantization timed on its own).  Peaks: FP4 x FP4 the
+    dense FP4 matrix-core rate, a pair with an FP8 operand the FP8 rate, and
+    NVFP4 scales (decoded into the bf16 matrix cores) the bf16 rate."""
+    m, k, n = 2048, 4096, 14336
+    g = torch.Generator(device=dev)
+    g.manual_seed(61)
+    x = torch.randn(m, k, generator=g, device=dev).to(torch.bfloat16)
+    w = torch.randn(n, k, generator=g, device=dev).to(torch.bfloat16)
+    flop = 2.0 * m * n * k
+    res = {"workload": "scaled GEMM m=2048 k=4096 n=14336, codes quantized from seeded normal "
+                       "bf16 activations and weights, f32 output"}
+
+    def quantized(t, fmt, layout):
+        rows, cols = t.shape
+        codes = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
+        if layout == "tensor":
+            sc = torch.empty(1, dtype=torch.float32, device=dev)
+        else:
+            sc = torch.empty(rows, cols // (32 if layout == "mx" else 16), dtype=torch.uint8,
+                             device=dev)
+        qmm.qmm_lowp_quantize(t, codes, sc, rows, cols, fmt, layout, stream)
+        return codes, sc
+
+    out = torch.empty(m, n, dtype=torch.float32, device=dev)
+    for name, lf, rf, layout, peak in (("mxfp4_x_mxfp4", "e2m1", "e2m1", "mx", FP4_PEAK_TFLOPS),
+                                       ("mx_e4m3_x_e2m1", "e4m3", "e2m1", "mx", FP8_PEAK_TFLOPS),
+                                       ("mx_e4m3_x_e4m3", "e4m3", "e4m3", "mx", FP8_PEAK_TFLOPS),
+                                       ("tensor_e4m3_x_e4m3", "e4m3", "e4m3", "tensor",
+                                        FP8_PEAK_TFLOPS),
+                                       ("nvfp4_x_nvfp4", "e2m1", "e2m1", "nvfp4",
+                                        BF16_PEAK_TFLOPS)):
+        lc, ls = quantized(x, lf, layout)
+        rc, rs = quantized(w, rf, layout)
+
+        def run(_, lc=lc, ls=ls, rc=rc, rs=rs, lf=lf, rf=rf, layout=layout):
+            qmm.qmm_lowp_matmul(lc, rc, ls, rs, None, out, m, n, k, layout, lf, rf, stream)
+
+        for i in range(2):
+            run(i)
+        torch.cuda.synchronize()
+        ms = _time_launches(run, max(10, args.steps // 10), stream)
+        tflops = flop / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tflops, 2), "peak": peak,
+                     "frac": round(tflops / peak, 4)}
+        del lc, ls, rc, rs
+    codes = torch.empty(m, k, dtype=torch.uint8, device=dev)
+    sc = torch.empty(m, k // 32, dtype=torch.uint8, device=dev)
+
+    def runq(_):
+        qmm.qmm_lowp_quantize(x, codes, sc, m, k, "e2m1", "mx", stream)
+
+    for i in range(2):
+        runq(i)
+    torch.cuda.synchronize()
+    msq = _time_launches(runq, max(20, args.steps // 5), stream)
+    qbytes = m * k * 2 + m * k + m * (k // 32)
+    res["quantize_activations_mx_e2m1"] = {
+        "us": round(msq * 1e3, 3), "bytes": qbytes, "GBps": round(qbytes / (msq * 1e-3) / 1e9, 1),
+        "frac_hbm": round(qbytes / (msq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return res
 
 
