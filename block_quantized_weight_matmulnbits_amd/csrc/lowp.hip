@@ -372,12 +372,31 @@ __global__ __launch_bounds__(LTPB) void lowp_nvfp4_kernel(
     const float s = lowp_decode<0>(q);
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     uint32_t pk[8];
+    // Exact products: the upper halves of their binary32 values are bf16.
+    auto two = [&](int j, f32x2 v) {
+      pk[j / 2] = (__float_as_uint(v.x * s) >> 16) | (__float_as_uint(v.y * s) & 0xFFFF0000u);
+    };
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      // Exact products: the upper halves of their binary32 values are bf16.
-      const float v0 = lowp_decode<F>(w[j >> 2] >> (8 * (j & 3))) * s;
-      const float v1 = lowp_decode<F>(w[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) * s;
-      pk[j / 2] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
+    for (int i = 0; i < 4; ++i) {
+      // Codes 4 i .. 4 i + 3 as exact binary32 values: gfx950's conversions
+      // with a unit scale (FP8: two bytes of the word per instruction; FP4:
+      // the code pairs first packed into bytes 0 and 2), else bit decoding.
+      if constexpr (F == 0 || F == 1) {
+        const uint32_t x = w[i];
+        two(4 * i, F == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.0f, false)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(x, 1.0f, false));
+        two(4 * i + 2, F == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.0f, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(x, 1.0f, true));
+      } else if constexpr (F == 4) {
+        uint32_t x = w[i] & 0x0F0F0F0Fu;
+        x |= x >> 4;
+        two(4 * i, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0));
+        two(4 * i + 2, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2)
+          two(4 * i + j, f32x2{lowp_decode<F>(w[i] >> (8 * j)), lowp_decode<F>(w[i] >> (8 * (j + 1)))});
+      }
     }
     const int ks = lkk / 32, g0 = (lkk & 31) / 8;
     const int t = row >> 4, r = row & 15;
