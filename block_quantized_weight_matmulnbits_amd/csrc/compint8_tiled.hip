@@ -1,6 +1,7 @@
 // compint8_tiled.hip -- CompInt8 (accuracy_level 4) with the int8 matrix
 // cores of gfx950, on the tiled weight layout (qmm_layout.h) and, for M >= 2,
-// on the operator's layout.
+// on the operator's layout (there also 3-bit weights: their two bit planes
+// are merged into the 2-bit codes' plane order).
 //
 // Definition (onnx-runtime-ep-cpu matmul_nbits.rs: quantize_activation_signed,
 // int4_dot_row_scalar, int8_row): with qa / sa the int8 activations and their
@@ -49,6 +50,9 @@ struct CtGeom {
   static constexpr int CB = TKC * BITS / 8;     // bytes per column chunk
   static constexpr int LB = CB / 4;             // code bytes per lane per chunk (16 codes)
 };
+// 3-bit codes (operator layout only): a block of bs codes is bs / 4 bytes of
+// the 2-bit plane then bs / 8 of the 1-bit plane (blocks of 64 codes or
+// more: a chunk lies inside one block).
 
 // The lane's 16 codes as four words of int8, in plane order (see unpack).
 template <int BITS>
@@ -65,6 +69,18 @@ __device__ __forceinline__ i32x4 unpack_codes(const u32x4& raw) {
     const uint32_t w = raw.x;
     return i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+  } else if constexpr (BITS == 3) {
+    // Operator layout's two planes: raw.x = the 2-bit plane of the lane's 16
+    // codes (code j at bits 2j), raw.y = the 1-bit plane (bit j).  Planes as
+    // for 2-bit codes; bit 4j + i of the 1-bit plane goes to bit 2 of byte j
+    // of plane i.
+    const uint32_t w = raw.x, h = raw.y;
+    auto hi = [&](int i) {
+      const uint32_t t = h >> i;
+      return ((t & 1u) << 2) | ((t & 0x10u) << 6) | ((t & 0x100u) << 10) | ((t & 0x1000u) << 14);
+    };
+    return i32x4{(int)((w & 0x03030303u) | hi(0)), (int)(((w >> 2) & 0x03030303u) | hi(1)),
+                 (int)(((w >> 4) & 0x03030303u) | hi(2)), (int)(((w >> 6) & 0x03030303u) | hi(3))};
   } else {
     // 16 bytes in order, as code - 128.
     return i32x4{(int)(raw.x ^ 0x80808080u), (int)(raw.y ^ 0x80808080u),
@@ -77,7 +93,9 @@ __device__ __forceinline__ i32x4 unpack_codes(const u32x4& raw) {
 // pick bytes of lo, 4-7 bytes of hi.
 template <int BITS>
 __device__ __forceinline__ i32x4 permute_acts(const u32x4& a) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 3) {
+    return permute_acts<2>(a);
+  } else if constexpr (BITS == 4) {
     return i32x4{(int)__builtin_amdgcn_perm(a.y, a.x, 0x06040200u),
                  (int)__builtin_amdgcn_perm(a.y, a.x, 0x07050301u),
                  (int)__builtin_amdgcn_perm(a.w, a.z, 0x06040200u),
@@ -105,6 +123,7 @@ struct CtSlot {
   u32x4 code;
   u32x4 act;
   uint32_t sw, zw;
+  uint32_t sw2, zw2;   // HB: the chunk's second block
 };
 
 // STAGE: the workgroup first copies its Mp activation rows into LDS, padded
@@ -112,7 +131,11 @@ struct CtSlot {
 // banks, and its waves read them there (rows past Mp as zeros, by a select);
 // otherwise every wave loads its rows from memory with each chunk.  The CS
 // column slices of the workgroup share the staged rows.
-template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE, bool OPL>
+// HB: blocks of 32 codes, two per 64-code chunk: each chunk runs its MFMAs
+// twice, once with the activations of the second block zeroed (lane groups
+// 2 and 3) and once with those of the first (groups 0 and 1), and closes both
+// blocks; shares of K are whole pairs of blocks.
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE, bool OPL, bool HB>
 __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
@@ -161,10 +184,12 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
       (void*)zps, 0, HAS_ZP ? (OPL ? N * zp_row_bytes : groups * kb * TG * BITS / 8) : 0, RSRC3);
   // Blocks of this wave's share (whole blocks, so no block is split).
-  const int bps = (kb + S - 1) / S;
+  // HB: units are pairs of blocks (one chunk each).
+  const int units = HB ? (kb + 1) / 2 : kb;
+  const int bps = (units + S - 1) / S;
   const int b_lo = s * bps;
-  const int b_hi = has_slice ? min(kb, b_lo + bps) : b_lo;
-  const int cpb = 1 << log2_cpb;                    // chunks per block
+  const int b_hi = has_slice ? min(units, b_lo + bps) : b_lo;
+  const int cpb = HB ? 1 : 1 << log2_cpb;           // chunks per unit
   const int c_lo = b_lo * cpb;
   const int nch = max(0, (b_hi - b_lo) * cpb);
 
@@ -180,7 +205,17 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   const int lane_act = rowA * Kp + g * 16;
   auto issue = [&](CtSlot& sl, int j) {
     const int c = c_lo + j;
-    if constexpr (LB == 16)
+    if constexpr (BITS == 3) {
+      // The lane's 16 codes: 4 bytes of the 2-bit plane and 2 of the 1-bit
+      // plane of its block (columns past N: past the extent, zeros).
+      const int bs = HB ? 32 : TKC << log2_cpb;
+      const int base = n * row_bytes + (HB ? 2 * c + (g >> 1) : c >> log2_cpb) * (3 * bs / 8);
+      const int i0 = HB ? 16 * (g & 1) : (c & (cpb - 1)) * TKC + 16 * g;
+      sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, base + i0 / 4, 0, BUF_STREAM),
+                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rc, base + bs / 4 + i0 / 8, 0,
+                                                                      BUF_STREAM),
+                      0u, 0u};
+    } else if constexpr (LB == 16)
       sl.code = __builtin_amdgcn_raw_buffer_load_b128(rc, lane_code + c * code_step, 0, BUF_STREAM);
     else if constexpr (LB == 8) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane_code + c * code_step, 0, BUF_STREAM);
@@ -190,14 +225,36 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
                       0u, 0u, 0u};
     }
     if constexpr (!STAGE) sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);
-    const int b = c >> log2_cpb;
+    const int b = HB ? 2 * c : c >> log2_cpb;
     const int si = sc_base + b * sc_step;
     const int zbit = zb_base + b * zb_step;
-    if constexpr (OPL) {
+    if constexpr (HB) {
+      // The second block's scale and zero point (read, and used, only as a
+      // value at bit 0: a load of its own width at its own offset).
+      const int si2 = si + sc_step, zbit2 = zbit + zb_step;
+      if constexpr (SZ == 4) sl.sw2 = __builtin_amdgcn_raw_buffer_load_b32(rs, si2 * 4, 0, 0);
+      else sl.sw2 = __builtin_amdgcn_raw_buffer_load_b16(rs, si2 * 2, 0, 0);
+      if constexpr (HAS_ZP) {
+        sl.zw2 = __builtin_amdgcn_raw_buffer_load_b8(rz, zbit2 >> 3, 0, 0);
+        if constexpr (BITS == 3) sl.zw2 |= __builtin_amdgcn_raw_buffer_load_b8(rz, (zbit2 >> 3) + 1, 0, 0) << 8;
+      }
+      // The first block's, the same way.
+      if constexpr (SZ == 4) sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, si * 4, 0, 0);
+      else sl.sw = __builtin_amdgcn_raw_buffer_load_b16(rs, si * 2, 0, 0);
+      if constexpr (HAS_ZP) {
+        sl.zw = __builtin_amdgcn_raw_buffer_load_b8(rz, zbit >> 3, 0, 0);
+        if constexpr (BITS == 3) sl.zw |= __builtin_amdgcn_raw_buffer_load_b8(rz, (zbit >> 3) + 1, 0, 0) << 8;
+      }
+    } else if constexpr (OPL) {
       // The value itself (shifted back to bit 0 of the word on use).
       if constexpr (SZ == 4) sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, si * 4, 0, 0);
       else sl.sw = __builtin_amdgcn_raw_buffer_load_b16(rs, si * 2, 0, 0);
-      if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b8(rz, zbit >> 3, 0, 0);
+      if constexpr (HAS_ZP) {
+        sl.zw = __builtin_amdgcn_raw_buffer_load_b8(rz, zbit >> 3, 0, 0);
+        // A 3-bit zero point may continue into the next byte (past the
+        // zero-point rows: zero).
+        if constexpr (BITS == 3) sl.zw |= __builtin_amdgcn_raw_buffer_load_b8(rz, (zbit >> 3) + 1, 0, 0) << 8;
+      }
     } else {
       sl.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, (si * SZ) & ~3, 0, 0);
       if constexpr (HAS_ZP) sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, ((zbit) >> 5) * 4, 0, 0);
@@ -227,13 +284,50 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     const i32x4 bv = unpack_codes<BITS>(sl.code);
     u32x4 raw_act;
     if constexpr (STAGE) {
+      // (HB, odd kb: the last chunk's second half lies past the staged rows;
+      // its block is not closed, zeros stand in.)
+      const int koff = (c_lo + j) * TKC + g * 16;
+      const bool kok = !HB || koff < Kp;
       const u32x4 v = *reinterpret_cast<const u32x4*>(qs + min(rowA, Mp - 1) * qrow +
-                                                      (c_lo + j) * TKC + g * 16);
-      raw_act = rowA < Mp ? v : u32x4{0u, 0u, 0u, 0u};
+                                                      (kok ? koff : 0));
+      raw_act = (rowA < Mp && kok) ? v : u32x4{0u, 0u, 0u, 0u};
     } else
 
       raw_act = sl.act;
     const i32x4 av = permute_acts<BITS>(raw_act);
+    if constexpr (HB) {
+      // Both blocks of the chunk, each closed at once.
+      const i32x4 zero = {0, 0, 0, 0};
+      const i32x4 av0 = g < 2 ? av : zero, av1 = g < 2 ? zero : av;
+      const i32x4 d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av0, bv, zero, 0, 0, 0);
+      const i32x4 s0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av0, ones, zero, 0, 0, 0);
+      const i32x4 d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av1, bv, zero, 0, 0, 0);
+      const i32x4 s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av1, ones, zero, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = 2 * (c_lo + j) + h;
+        if (b >= kb) break;
+        const uint32_t sw = h ? sl.sw2 : sl.sw, zw = h ? sl.zw2 : sl.zw;
+        float sc;
+        if constexpr (SZ == 4) sc = __uint_as_float(sw);
+        else sc = bits16_to_f32<SDT>((uint16_t)sw);
+        int z = 1 << (BITS - 1);
+        if constexpr (HAS_ZP) z = (int)((zw >> ((zb_base + b * zb_step) & 7)) & m);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(saT + b * 16 + 4 * g);
+        const int zo = z - OFF;
+        const i32x4 dd = h ? d1 : d0, ss = h ? s1 : s0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = dd[e] - zo * ss[e];
+          if constexpr (DOTS) {
+            const int r = 4 * g + e;
+            if (r < Mp && n < N) dots[((int64_t)r * N + n) * kb + b] = d;
+          }
+          y[e] = fmaf((float)d, s4[e] * sc, y[e]);
+        }
+      }
+      return;
+    }
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
     asum = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones, asum, 0, 0, 0);
     if (((j + 1) & (cpb - 1)) == 0) {
@@ -304,7 +398,8 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
                                   a.zp != nullptr);
   const int chunks = (int)tg.chunks;             // kb * bs / 64 on either layout
-  const int log2_cpb = __builtin_ctz((unsigned)(a.block_size / TKC));
+  const bool hb = a.block_size == 32;
+  const int log2_cpb = hb ? 0 : __builtin_ctz((unsigned)(a.block_size / TKC));
   const int n_slices = (int)tg.groups * 2;
   const int Kp = (int)(a.kb * a.block_size);
   // Two slices (one group) per workgroup, shares of K until a workgroup has
@@ -314,11 +409,20 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   const int CS = wide ? 4 : 2;
   const int maxw = wide ? 16 : 8;
   int S = 1;
-  while (CS * S < maxw && (a.kb + 2 * S - 1) / (2 * S) >= 2) S *= 2;
+  const int64_t units = hb ? (a.kb + 1) / 2 : a.kb;
+  while (CS * S < maxw && (units + 2 * S - 1) / (2 * S) >= 2) S *= 2;
   const int rows = (int)std::min<int64_t>(16, a.M);
   const size_t lds = ct_lds(a.kb, Kp, CS, S, STAGE, rows);
-  auto kern = a.tiled ? compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, false>
-                      : compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true>;
+  decltype(&compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true, false>) kern;
+  if constexpr (BITS == 3)
+    kern = hb ? compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true, true>
+              : compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true, false>;
+  else if (a.tiled)
+    kern = hb ? compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, false, true>
+              : compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, false, false>;
+  else
+    kern = hb ? compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true, true>
+              : compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, STAGE, true, false>;
   if (lds > 64 * 1024) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)CT_STAGE_LDS_MAX);
     if (e != hipSuccess) return e;
@@ -332,7 +436,8 @@ hipError_t launch_t(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
                        a.B + (a.tiled ? tg.codes_off : 0), (const uint8_t*)a.scales, a.zp,
                        (const YT*)a.bias, DOTS ? nullptr : (YT*)a.Y + m0 * a.N,
                        DOTS ? dots + m0 * a.N * a.kb : nullptr, Mp, (int)a.N, (int)a.kb, Kp,
-                       chunks, log2_cpb, n_slices, CS, S, (int)(a.kb * a.blob),
+                       chunks, log2_cpb, n_slices, CS, S,
+                       (int)(BITS == 3 ? a.kb * (3 * a.block_size / 8) : a.kb * a.blob),
                        (int)a.zp_row_bytes);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -380,6 +485,7 @@ template <bool DOTS>
 hipError_t launch_b(const MatArgs& a, const int8_t* qa, const float* sa, int32_t* dots) {
   switch (a.bits) {
     case 2: return launch_s<2, DOTS>(a, qa, sa, dots);
+    case 3: return launch_s<3, DOTS>(a, qa, sa, dots);
     case 4: return launch_s<4, DOTS>(a, qa, sa, dots);
     default: return launch_s<8, DOTS>(a, qa, sa, dots);
   }
@@ -393,12 +499,25 @@ bool compint8_tiled_supported(const MatArgs& a) {
   // zero-point rows of N + 32 columns, the slices' padding).
   const TiledGeom tg = tiled_geom(a.K, a.N, a.block_size, a.bits, a.s_dtype == DT_F32 ? 4 : 2,
                                   a.zp != nullptr);
+  const int64_t row_bytes = a.bits == 3 ? a.kb * (3 * a.block_size / 8) : a.kb * a.blob;
+  if (a.bits == 3 && a.tiled) return false;      // 3-bit weights: operator layout only
   const bool fits = a.tiled ? tg.total < 0x7FFFFF00LL
-                            : (a.N + 32) * a.kb * a.blob < 0x7FFFFF00LL &&
+                            : (a.N + 32) * row_bytes < 0x7FFFFF00LL &&
                                   (a.N + 32) * a.kb * 4 < 0x7FFFFF00LL &&
                                   (a.N + 32) * a.zp_row_bytes * 8 < 0x7FFFFF00LL;
-  return a.bits != 3 && a.block_size >= TKC && (a.kb * 16 + 8 * 256) * 4 <= 64 * 1024 && fits &&
+  return a.block_size >= 32 && (a.kb * 16 + 8 * 256) * 4 <= 64 * 1024 && fits &&
          16 * a.kb * a.block_size < 0x7FFFFF00LL;
+}
+
+bool compint8_tiled_preferred(const MatArgs& a) {
+  // On the operator's layout the other kernels win at few rows where this one
+  // reads more per code: blocks of 32 (two blocks per chunk: twice the MFMAs
+  // and scale loads) and 3-bit weights (two planes) -- measured at K 4096,
+  // N 14336: 4-bit bs 32, M = 4 / 8: 36.8 / 37.4 us here against 22.3 / 63.4
+  // on compint8_kernel; 3-bit: 53.9 / 54.4 against 40.4 / 78.2 on the
+  // generic kernel.
+  if (a.M < 2 || !compint8_tiled_supported(a)) return false;
+  return a.M >= 8 || (a.block_size >= TKC && a.bits != 3);
 }
 
 hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa) {

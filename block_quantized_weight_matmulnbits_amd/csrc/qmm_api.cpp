@@ -256,7 +256,8 @@ int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t
   const bool small = M > 0 && compint8_small_supported(a);
   if (a.tiled && !small && !compint8_tiled_supported(a))
     return fail(QMM_ERR_UNSUPPORTED, "%s: on the tiled layout CompInt8 needs "
-                "block_size >= 64 (whole 64-code chunks per block) and at most 896 blocks per "
+                "block_size >= 32 (64-code chunks holding one block, or two of 32) and at most 896 "
+                "blocks per "
                 "row, or M = 1 with a block of at least one 16-byte unit of codes and at most "
                 "1024 codes (got M=%lld, block_size=%d, %lld blocks). How to fix: pass the "
                 "operator's layout (QMM_LAYOUT_ORT) for this weight.", fn, (long long)M,
@@ -276,8 +277,10 @@ int gemm_compint8_impl(const char* fn, const void* A, int a_dtype, const uint8_t
   float* sa = (float*)((char*)workspace + ws_qa_bytes(a.M, a.kb, a.block_size));
   hipError_t e = launch_quantize_a(a, qa, sa);
   if (e == hipSuccess) {
-    if (a.bits == 3) e = launch_generic_int(a, qa, 1, sa, nullptr);
-    else if (a.tiled || (a.M >= 2 && compint8_tiled_supported(a))) e = launch_compint8_tiled(a, qa, sa);
+    // The int8 matrix cores where they are faster (compint8_tiled_preferred);
+    // else 3-bit weights on the generic kernel, the rest on compint8_kernel.
+    if (a.tiled || compint8_tiled_preferred(a)) e = launch_compint8_tiled(a, qa, sa);
+    else if (a.bits == 3) e = launch_generic_int(a, qa, 1, sa, nullptr);
     else e = launch_compint8(a, qa, sa);
   }
   return hip_status(e, fn);
@@ -657,7 +660,7 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
   const bool small = M > 0 && qmm::compint8_small_supported(a);
   if (a.tiled && !small && !qmm::compint8_tiled_supported(a))
     return fail(QMM_ERR_UNSUPPORTED, "qmm_debug_compint8_block_dots: on the tiled layout "
-                "CompInt8 needs block_size >= 64, or M = 1 with a block of at least one 16-byte "
+                "CompInt8 needs block_size >= 32, or M = 1 with a block of at least one 16-byte "
                 "unit of codes. How to fix: pass the operator's layout.");
   if (M == 0) return QMM_OK;
   st = check_workspace("qmm_debug_compint8_block_dots", a, workspace, workspace_bytes);
@@ -676,9 +679,9 @@ int qmm_debug_compint8_block_dots(const void* A, int a_dtype, const uint8_t* B, 
   }
   if (e == hipSuccess) e = qmm::launch_quantize_a(a, qa, sa);
   if (e == hipSuccess) {
-    if (a.bits == 3) e = qmm::launch_generic_int(a, qa, 1, sa, dots);
-    else if (a.tiled || (a.M >= 2 && qmm::compint8_tiled_supported(a)))
+    if (a.tiled || qmm::compint8_tiled_preferred(a))
       e = qmm::launch_compint8_tiled_dots(a, qa, sa, dots);
+    else if (a.bits == 3) e = qmm::launch_generic_int(a, qa, 1, sa, dots);
     else e = qmm::launch_compint8_dots(a, qa, sa, dots);
   }
   return hip_status(e, "qmm_debug_compint8_block_dots");

@@ -67,6 +67,8 @@ hipError_t launch_compint8_small(const MatArgs& a);
 hipError_t launch_compint8_small_dots(const MatArgs& a, int8_t* qa, float* sa, int32_t* dots);
 // CompInt8 on the tiled layout with int8 MFMA (compint8_tiled.hip).
 bool compint8_tiled_supported(const MatArgs& a);
+// Whether M >= 2 on the operator's layout takes compint8_tiled (faster there).
+bool compint8_tiled_preferred(const MatArgs& a);
 hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa);
 hipError_t launch_compint8_tiled_dots(const MatArgs& a, const int8_t* qa, const float* sa,
                                       int32_t* dots);

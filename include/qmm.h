@@ -142,7 +142,7 @@ int qmm_gemm(const void *A, int a_dtype, const uint8_t *B, int b_layout,
  * the tiled layout the quantization runs inside the one launch and the
  * workspace is checked but not written).
  * accuracy_level must be 4.  Arguments otherwise as for qmm_gemm.  B may be
- * the tiled buffer of qmm_repack when block_size >= 64 (the block dots then
+ * the tiled buffer of qmm_repack when block_size >= 32 (the block dots then
  * run on the int8 matrix cores), and for M = 1 also when block_size is at
  * least one 16-byte unit of codes (32, 64 or 16 codes for 4, 2 or 8 bits)
  * and at most 1024; otherwise QMM_ERR_UNSUPPORTED.

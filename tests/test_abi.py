@@ -155,9 +155,9 @@ def test_repack_rejects_bad_arguments(qmm):
 
 
 def test_compint8_tiled_layout_needs_whole_chunks_per_block(qmm):
-    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, 0, None, FAKE, 4, 4096, 4096, 32,
+    st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, 0, None, FAKE, 4, 4096, 4096, 16,
                                    4, 4, FAKE, 1 << 30, None)
-    assert st == -2 and "block_size >= 64" in qmm.qmm_last_error()
+    assert st == -2 and "block_size >= 32" in qmm.qmm_last_error()
     # M = 1 takes blocks down to one 16-byte unit of codes (32 codes at 4
     # bits); 16 is shorter, so it is rejected on the host as well.
     st = qmm.lib.qmm_gemm_compint8(FAKE, 2, FAKE, 1, None, 2, None, None, 0, None, FAKE, 1, 4096, 4096, 16,

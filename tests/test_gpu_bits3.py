@@ -177,3 +177,31 @@ def test_repack_and_group_indices_are_rejected():
         q.qmm_gemv(case.A.reshape(-1), case.B, case.scales, case.zero_points, None, Y, 256, 64,
                    32, 3, g_idx=g)
     assert err.value.status == q.QMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("bs", [64, 128, 256])
+def test_compint8_matrix_core_route_dots_exact(bs):
+    """From M = 8 (M = 6 takes the generic kernel): the int8 matrix-core
+    kernel with the two planes merged; its int32 block dots equal the
+    oracle's bit for bit, with and without zero points (zero points
+    straddling bytes), M past one 16-row pass."""
+    for i, (M, K, N) in enumerate([(16, 4096, 300), (6, 2048, 200), (33, 1024, 70)]):
+        case = case_of(M, K, N, bs, a_dtype="bf16", has_zp=(i != 1), has_bias=True,
+                       seed=7000 + bs + i)
+        print(f"[bits3 compint8 mfma] M={M} K={K} N={N} bs={bs}", flush=True)
+        c = case.to(DEV)
+        kb = case.k_blocks
+        qa, sa = oracle.quantize_a(case.A.float().numpy().reshape(M, K), K, bs)
+        dots = torch.empty(M, N, kb, dtype=torch.int32, device=DEV)
+        qmm().qmm_debug_compint8_block_dots(c.A, c.B, c.zero_points, M, K, N, bs, 3, dots,
+                                            ws_compint8(M, K, bs))
+        torch.cuda.synchronize()
+        assert np.array_equal(dots.cpu().numpy(), oracle.compint8_block_dots(
+            qa, u8(case.B), u8(case.zero_points), N, K, bs, 3))
+        Y, S = oracle.compint8_matmul(qa, sa, u8(case.B), f64(case.scales), u8(case.zero_points),
+                                      f64(case.bias), N, K, bs, 3)
+        y = torch.empty(M, N, dtype=c.A.dtype, device=DEV)
+        qmm().qmm_gemm_compint8(c.A, c.B, c.scales, c.zero_points, c.bias, y, M, K, N, bs, 3,
+                                ws_compint8(M, K, bs))
+        torch.cuda.synchronize()
+        assert_within(y, Y, S, TOL[c.A.dtype], "bits3 compint8 mfma")

@@ -119,7 +119,7 @@ def check_all(case, what, strict=False):
     assert np.array_equal(gsa, sa), f"{what}: activation scales differ"
     assert np.array_equal(gqa, qa), f"{what}: int8 activations differ"
     tiled = LAYOUT["v"] == "tiled"
-    mfma_ok = not tiled or case.block_size >= 64
+    mfma_ok = not tiled or case.block_size >= 32
     small_ok = small_route(case)
     if mfma_ok or small_ok:
         dots = oracle.compint8_block_dots(qa, u8(case.B), u8(case.zero_points), case.N, case.K,
@@ -219,3 +219,40 @@ def test_deterministic():
     from block_quantized_weight_matmulnbits_amd.workloads import compint8_case
     case = compint8_case(4, 4, 128, False)
     assert torch.equal(gpu_matmul(case), gpu_matmul(case))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_block32_matrix_core_route_dots_exact(bits):
+    """Blocks of 32 codes: the int8 matrix-core kernel closes two blocks per
+    64-code chunk (on the operator's layout from M = 8, on the tiled layout
+    from M = 2; M = 5 on the operator's layout takes the other kernels); the
+    int32 block dots equal the oracle's bit for bit (odd kb included) and the
+    output is within tolerance."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    for i, (M, K, N) in enumerate([(16, 4096, 300), (5, 1056, 130), (20, 352, 64)]):
+        case = make_matmul_case(M, K, N, 32, bits, a_dtype="bf16", has_zp=(i != 1),
+                                has_bias=True, seed=900 + 10 * bits + i)
+        print(f"[compint8 bs32] bits={bits} M={M} K={K} N={N}", flush=True)
+        c = case.to(DEV)
+        kb = case.k_blocks
+        qa, sa = oracle.quantize_a(case.A.float().numpy().reshape(M, K), K, 32)
+        ws = torch.empty(qmm().qmm_compint8_workspace_size(M, K, 32), dtype=torch.uint8,
+                         device=DEV)
+        dots = torch.empty(M, N, kb, dtype=torch.int32, device=DEV)
+        qmm().qmm_debug_compint8_block_dots(c.A, c.B, c.zero_points, M, K, N, 32, bits, dots, ws)
+        torch.cuda.synchronize()
+        want = oracle.compint8_block_dots(qa, u8(case.B), u8(case.zero_points), N, K, 32, bits)
+        assert np.array_equal(dots.cpu().numpy(), want), (M, K, N)
+        Y, S = oracle.compint8_matmul(qa, sa, u8(case.B), f64(case.scales), u8(case.zero_points),
+                                      f64(case.bias), N, K, 32, bits)
+        y = torch.empty(M, N, dtype=c.A.dtype, device=DEV)
+        qmm().qmm_gemm_compint8(c.A, c.B, c.scales, c.zero_points, c.bias, y, M, K, N, 32, bits,
+                                ws)
+        torch.cuda.synchronize()
+        assert_within(y, Y, S, TOL[c.A.dtype], "compint8 bs32")
+        if bits != 3:
+            t = qmm().qmm_repack(c.B, c.scales, c.zero_points, K, N, 32, bits)
+            yt = torch.empty_like(y)
+            qmm().qmm_gemm_compint8(c.A, t, None, None, c.bias, yt, M, K, N, 32, bits, ws)
+            torch.cuda.synchronize()
+            assert_within(yt, Y, S, TOL[c.A.dtype], "compint8 bs32 tiled")
