@@ -36,6 +36,7 @@
 #include "qmm_layout.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace qmm {
 
@@ -124,6 +125,7 @@ struct CtSlot {
   u32x4 act;
   uint32_t sw, zw;
   uint32_t sw2, zw2;   // HB: the chunk's second block
+  u32x4 act2;          // AB = 2: the lane's activations 8..15
 };
 
 // STAGE: the workgroup first copies its Mp activation rows into LDS, padded
@@ -135,7 +137,13 @@ struct CtSlot {
 // twice, once with the activations of the second block zeroed (lane groups
 // 2 and 3) and once with those of the first (groups 0 and 1), and closes both
 // blocks; shares of K are whole pairs of blocks.
-template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE, bool OPL, bool HB>
+// AB = 2: int16 activations (the int16 route, operator layout, unstaged):
+// a = 256 ah + (al - 128) + 128 with ah = a >> 8 and al - 128 = (a & 255) ^
+// 128 both int8, so sum a (c - zp) = 256 sum ah (c - zp) + sum (al - 128)
+// (c - zp) + 128 sum (c - zp): two activation planes through the MFMAs, and
+// the codes' sum per block by one more MFMA against all-ones activations.
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS, bool STAGE, bool OPL, bool HB,
+          int AB = 1>
 __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zps,
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)codes, 0, OPL ? N * row_bytes : groups * chunks * TG * CB, RSRC3);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)qa, 0, Mp * Kp, RSRC3);
+      (void*)qa, 0, Mp * Kp * AB, RSRC3);
   // No scales (the block-dot export on the operator layout): every scale
   // load is out of range and reads zero.
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   const int sc_base = OPL ? n * kb : grp * kb * TG + col, sc_step = OPL ? 1 : TG;
   const int zb_base = OPL ? n * zp_row_bytes * 8 : (grp * kb * TG + col) * BITS;
   const int zb_step = OPL ? BITS : TG * BITS;
-  const int lane_act = rowA * Kp + g * 16;
+  const int lane_act = (rowA * Kp + g * 16) * AB;
   auto issue = [&](CtSlot& sl, int j) {
     const int c = c_lo + j;
     if constexpr (BITS == 3) {
@@ -224,7 +232,8 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
       sl.code = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rc, lane_code + c * code_step, 0, BUF_STREAM),
                       0u, 0u, 0u};
     }
-    if constexpr (!STAGE) sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC, 0, 0);
+    if constexpr (!STAGE) sl.act = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC * AB, 0, 0);
+    if constexpr (AB == 2) sl.act2 = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_act + c * TKC * 2 + 16, 0, 0);
     const int b = HB ? 2 * c : c >> log2_cpb;
     const int si = sc_base + b * sc_step;
     const int zbit = zb_base + b * zb_step;
@@ -279,6 +288,7 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
   const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
   f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
   i32x4 acc = {0, 0, 0, 0}, asum = {0, 0, 0, 0};
+  i32x4 acc2 = {0, 0, 0, 0}, asum2 = {0, 0, 0, 0}, csum = {0, 0, 0, 0};   // AB = 2
   // Chunk j: two MFMAs; at the block's last chunk the epilogue scales it.
   auto consume = [&](const CtSlot& sl, int j) {
     const i32x4 bv = unpack_codes<BITS>(sl.code);
@@ -294,6 +304,67 @@ __global__ __launch_bounds__(CT_MAXW * 64) void compint8_tiled_kernel(
     } else
 
       raw_act = sl.act;
+    if constexpr (AB == 2) {
+      // The two int8 planes of the lane's 16 int16 activations (natural
+      // order), then the codes' plane order.
+      const uint32_t d[8] = {sl.act.x, sl.act.y, sl.act.z, sl.act.w,
+                             sl.act2.x, sl.act2.y, sl.act2.z, sl.act2.w};
+      u32x4 hi, lo;
+      hi.x = __builtin_amdgcn_perm(d[1], d[0], 0x07050301u); lo.x = __builtin_amdgcn_perm(d[1], d[0], 0x06040200u);
+      hi.y = __builtin_amdgcn_perm(d[3], d[2], 0x07050301u); lo.y = __builtin_amdgcn_perm(d[3], d[2], 0x06040200u);
+      hi.z = __builtin_amdgcn_perm(d[5], d[4], 0x07050301u); lo.z = __builtin_amdgcn_perm(d[5], d[4], 0x06040200u);
+      hi.w = __builtin_amdgcn_perm(d[7], d[6], 0x07050301u); lo.w = __builtin_amdgcn_perm(d[7], d[6], 0x06040200u);
+      lo ^= 0x80808080u;
+      const i32x4 ah = permute_acts<BITS>(hi), al = permute_acts<BITS>(lo);
+      const i32x4 zero = {0, 0, 0, 0};
+      // Per half (HB: the chunk's two blocks; else one pass over the chunk).
+#pragma unroll
+      for (int h = 0; h < (HB ? 2 : 1); ++h) {
+        const bool live = !HB || (h == 0 ? g < 2 : g >= 2);
+        const i32x4 ahh = live ? ah : zero, alh = live ? al : zero, onh = live ? ones : zero;
+        i32x4 t_h = HB ? zero : acc, s_h = HB ? zero : asum;
+        i32x4 t_l = HB ? zero : acc2, s_l = HB ? zero : asum2, cs = HB ? zero : csum;
+        t_h = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahh, bv, t_h, 0, 0, 0);
+        s_h = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahh, ones, s_h, 0, 0, 0);
+        t_l = __builtin_amdgcn_mfma_i32_16x16x64_i8(alh, bv, t_l, 0, 0, 0);
+        s_l = __builtin_amdgcn_mfma_i32_16x16x64_i8(alh, ones, s_l, 0, 0, 0);
+        cs = __builtin_amdgcn_mfma_i32_16x16x64_i8(onh, bv, cs, 0, 0, 0);
+        const bool close = HB || ((j + 1) & (cpb - 1)) == 0;
+        if (!HB && !close) {
+          acc = t_h; asum = s_h; acc2 = t_l; asum2 = s_l; csum = cs;
+          continue;
+        }
+        const int b = HB ? 2 * (c_lo + j) + h : b_lo + (j >> log2_cpb);
+        if (b >= kb) break;
+        const uint32_t sw = (HB && h) ? sl.sw2 : sl.sw, zw = (HB && h) ? sl.zw2 : sl.zw;
+        const int si = sc_base + b * sc_step;
+        const int zbit = zb_base + b * zb_step;
+        float sc;
+        if constexpr (SZ == 4) sc = __uint_as_float(sw);
+        else sc = bits16_to_f32<SDT>((uint16_t)(OPL || HB ? sw : sw >> ((si & 1) * 16)));
+        int z = 1 << (BITS - 1);
+        if constexpr (HAS_ZP) z = (int)((zw >> (zbit & (OPL || HB ? 7 : 31))) & m);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(saT + b * 16 + 4 * g);
+        const int zo = z - OFF;
+        const int kcount = HB ? 32 : TKC * cpb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // Modular int32 arithmetic; the exact block dot fits (|dot| <
+          // 2^31 for blocks of at most 128 codes).
+          const int d = 256 * (t_h[e] - zo * s_h[e]) + (t_l[e] - zo * s_l[e]) +
+                        128 * (cs[e] - zo * kcount);
+          if constexpr (DOTS) {
+            const int r = 4 * g + e;
+            if (r < Mp && n < N) dots[((int64_t)r * N + n) * kb + b] = d;
+          }
+          y[e] = fmaf((float)d, s4[e] * sc, y[e]);
+        }
+        if constexpr (!HB) {
+          acc = zero; asum = zero; acc2 = zero; asum2 = zero; csum = zero;
+        }
+      }
+      return;
+    }
     const i32x4 av = permute_acts<BITS>(raw_act);
     if constexpr (HB) {
       // Both blocks of the chunk, each closed at once.
@@ -491,7 +562,84 @@ hipError_t launch_b(const MatArgs& a, const int8_t* qa, const float* sa, int32_t
   }
 }
 
+// int16 activations (AB = 2): operator layout, unstaged.
+template <int BITS, int SDT, int YDT, bool HAS_ZP, bool DOTS>
+hipError_t launch_i16_t(const MatArgs& a, const int16_t* qa, const float* sa, int32_t* dots) {
+  const bool hb = a.block_size == 32;
+  const int log2_cpb = hb ? 0 : __builtin_ctz((unsigned)(a.block_size / TKC));
+  const int chunks = (int)((a.kb * a.block_size + TKC - 1) / TKC);
+  const int n_slices = (int)((a.N + TG - 1) / TG) * 2;
+  const int Kp = (int)(a.kb * a.block_size);
+  const int CS = 2;
+  const int64_t units = hb ? (a.kb + 1) / 2 : a.kb;
+  int S = 1;
+  while (CS * S < 8 && (units + 2 * S - 1) / (2 * S) >= 2) S *= 2;
+  const size_t lds = ct_lds(a.kb, Kp, CS, S, false, 0);
+  auto kern = hb ? compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, false, true, true, 2>
+                 : compint8_tiled_kernel<BITS, SDT, YDT, HAS_ZP, DOTS, false, true, false, 2>;
+  const int grid = (n_slices + CS - 1) / CS;
+  using YT = typename dt<YDT>::T;
+  const int row_bytes = (int)(BITS == 3 ? a.kb * (3 * a.block_size / 8) : a.kb * a.blob);
+  for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+    const int Mp = (int)std::min<int64_t>(16, a.M - m0);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(CS * S * 64), lds, a.stream,
+                       (const int8_t*)(qa + m0 * Kp), sa + m0 * a.kb, a.B,
+                       (const uint8_t*)a.scales, a.zp, (const YT*)a.bias,
+                       DOTS ? nullptr : (YT*)a.Y + m0 * a.N,
+                       DOTS ? dots + m0 * a.N * a.kb : nullptr, Mp, (int)a.N, (int)a.kb, Kp,
+                       chunks, log2_cpb, n_slices, CS, S, row_bytes, (int)a.zp_row_bytes);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int BITS, int SDT, bool DOTS>
+hipError_t launch_i16_s(const MatArgs& a, const int16_t* qa, const float* sa, int32_t* dots) {
+  auto y = [&](auto ydt) {
+    constexpr int YDT = decltype(ydt)::value;
+    return a.zp ? launch_i16_t<BITS, SDT, YDT, true, DOTS>(a, qa, sa, dots)
+                : launch_i16_t<BITS, SDT, YDT, false, DOTS>(a, qa, sa, dots);
+  };
+  switch (a.a_dtype) {
+    case DT_F32: return y(std::integral_constant<int, DT_F32>{});
+    case DT_F16: return y(std::integral_constant<int, DT_F16>{});
+    default: return y(std::integral_constant<int, DT_BF16>{});
+  }
+}
+
+template <int BITS, bool DOTS>
+hipError_t launch_i16_b(const MatArgs& a, const int16_t* qa, const float* sa, int32_t* dots) {
+  switch (a.s_dtype) {
+    case DT_F32: return launch_i16_s<BITS, DT_F32, DOTS>(a, qa, sa, dots);
+    case DT_F16: return launch_i16_s<BITS, DT_F16, DOTS>(a, qa, sa, dots);
+    default: return launch_i16_s<BITS, DT_BF16, DOTS>(a, qa, sa, dots);
+  }
+}
+
+template <bool DOTS>
+hipError_t launch_i16(const MatArgs& a, const int16_t* qa, const float* sa, int32_t* dots) {
+  switch (a.bits) {
+    case 2: return launch_i16_b<2, DOTS>(a, qa, sa, dots);
+    case 3: return launch_i16_b<3, DOTS>(a, qa, sa, dots);
+    case 4: return launch_i16_b<4, DOTS>(a, qa, sa, dots);
+    default: return launch_i16_b<8, DOTS>(a, qa, sa, dots);
+  }
+}
+
 }  // namespace
+
+bool int16_tiled_preferred(const MatArgs& a) {
+  // From M = 8 on the operator's layout, blocks of at most 128 codes (the
+  // int32 block dot of int16 activations).
+  return !a.tiled && a.M >= 8 && a.block_size <= 128 && compint8_tiled_supported(a) &&
+         32 * a.kb * a.block_size < 0x7FFFFF00LL;
+}
+
+hipError_t launch_int16_tiled(const MatArgs& a, const int16_t* qa, const float* sa,
+                              int32_t* dots) {
+  return dots ? launch_i16<true>(a, qa, sa, dots) : launch_i16<false>(a, qa, sa, nullptr);
+}
 
 bool compint8_tiled_supported(const MatArgs& a) {
   // Whole blocks of 64-code chunks; LDS for the activation scales; 32-bit

@@ -393,7 +393,12 @@ static int int16_impl(const char* fn, const void* A, int a_dtype, const uint8_t*
   hipError_t e = hipSuccess;
   if (dots) e = hipMemsetAsync(dots, 0, (size_t)(a.M * a.N * a.kb) * sizeof(int32_t), a.stream);
   if (e == hipSuccess) e = qmm::launch_quantize_a16(a, qa, sa);
-  if (e == hipSuccess) e = qmm::launch_generic_int(a, qa, 2, sa, dots);
+  if (e == hipSuccess) {
+    // From M = 8 the int8 matrix cores with the activations split into two
+    // int8 planes; else the generic kernel.
+    e = qmm::int16_tiled_preferred(a) ? qmm::launch_int16_tiled(a, qa, sa, dots)
+                                      : qmm::launch_generic_int(a, qa, 2, sa, dots);
+  }
   return hip_status(e, fn);
 }
 

@@ -69,6 +69,9 @@ hipError_t launch_compint8_small_dots(const MatArgs& a, int8_t* qa, float* sa, i
 bool compint8_tiled_supported(const MatArgs& a);
 // Whether M >= 2 on the operator's layout takes compint8_tiled (faster there).
 bool compint8_tiled_preferred(const MatArgs& a);
+// int16 activations on the int8 matrix cores (two activation planes).
+bool int16_tiled_preferred(const MatArgs& a);
+hipError_t launch_int16_tiled(const MatArgs& a, const int16_t* qa, const float* sa, int32_t* dots);
 hipError_t launch_compint8_tiled(const MatArgs& a, const int8_t* qa, const float* sa);
 hipError_t launch_compint8_tiled_dots(const MatArgs& a, const int8_t* qa, const float* sa,
                                       int32_t* dots);

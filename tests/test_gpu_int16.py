@@ -101,3 +101,17 @@ def test_decode_projection_full_size():
     case = make_matmul_case(1, 4096, 14336, 32, 8, a_dtype="bf16", has_zp=True, seed=41)
     r = check(case, strict=True)
     print(f"  max |err|/S = {r:.3e}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_matrix_core_route(bits, bs):
+    """From M = 8 the int16 activations run on the int8 matrix cores as two
+    int8 planes (a = 256 (a >> 8) + ((a & 255) ^ 128) - 128 + 128): the int32
+    block dots equal the oracle's bit for bit, over one and two 16-row
+    passes, blocks of 32 (two per 64-code chunk) included."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    for i, (M, K, N) in enumerate([(16, 4096, 300), (20, 1000, 70)]):
+        case = make_matmul_case(M, K, N, bs, bits, a_dtype="bf16", has_zp=(i == 0),
+                                has_bias=True, seed=6500 + 10 * bits + bs + i)
+        check(case)
