@@ -16,12 +16,30 @@
 // reads in bounds) in LDS; the lanes of a wave walk the chunk's 32-bit words
 // of codes of each of its columns (adjacent lanes, adjacent words), look up
 // each code's scale and zero point in the column's rows (cached reads) and
-// accumulate.  Used for every M with f32 activations and for M <= 16
-// otherwise; larger M with 16-bit activations runs the matrix-core GEMM
-// with the same lookups (gemm.hip).
+// accumulate.  Used for M >= 2 with f32 activations and for M <= 16
+// otherwise when the matrix-core GEMM's table does not fit; larger M with
+// 16-bit activations runs the matrix-core GEMM with the same lookups
+// (gemm.hip, gidx_mfma.hip).
+//
+// gidx_gemv_kernel (M = 1, any activation dtype): a workgroup of W waves
+// owns CW = 16 R output columns and cuts K into 4 W slices; lane l of wave w
+// takes columns (l % 16) + 16 r and slice 4 w + l / 16.  A row of codes is
+// read in 16-byte units (128 / BITS codes each): chunk ch holds 64 codes of
+// every slice, slice s taking units s, s + 4 W, ... of the chunk (each load
+// of a wave covers 64 contiguous bytes of 16 columns, through one buffer
+// resource for the workgroup's rows).  Before the K loop the workgroup
+// builds in LDS the table of its columns' {scale, zp * scale} in fp32 for
+// every group (entry (g, c) at g (CW + 1) + c), and per chunk it stages the
+// chunk's activations (fp32) and group indices (clamped into 0..kb-1, stored
+// as byte offsets of table rows) in a double buffer, loaded one chunk ahead
+// like the codes.  The 16 lanes of a quarter wave work on the same code
+// position, so they read one table row's adjacent entries.  Per code: one
+// address add, one 8-byte table read per column, fma(q, scale, -zp * scale)
+// (the exact dequantized value for 16-bit scales) and the fma into the
+// column's accumulator; the slices are summed at the end in a fixed order.
 #include <algorithm>
 
-#include "qmm_device.h"
+#include "mfma_ops.h"
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -100,12 +118,206 @@ __global__ __launch_bounds__(256) void gidx_rows_kernel(
     }
 }
 
+constexpr int GV_SLICE = 64;                // codes of a row per slice and chunk
+constexpr int64_t GV_LDS_MAX = 96 * 1024;
+
+// LDS of gidx_gemv_kernel: two staging buffers of a chunk (activation and
+// table offset per position), then the table.
+int64_t gidx_gemv_lds(int64_t kb, int R, int W) {
+  return (int64_t)2 * (4 * W * GV_SLICE) * 8 + (kb + 1) * (16 * R + 1) * 8;
+}
+
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int W, int PF>
+__global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
+    const typename dt<XDT>::T* __restrict__ A, const uint8_t* __restrict__ B,
+    const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
+    const int32_t* __restrict__ g_idx, const typename dt<XDT>::T* __restrict__ bias,
+    typename dt<XDT>::T* __restrict__ Y, int K, int N, int kb, int row_bytes, int zp_row_bytes,
+    int chunks) {
+  constexpr int CW = 16 * R, TS = CW + 1;
+  constexpr int T = 64 * W;                     // threads
+  constexpr int CH = 4 * W * GV_SLICE;          // codes of a row per chunk
+  constexpr int P = 128 / BITS;                 // codes per 16-byte unit
+  constexpr int UPC = GV_SLICE / P;             // units per slice per chunk
+  constexpr int WPU = 32 / BITS;                // codes per 32-bit word
+  static_assert(CH == 4 * T, "each thread stages 4 positions of a chunk");
+  extern __shared__ __align__(16) unsigned char gv_smem[];
+  float* xs = reinterpret_cast<float*>(gv_smem);                     // [2][CH]
+  int* gs = reinterpret_cast<int*>(gv_smem + 2 * CH * 4);            // [2][CH]
+  f32x2* tab = reinterpret_cast<f32x2*>(gv_smem + 2 * CH * 8);       // [kb + 1][TS]
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c = lane & 15, s = wave * 4 + (lane >> 4);
+  const int col0 = blockIdx.x * CW;
+
+  // One resource for the workgroup's rows (a buffer resource must be the
+  // same in every lane); a lane's column is a byte offset into it.
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + (int64_t)col0 * row_bytes), 0, min(CW, N - col0) * row_bytes, BUF_WORD3);
+  // Codes of chunks ch .. ch + PF (slot 0: the chunk being computed).
+  u32x4 cd[PF + 1][R][UPC];
+  auto load_codes = [&](int ch, u32x4 (&dst)[R][UPC]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < UPC; ++i)
+        dst[r][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, (c + 16 * r) * row_bytes + ((ch * UPC + i) * 4 * W + s) * 16, 0, BUF_STREAM);
+  };
+  float xv[4];
+  int gv[4];
+  // Loads are unconditional (of an element in bounds) and selected after,
+  // so that they are issued together; positions past K stage zeros.
+  auto stage_load = [&](int ch) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = ch * CH + t * 4 + j;
+      const int kk = min(k, K - 1);
+      const float x = dt<XDT>::to_f32(A[kk]);
+      const int g = min(max(g_idx[kk], 0), kb - 1);
+      xv[j] = k < K ? x : 0.0f;
+      gv[j] = k < K ? g * (TS * 8) : 0;
+    }
+  };
+  auto stage_store = [&](int buf) {
+    *reinterpret_cast<f32x4*>(xs + buf * CH + t * 4) = f32x4{xv[0], xv[1], xv[2], xv[3]};
+    *reinterpret_cast<i32x4*>(gs + buf * CH + t * 4) = i32x4{gv[0], gv[1], gv[2], gv[3]};
+  };
+
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_codes(p, cd[p]);
+  // The table: lanes take adjacent groups of one column (adjacent scales);
+  // groups past kb go to the spare row kb, which no lookup reads.
+  for (int g0 = 0; g0 < kb; g0 += T) {
+    const int g = min(g0 + t, kb - 1);
+    float sv[CW], zv[CW];
+#pragma unroll
+    for (int cc = 0; cc < CW; ++cc) {
+      const int64_t n = min(col0 + cc, N - 1);
+      sv[cc] = dt<SDT>::to_f32(scales[n * kb + g]);
+      zv[cc] = (float)load_zp<BITS, HAS_ZP>(zp + n * zp_row_bytes, g);
+    }
+    const int row = g0 + t < kb ? g : kb;
+#pragma unroll
+    for (int cc = 0; cc < CW; ++cc) tab[row * TS + cc] = f32x2{sv[cc], zv[cc] * sv[cc]};
+  }
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  const unsigned char* tbytes = reinterpret_cast<const unsigned char*>(tab) + c * 8;
+  for (int ch = 0; ch < chunks; ++ch) {
+    // Chunk ch + PF's codes and chunk ch + 1's staging values (past the
+    // row: zeros from the buffer loads' range check and from stage_load),
+    // loaded without a branch so that the loop body stays one block.
+    load_codes(ch + PF, cd[PF]);
+    stage_load(ch + 1);
+    const int buf = ch & 1;
+    const float* xb = xs + buf * CH;
+    const int* gb = gs + buf * CH;
+#pragma unroll
+    for (int i = 0; i < UPC; ++i) {
+      const int kl = (i * 4 * W + s) * P;   // this lane's unit within the chunk
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        float q[R][WPU];
+#pragma unroll
+        for (int r = 0; r < R; ++r) word_codes_f32<BITS>(cd[0][r][i][wd], q[r]);
+#pragma unroll
+        for (int j4 = 0; j4 < WPU; j4 += 4) {
+          const int k4 = kl + wd * WPU + j4;
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(xb + k4);
+          const i32x4 g4 = *reinterpret_cast<const i32x4*>(gb + k4);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const unsigned char* e = tbytes + g4[jj];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const f32x2 sz = *reinterpret_cast<const f32x2*>(e + 128 * r);
+              const float w = fmaf(q[r][j4 + jj], sz.x, -sz.y);
+              acc[r] = fmaf(a4[jj], w, acc[r]);
+            }
+          }
+        }
+        // One word's LDS reads at a time: hoisting every read of the chunk
+        // would take the whole register file.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    stage_store(buf ^ 1);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < UPC; ++i) cd[p][r][i] = cd[p + 1][r][i];
+  }
+  // Slices of a wave (lanes c, c + 16, c + 32, c + 48), then the waves in
+  // order.
+  float* red = xs;   // [W][CW], free after the last barrier
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float v = acc[r];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (lane < 16) red[wave * CW + c + 16 * r] = v;
+  }
+  __syncthreads();
+  if (t < CW && col0 + t < N) {
+    float o = red[t];
+#pragma unroll
+    for (int w = 1; w < W; ++w) o += red[w * CW + t];
+    if (bias) o += dt<XDT>::to_f32(bias[col0 + t]);
+    Y[col0 + t] = dt<XDT>::from_f32(o);
+  }
+}
+
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int W, int PF>
+hipError_t launch_gemv_r(const MatArgs& a) {
+  using XT = typename dt<XDT>::T;
+  using ST = typename dt<SDT>::T;
+  const auto kern = gidx_gemv_kernel<BITS, XDT, SDT, HAS_ZP, R, W, PF>;
+  const int64_t lds = gidx_gemv_lds(a.kb, R, W);
+  if (lds > 64 * 1024) {
+    const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)GV_LDS_MAX);
+    if (e != hipSuccess) return e;
+  }
+  const int grid = (int)((a.N + 16 * R - 1) / (16 * R));
+  const int row_bytes = (int)(a.kb * a.blob);
+  const int64_t ch = 4 * W * GV_SLICE;
+  const int chunks = (int)((a.kb * a.block_size + ch - 1) / ch);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), (size_t)lds, a.stream, (const XT*)a.A, a.B,
+                     (const ST*)a.scales, a.zp, a.g_idx, (const XT*)a.bias, (XT*)a.Y, (int)a.K,
+                     (int)a.N, (int)a.kb, row_bytes, (int)a.zp_row_bytes, chunks);
+  return hipGetLastError();
+}
+
+// The M = 1 route: one column per lane (two measured no faster), codes one
+// chunk ahead (two or three chunks ahead measured slower); 8 waves (32
+// slices) when the grid has fewer than 512 workgroups and their LDS fits,
+// else 4 waves; 0 when neither fits (the row kernel then).
+int gidx_gemv_waves(const MatArgs& a) {
+  if (a.M != 1 || 16 * a.kb * a.blob >= ((int64_t)1 << 31)) return 0;
+  if ((a.N + 15) / 16 < 512 && gidx_gemv_lds(a.kb, 1, 8) <= GV_LDS_MAX) return 8;
+  return gidx_gemv_lds(a.kb, 1, 4) <= GV_LDS_MAX ? 4 : 0;
+}
+
+template <int BITS, int XDT, int SDT, bool HAS_ZP>
+hipError_t launch_gemv_t(const MatArgs& a) {
+  return gidx_gemv_waves(a) == 8 ? launch_gemv_r<BITS, XDT, SDT, HAS_ZP, 1, 8, 1>(a)
+                                 : launch_gemv_r<BITS, XDT, SDT, HAS_ZP, 1, 4, 1>(a);
+}
+
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 hipError_t launch_rows_t(const MatArgs& a) {
   using XT = typename dt<XDT>::T;
   using ST = typename dt<SDT>::T;
   constexpr int R = 2;
   const int grid = (int)((a.N + 4 * R - 1) / (4 * R));
+  if (gidx_gemv_waves(a) != 0) return launch_gemv_t<BITS, XDT, SDT, HAS_ZP>(a);
   // One row per pass for M = 1 (no idle accumulators), else 8.
   if (a.M == 1) {
     hipLaunchKernelGGL((gidx_rows_kernel<BITS, XDT, SDT, HAS_ZP, R, 1>), dim3(grid), dim3(256),

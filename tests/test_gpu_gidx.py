@@ -216,3 +216,34 @@ def test_every_route_exact(bits):
         else:
             y = run(case, g)
         assert torch.equal(y.cpu(), expect), name
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_decode_routes_exact(bits):
+    """Exact data through qmm_gemv with group indices on each M = 1 route:
+    the tabled kernel with 8 waves (fewer than 512 workgroups; ragged N and
+    K, f32 and f16 activations), with 4 waves (N 16400), with its LDS past
+    64 KiB (K 8192 at block 16: a table of 512 groups, 4 waves since 8 do
+    not fit), and the row kernel when no table fits (1024 groups)."""
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    rng = np.random.default_rng(301 + bits)
+    cases = [("eight waves f32", 1000, 77, 32, "f32", "f16"),
+             ("eight waves f16", 4100, 300, 64, "f16", "bf16"),
+             ("four waves", 512, 16400, 32, "bf16", "bf16"),
+             ("large table", 8192, 100, 16, "bf16", "f16"),
+             ("rows", 16384, 40, 16, "bf16", "bf16")]
+    for i, (name, K, N, bs, a_dtype, s_dtype) in enumerate(cases):
+        case = make_matmul_case(1, K, N, bs, bits, a_dtype=a_dtype, s_dtype=s_dtype,
+                                has_zp=i % 2 == 0, has_bias=i % 2 == 1, seed=700 + i)
+        case.A = torch.from_numpy(rng.integers(-3, 4, (1, K)).astype(np.float32)).to(case.A.dtype)
+        kb = case.k_blocks
+        case.scales = torch.from_numpy(
+            2.0 ** rng.integers(-4, 0, (N, kb)).astype(np.float32)).to(case.scales.dtype)
+        if case.bias is not None:
+            case.bias = torch.from_numpy(rng.integers(-8, 9, N).astype(np.float32)).to(case.A.dtype)
+        g = gidx_pattern("act_order", K, bs, kb, rng)
+        print(f"[gidx decode] {name}: K={K} N={N} bs={bs} bits={bits} a={a_dtype} s={s_dtype}",
+              flush=True)
+        Y, _ = oracle_y(case, g)
+        y = run(case, g, "gemv")
+        assert torch.equal(y.cpu(), torch.from_numpy(Y).to(case.A.dtype)), name
