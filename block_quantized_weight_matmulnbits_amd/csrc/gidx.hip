@@ -16,12 +16,13 @@
 // reads in bounds) in LDS; the lanes of a wave walk the chunk's 32-bit words
 // of codes of each of its columns (adjacent lanes, adjacent words), look up
 // each code's scale and zero point in the column's rows (cached reads) and
-// accumulate.  Used for M >= 2 with f32 activations and for M <= 16
-// otherwise when the matrix-core GEMM's table does not fit; larger M with
+// accumulate.  Used past gidx_gemv_kernel's rows with f32 activations, and
+// for M <= 16 otherwise when the matrix-core GEMM's table does not fit; larger M with
 // 16-bit activations runs the matrix-core GEMM with the same lookups
 // (gemm.hip, gidx_mfma.hip).
 //
-// gidx_gemv_kernel (M = 1, any activation dtype): a workgroup of W waves
+// gidx_gemv_kernel (M <= 4 or 8, any activation dtype; MT rows per launch,
+// every code dequantized once for them): a workgroup of W waves
 // owns CW = 16 R output columns and cuts K into 4 W slices; lane l of wave w
 // takes columns (l % 16) + 16 r and slice 4 w + l / 16.  A row of codes is
 // read in 16-byte units (128 / BITS codes each): chunk ch holds 64 codes of
@@ -121,19 +122,19 @@ __global__ __launch_bounds__(256) void gidx_rows_kernel(
 constexpr int GV_SLICE = 64;                // codes of a row per slice and chunk
 constexpr int64_t GV_LDS_MAX = 96 * 1024;
 
-// LDS of gidx_gemv_kernel: two staging buffers of a chunk (activation and
-// table offset per position), then the table.
-int64_t gidx_gemv_lds(int64_t kb, int R, int W) {
-  return (int64_t)2 * (4 * W * GV_SLICE) * 8 + (kb + 1) * (16 * R + 1) * 8;
+// LDS of gidx_gemv_kernel: two staging buffers of a chunk (MT activations
+// and a table offset per position), then the table.
+int64_t gidx_gemv_lds(int64_t kb, int R, int W, int MT) {
+  return (int64_t)2 * (4 * W * GV_SLICE) * (4 * MT + 4) + (kb + 1) * (16 * R + 1) * 8;
 }
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int W, int PF>
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int W, int PF, int MT>
 __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
     const typename dt<XDT>::T* __restrict__ A, const uint8_t* __restrict__ B,
     const typename dt<SDT>::T* __restrict__ scales, const uint8_t* __restrict__ zp,
     const int32_t* __restrict__ g_idx, const typename dt<XDT>::T* __restrict__ bias,
-    typename dt<XDT>::T* __restrict__ Y, int K, int N, int kb, int row_bytes, int zp_row_bytes,
-    int chunks) {
+    typename dt<XDT>::T* __restrict__ Y, int Mp, int K, int N, int kb, int row_bytes,
+    int zp_row_bytes, int chunks) {
   constexpr int CW = 16 * R, TS = CW + 1;
   constexpr int T = 64 * W;                     // threads
   constexpr int CH = 4 * W * GV_SLICE;          // codes of a row per chunk
@@ -142,9 +143,9 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   constexpr int WPU = 32 / BITS;                // codes per 32-bit word
   static_assert(CH == 4 * T, "each thread stages 4 positions of a chunk");
   extern __shared__ __align__(16) unsigned char gv_smem[];
-  float* xs = reinterpret_cast<float*>(gv_smem);                     // [2][CH]
-  int* gs = reinterpret_cast<int*>(gv_smem + 2 * CH * 4);            // [2][CH]
-  f32x2* tab = reinterpret_cast<f32x2*>(gv_smem + 2 * CH * 8);       // [kb + 1][TS]
+  float* xs = reinterpret_cast<float*>(gv_smem);                     // [2][MT][CH]
+  int* gs = reinterpret_cast<int*>(gv_smem + 2 * MT * CH * 4);       // [2][CH]
+  f32x2* tab = reinterpret_cast<f32x2*>(gv_smem + 2 * (MT + 1) * CH * 4);  // [kb + 1][TS]
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = lane & 15, s = wave * 4 + (lane >> 4);
   const int col0 = blockIdx.x * CW;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
         dst[r][i] = __builtin_amdgcn_raw_buffer_load_b128(
             rb, (c + 16 * r) * row_bytes + ((ch * UPC + i) * 4 * W + s) * 16, 0, BUF_STREAM);
   };
-  float xv[4];
+  float xv[MT][4];
   int gv[4];
   // Loads are unconditional (of an element in bounds) and selected after,
   // so that they are issued together; positions past K stage zeros.
@@ -172,14 +173,21 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
     for (int j = 0; j < 4; ++j) {
       const int k = ch * CH + t * 4 + j;
       const int kk = min(k, K - 1);
-      const float x = dt<XDT>::to_f32(A[kk]);
       const int g = min(max(g_idx[kk], 0), kb - 1);
-      xv[j] = k < K ? x : 0.0f;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        // Rows past Mp read row Mp - 1 and stage zeros.
+        const float x = dt<XDT>::to_f32(A[(int64_t)min(m, Mp - 1) * K + kk]);
+        xv[m][j] = (k < K && m < Mp) ? x : 0.0f;
+      }
       gv[j] = k < K ? g * (TS * 8) : 0;
     }
   };
   auto stage_store = [&](int buf) {
-    *reinterpret_cast<f32x4*>(xs + buf * CH + t * 4) = f32x4{xv[0], xv[1], xv[2], xv[3]};
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      *reinterpret_cast<f32x4*>(xs + (buf * MT + m) * CH + t * 4) =
+          f32x4{xv[m][0], xv[m][1], xv[m][2], xv[m][3]};
     *reinterpret_cast<i32x4*>(gs + buf * CH + t * 4) = i32x4{gv[0], gv[1], gv[2], gv[3]};
   };
 
@@ -204,9 +212,11 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   stage_store(0);
   __syncthreads();
 
-  float acc[R];
+  float acc[R][MT];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
   const unsigned char* tbytes = reinterpret_cast<const unsigned char*>(tab) + c * 8;
   for (int ch = 0; ch < chunks; ++ch) {
     // Chunk ch + PF's codes and chunk ch + 1's staging values (past the
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
     load_codes(ch + PF, cd[PF]);
     stage_load(ch + 1);
     const int buf = ch & 1;
-    const float* xb = xs + buf * CH;
+    const float* xb = xs + buf * MT * CH;
     const int* gb = gs + buf * CH;
 #pragma unroll
     for (int i = 0; i < UPC; ++i) {
@@ -228,7 +238,9 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
 #pragma unroll
         for (int j4 = 0; j4 < WPU; j4 += 4) {
           const int k4 = kl + wd * WPU + j4;
-          const f32x4 a4 = *reinterpret_cast<const f32x4*>(xb + k4);
+          f32x4 a4[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) a4[m] = *reinterpret_cast<const f32x4*>(xb + m * CH + k4);
           const i32x4 g4 = *reinterpret_cast<const i32x4*>(gb + k4);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
@@ -237,7 +249,8 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
             for (int r = 0; r < R; ++r) {
               const f32x2 sz = *reinterpret_cast<const f32x2*>(e + 128 * r);
               const float w = fmaf(q[r][j4 + jj], sz.x, -sz.y);
-              acc[r] = fmaf(a4[jj], w, acc[r]);
+#pragma unroll
+              for (int m = 0; m < MT; ++m) acc[r][m] = fmaf(a4[m][jj], w, acc[r][m]);
             }
           }
         }
@@ -257,58 +270,86 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   }
   // Slices of a wave (lanes c, c + 16, c + 32, c + 48), then the waves in
   // order.
-  float* red = xs;   // [W][CW], free after the last barrier
+  float* red = xs;   // [W][MT][CW], free after the last barrier
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float v = acc[r];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (lane < 16) red[wave * CW + c + 16 * r] = v;
-  }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = acc[r][m];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) red[(wave * MT + m) * CW + c + 16 * r] = v;
+    }
   __syncthreads();
-  if (t < CW && col0 + t < N) {
-    float o = red[t];
+  static_assert(MT * CW <= T, "one thread per output");
+  const int m = t / CW, cc = t % CW;
+  if (m < Mp && m < MT && col0 + cc < N) {
+    float o = red[m * CW + cc];
 #pragma unroll
-    for (int w = 1; w < W; ++w) o += red[w * CW + t];
-    if (bias) o += dt<XDT>::to_f32(bias[col0 + t]);
-    Y[col0 + t] = dt<XDT>::from_f32(o);
+    for (int w = 1; w < W; ++w) o += red[(w * MT + m) * CW + cc];
+    if (bias) o += dt<XDT>::to_f32(bias[col0 + cc]);
+    Y[(int64_t)m * N + col0 + cc] = dt<XDT>::from_f32(o);
   }
 }
 
-template <int BITS, int XDT, int SDT, bool HAS_ZP, int R, int W, int PF>
+// One launch per MT rows of A (each reads every code once for its rows).
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int W, int MT>
 hipError_t launch_gemv_r(const MatArgs& a) {
   using XT = typename dt<XDT>::T;
   using ST = typename dt<SDT>::T;
-  const auto kern = gidx_gemv_kernel<BITS, XDT, SDT, HAS_ZP, R, W, PF>;
-  const int64_t lds = gidx_gemv_lds(a.kb, R, W);
+  const auto kern = gidx_gemv_kernel<BITS, XDT, SDT, HAS_ZP, 1, W, 1, MT>;
+  const int64_t lds = gidx_gemv_lds(a.kb, 1, W, MT);
   if (lds > 64 * 1024) {
     const hipError_t e = ensure_dynamic_lds((const void*)kern, (int)GV_LDS_MAX);
     if (e != hipSuccess) return e;
   }
-  const int grid = (int)((a.N + 16 * R - 1) / (16 * R));
+  const int grid = (int)((a.N + 15) / 16);
   const int row_bytes = (int)(a.kb * a.blob);
   const int64_t ch = 4 * W * GV_SLICE;
   const int chunks = (int)((a.kb * a.block_size + ch - 1) / ch);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), (size_t)lds, a.stream, (const XT*)a.A, a.B,
-                     (const ST*)a.scales, a.zp, a.g_idx, (const XT*)a.bias, (XT*)a.Y, (int)a.K,
-                     (int)a.N, (int)a.kb, row_bytes, (int)a.zp_row_bytes, chunks);
-  return hipGetLastError();
+  for (int64_t m0 = 0; m0 < a.M; m0 += MT) {
+    const int Mp = (int)std::min<int64_t>(MT, a.M - m0);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), (size_t)lds, a.stream,
+                       (const XT*)a.A + m0 * a.K, a.B, (const ST*)a.scales, a.zp, a.g_idx,
+                       (const XT*)a.bias, (XT*)a.Y + m0 * a.N, Mp, (int)a.K, (int)a.N, (int)a.kb,
+                       row_bytes, (int)a.zp_row_bytes, chunks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-// The M = 1 route: one column per lane (two measured no faster), codes one
-// chunk ahead (two or three chunks ahead measured slower); 8 waves (32
-// slices) when the grid has fewer than 512 workgroups and their LDS fits,
-// else 4 waves; 0 when neither fits (the row kernel then).
+// The route for M <= 4, and M <= 8 when the matrix-core GEMM's grid of
+// 64-column tiles would cover under half the compute units (measured,
+// K 4096 N 14336: M = 2 / 4 / 8 30 / 38 / 75 us here against 59-60 us on the
+// matrix cores; K 14336 N 4096: 29 / 41 / 82 us against 170 us): one column
+// per lane (two measured no faster), codes one chunk ahead (two or three
+// chunks ahead measured slower), MT = 1, 2 or 4 rows per launch; 8 waves
+// (32 slices) when the grid has fewer than 512 workgroups and their LDS
+// fits, else 4 waves; 0 when neither fits (another kernel then).
+int gidx_gemv_rows(int64_t M) { return M == 1 ? 1 : M == 2 ? 2 : 4; }
+
 int gidx_gemv_waves(const MatArgs& a) {
-  if (a.M != 1 || 16 * a.kb * a.blob >= ((int64_t)1 << 31)) return 0;
-  if ((a.N + 15) / 16 < 512 && gidx_gemv_lds(a.kb, 1, 8) <= GV_LDS_MAX) return 8;
-  return gidx_gemv_lds(a.kb, 1, 4) <= GV_LDS_MAX ? 4 : 0;
+  const bool few = a.M <= 4 || (a.M <= 8 && (a.N + 63) / 64 < 128);
+  if (!few || 16 * a.kb * a.blob >= ((int64_t)1 << 31)) return 0;
+  const int mt = gidx_gemv_rows(a.M);
+  if ((a.N + 15) / 16 < 512 && gidx_gemv_lds(a.kb, 1, 8, mt) <= GV_LDS_MAX) return 8;
+  return gidx_gemv_lds(a.kb, 1, 4, mt) <= GV_LDS_MAX ? 4 : 0;
+}
+
+template <int BITS, int XDT, int SDT, bool HAS_ZP, int W>
+hipError_t launch_gemv_w(const MatArgs& a) {
+  switch (gidx_gemv_rows(a.M)) {
+    case 1: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 1>(a);
+    case 2: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 2>(a);
+    default: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 4>(a);
+  }
 }
 
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
 hipError_t launch_gemv_t(const MatArgs& a) {
-  return gidx_gemv_waves(a) == 8 ? launch_gemv_r<BITS, XDT, SDT, HAS_ZP, 1, 8, 1>(a)
-                                 : launch_gemv_r<BITS, XDT, SDT, HAS_ZP, 1, 4, 1>(a);
+  return gidx_gemv_waves(a) == 8 ? launch_gemv_w<BITS, XDT, SDT, HAS_ZP, 8>(a)
+                                 : launch_gemv_w<BITS, XDT, SDT, HAS_ZP, 4>(a);
 }
 
 template <int BITS, int XDT, int SDT, bool HAS_ZP>
@@ -365,7 +406,7 @@ hipError_t launch_rows_x(const MatArgs& a) {
 }  // namespace
 
 hipError_t launch_gidx(const MatArgs& a) {
-  if (gemm_mfma_gidx_supported(a)) return launch_gemm_mfma_gidx(a);
+  if (gidx_gemv_waves(a) == 0 && gemm_mfma_gidx_supported(a)) return launch_gemm_mfma_gidx(a);
   switch (a.bits) {
     case 2: return launch_rows_x<2>(a);
     case 4: return launch_rows_x<4>(a);
