@@ -21,7 +21,7 @@
 // 16-bit activations runs the matrix-core GEMM with the same lookups
 // (gemm.hip, gidx_mfma.hip).
 //
-// gidx_gemv_kernel (M <= 4 or 8, any activation dtype; MT rows per launch,
+// gidx_gemv_kernel (M <= 4 or 16, any activation dtype; MT rows per launch,
 // every code dequantized once for them): a workgroup of W waves
 // owns CW = 16 R output columns and cuts K into 4 W slices; lane l of wave w
 // takes columns (l % 16) + 16 r and slice 4 w + l / 16.  A row of codes is
@@ -319,18 +319,19 @@ hipError_t launch_gemv_r(const MatArgs& a) {
   return hipSuccess;
 }
 
-// The route for M <= 4, and M <= 8 when the matrix-core GEMM's grid of
+// The route for M <= 4, and M <= 16 when the matrix-core GEMM's grid of
 // 64-column tiles would cover under half the compute units (measured,
-// K 4096 N 14336: M = 2 / 4 / 8 30 / 38 / 75 us here against 59-60 us on the
-// matrix cores; K 14336 N 4096: 29 / 41 / 82 us against 170 us): one column
-// per lane (two measured no faster), codes one chunk ahead (two or three
-// chunks ahead measured slower), MT = 1, 2 or 4 rows per launch; 8 waves
+// K 4096 N 14336: M = 2 / 4 30 / 38 us here against 59-60 us on the matrix
+// cores, M = 8 75 us against 60; K 14336 N 4096: M = 2 / 4 / 8 / 16
+// 29 / 42 / 72 / 144 us against 170-176 us): one column per lane (two
+// measured no faster), codes one chunk ahead (two or three chunks ahead
+// measured slower), MT = 1, 2, 4 or 8 rows per launch; 8 waves
 // (32 slices) when the grid has fewer than 512 workgroups and their LDS
 // fits, else 4 waves; 0 when neither fits (another kernel then).
-int gidx_gemv_rows(int64_t M) { return M == 1 ? 1 : M == 2 ? 2 : 4; }
+int gidx_gemv_rows(int64_t M) { return M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8; }
 
 int gidx_gemv_waves(const MatArgs& a) {
-  const bool few = a.M <= 4 || (a.M <= 8 && (a.N + 63) / 64 < 128);
+  const bool few = a.M <= 4 || (a.M <= 16 && (a.N + 63) / 64 < 128);
   if (!few || 16 * a.kb * a.blob >= ((int64_t)1 << 31)) return 0;
   const int mt = gidx_gemv_rows(a.M);
   if ((a.N + 15) / 16 < 512 && gidx_gemv_lds(a.kb, 1, 8, mt) <= GV_LDS_MAX) return 8;
@@ -342,7 +343,8 @@ hipError_t launch_gemv_w(const MatArgs& a) {
   switch (gidx_gemv_rows(a.M)) {
     case 1: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 1>(a);
     case 2: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 2>(a);
-    default: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 4>(a);
+    case 4: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 4>(a);
+    default: return launch_gemv_r<BITS, XDT, SDT, HAS_ZP, W, 8>(a);
   }
 }
 

@@ -183,7 +183,8 @@ def test_every_route_exact(bits):
     at least 256 workgroups, table of at most 63 groups) and with 64-column
     tiles (M = 6 on a grid of 257 workgroups, M = 16, ragged N), the
     256-column kernel with lookups in memory (M > 16, a table of 160 groups
-    does not fit in LDS), the row kernel (M = 12, same), and a group-index
+    does not fit in LDS), the row kernel (M = 12 on a grid of 129
+    workgroups, same table), and a group-index
     array that is not 16-byte aligned (the tabled kernel reads it 16 bytes
     at a time)."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
@@ -192,7 +193,7 @@ def test_every_route_exact(bits):
              ("table64 M6", 6, 1032, 16400, 64, "f16", "f16"),
              ("table64 M16", 16, 776, 97, 16, "bf16", "bf16"),
              ("memory", 40, 2560, 130, 16, "bf16", "f16"),
-             ("rows", 12, 2560, 70, 16, "f16", "bf16"),
+             ("rows", 12, 2560, 8200, 16, "f16", "bf16"),
              ("unaligned", 24, 512, 200, 32, "bf16", "bf16")]
     for i, (name, M, K, N, bs, a_dtype, s_dtype) in enumerate(cases):
         case = make_matmul_case(M, K, N, bs, bits, a_dtype=a_dtype, s_dtype=s_dtype,
@@ -225,8 +226,9 @@ def test_gemv_routes_exact(bits):
     shapes: 8 waves (fewer than 512 workgroups; ragged N and K, f32 and f16
     activations), 4 waves (N 16400), LDS past 64 KiB (K 8192 at block 16: a
     table of 512 groups, 4 waves since 8 do not fit), 2 rows, 3 rows (one
-    idle row slot), 8 rows (two launches of 4 on a short matrix-core grid),
-    and the row kernel when no table fits (1024 groups)."""
+    idle row slot), 8 rows and 12 rows (two launches of 8, the second with 4
+    rows) on a short matrix-core grid, and the row kernel when no table fits
+    (1024 groups)."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
     rng = np.random.default_rng(301 + bits)
     cases = [("eight waves f32", 1, 1000, 77, 32, "f32", "f16"),
@@ -236,6 +238,7 @@ def test_gemv_routes_exact(bits):
              ("two rows", 2, 1000, 300, 32, "bf16", "bf16"),
              ("three rows", 3, 2100, 100, 64, "f16", "f16"),
              ("eight rows", 8, 4096, 200, 32, "bf16", "f32"),
+             ("twelve rows", 12, 1000, 150, 32, "f16", "bf16"),
              ("rows", 1, 16384, 40, 16, "bf16", "bf16")]
     for i, (name, M, K, N, bs, a_dtype, s_dtype) in enumerate(cases):
         case = make_matmul_case(M, K, N, bs, bits, a_dtype=a_dtype, s_dtype=s_dtype,
