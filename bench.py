@@ -70,7 +70,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU-oracle sample")
     p.add_argument("--only", choices=["compint8", "prefill", "conv", "tiny", "fp4", "lowbit", "batched",
-                                      "lowp"],
+                                      "lowp", "gidx"],
                    default=None,
                    help="time only this workload and print its object (profiling runs)")
     p.add_argument("--read-sweep", action="store_true",
@@ -112,7 +112,7 @@ def main():
             del src, dst
         fn = {"compint8": bench_compint8, "prefill": bench_prefill, "conv": bench_conv,
               "tiny": bench_tiny, "fp4": bench_fp4, "lowbit": bench_lowbit,
-              "batched": bench_batched, "lowp": bench_lowp}[args.only]
+              "batched": bench_batched, "lowp": bench_lowp, "gidx": bench_gidx}[args.only]
         print(json.dumps({args.only: fn(qmm, dev, stream, args)}), flush=True)
         return
     if args.copy_calibration:
@@ -356,6 +356,7 @@ def main():
     out["fp4"] = bench_fp4(qmm, dev, stream, args)
     out["lowbit"] = bench_lowbit(qmm, dev, stream, args)
     out["lowp"] = bench_lowp(qmm, dev, stream, args)
+    out["gidx"] = bench_gidx(qmm, dev, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
@@ -820,6 +821,69 @@ def bench_lowbit(qmm, dev, stream, args):
     flop = 2.0 * c.M * c.N * c.K
     res["b3_prefill_M2048"] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
                                "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
+def bench_gidx(qmm, dev, stream, args):
+    """Group indices (act-order g_idx) on the decode-shaped projection K=4096
+    N=14336, 4-bit asymmetric bs 32, bf16 scales and activations, operator
+    layout: g_idx[k] = rank(k) // 32 for a seeded random order of K (every
+    group has 32 members).  M = 1 (qmm_gemv), 2 and 16 (qmm_gemm; the tabled
+    GEMV and the tabled MFMA kernel) with weights rotating through copies so
+    each launch streams them from HBM (bytes include the index array), and
+    the prefill M = 2048 (TFLOP/s)."""
+    import numpy as np
+    from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
+    K, N, bs = 4096, 14336, 32
+    rng = np.random.default_rng(71)
+    order = rng.permutation(K)
+    rank = np.empty(K, np.int64)
+    rank[order] = np.arange(K)
+    gi = torch.from_numpy((rank // bs).astype(np.int32)).to(dev)
+    base = make_matmul_case(1, K, N, bs, 4, a_dtype="bf16", has_zp=True, seed=72).to(dev)
+    nbytes = base.weight_bytes() + K * 4
+    n_copies = max(2, -(-POOL_BYTES // nbytes))
+    pool = [(base.B, base.scales, base.zero_points)] + [
+        (base.B.clone(), base.scales.clone(), base.zero_points.clone())
+        for _ in range(n_copies - 1)]
+    res = {"workload": "K=4096 N=14336, 4-bit asymmetric bs 32, bf16, act-order g_idx"}
+    for M in (1, 2, 16):
+        c = make_matmul_case(M, K, N, bs, 4, a_dtype="bf16", has_zp=True, seed=73 + M)
+        A = c.A.to(dev)
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+        def run(i, A=A, Y=Y, M=M):
+            B, sc, zp = pool[i % len(pool)]
+            if M == 1:
+                qmm.qmm_gemv(A.reshape(-1), B, sc, zp, None, Y.reshape(-1), K, N, bs, 4,
+                             stream=stream, g_idx=gi)
+            else:
+                qmm.qmm_gemm(A, B, sc, zp, None, Y, M, K, N, bs, 4, stream=stream, g_idx=gi)
+
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        ms = _time_launches(run, max(10, args.steps // 4), stream)
+        byts = nbytes + A.numel() * 2 + M * N * 2
+        res[f"M{M}"] = {"us": round(ms * 1e3, 2), "bytes": byts,
+                        "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del pool
+    c = make_matmul_case(2048, K, N, bs, 4, a_dtype="bf16", has_zp=True, seed=74).to(dev)
+    Y = torch.empty(c.M, N, dtype=torch.bfloat16, device=dev)
+
+    def runp(_):
+        qmm.qmm_gemm(c.A, c.B, c.scales, c.zero_points, None, Y, c.M, K, N, bs, 4, stream=stream,
+                     g_idx=gi)
+
+    for i in range(3):
+        runp(i)
+    torch.cuda.synchronize()
+    ms = _time_launches(runp, max(20, args.steps // 5), stream)
+    flop = 2.0 * c.M * N * K
+    res["prefill_M2048"] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                            "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                                    4)}
     return res
 
 
