@@ -227,8 +227,8 @@ def test_gemv_routes_exact(bits):
     activations), 4 waves (N 16400), LDS past 64 KiB (K 8192 at block 16: a
     table of 512 groups, 4 waves since 8 do not fit), 2 rows, 3 rows (one
     idle row slot), 8 rows and 12 rows (two launches of 8, the second with 4
-    rows) on a short matrix-core grid, and the row kernel when no table fits
-    (1024 groups)."""
+    rows) on a short matrix-core grid, the row kernel when no table fits
+    (1024 groups), and the smallest shapes (one block, one column; N = 5)."""
     from block_quantized_weight_matmulnbits_amd.workloads import make_matmul_case
     rng = np.random.default_rng(301 + bits)
     cases = [("eight waves f32", 1, 1000, 77, 32, "f32", "f16"),
@@ -239,7 +239,9 @@ def test_gemv_routes_exact(bits):
              ("three rows", 3, 2100, 100, 64, "f16", "f16"),
              ("eight rows", 8, 4096, 200, 32, "bf16", "f32"),
              ("twelve rows", 12, 1000, 150, 32, "f16", "bf16"),
-             ("rows", 1, 16384, 40, 16, "bf16", "bf16")]
+             ("rows", 1, 16384, 40, 16, "bf16", "bf16"),
+             ("one block one column", 1, 16, 1, 16, "bf16", "bf16"),
+             ("four rows five columns", 4, 40, 5, 16, "f32", "f32")]
     for i, (name, M, K, N, bs, a_dtype, s_dtype) in enumerate(cases):
         case = make_matmul_case(M, K, N, bs, bits, a_dtype=a_dtype, s_dtype=s_dtype,
                                 has_zp=i % 2 == 0, has_bias=i % 2 == 1, seed=700 + i)
