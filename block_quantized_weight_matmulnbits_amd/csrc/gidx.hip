@@ -30,10 +30,11 @@
 // of a wave covers 64 contiguous bytes of 16 columns, through one buffer
 // resource for the workgroup's rows).  Before the K loop the workgroup
 // builds in LDS the table of its columns' {scale, zp * scale} in fp32 for
-// every group (entry (g, c) at g (CW + 1) + c), and per chunk it stages the
-// chunk's activations (fp32) and group indices (clamped into 0..kb-1, stored
-// as byte offsets of table rows) in a double buffer, loaded one chunk ahead
-// like the codes.  The 16 lanes of a quarter wave work on the same code
+// every group (entry (g, c) at g (CW + 1) + c); per chunk each wave stages
+// its own slices' activations (fp32) and group indices (clamped into
+// 0..kb-1, stored as byte offsets of table rows) in a double buffer, loaded
+// one chunk ahead like the codes, so the chunk loop has no workgroup
+// barrier.  The 16 lanes of a quarter wave work on the same code
 // position, so they read one table row's adjacent entries.  Per code: one
 // address add, one 8-byte table read per column, fma(q, scale, -zp * scale)
 // (the exact dequantized value for 16-bit scales) and the fma into the
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   constexpr int P = 128 / BITS;                 // codes per 16-byte unit
   constexpr int UPC = GV_SLICE / P;             // units per slice per chunk
   constexpr int WPU = 32 / BITS;                // codes per 32-bit word
+  constexpr int WCH = CH / W;                   // positions a wave stages per chunk
   static_assert(CH == 4 * T, "each thread stages 4 positions of a chunk");
   extern __shared__ __align__(16) unsigned char gv_smem[];
   float* xs = reinterpret_cast<float*>(gv_smem);                     // [2][MT][CH]
@@ -166,12 +168,18 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   };
   float xv[MT][4];
   int gv[4];
+  // Each wave stages the positions of its own 4 slices (entry (i, q, e) of
+  // its region: unit i of slice 4 w + q, code e), so that only the wave
+  // reads what it wrote and the chunk loop needs no workgroup barrier.
+  // Lane l stages entries 4 l .. 4 l + 3 (one unit, consecutive codes).
+  const int sidx = lane * 4, si = sidx / (4 * P), sq = (sidx / P) % 4, se = sidx % P;
+  const int skl = (si * 4 * W + wave * 4 + sq) * P + se;   // its chunk offset
   // Loads are unconditional (of an element in bounds) and selected after,
   // so that they are issued together; positions past K stage zeros.
   auto stage_load = [&](int ch) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = ch * CH + t * 4 + j;
+      const int k = ch * CH + skl + j;
       const int kk = min(k, K - 1);
       const int g = min(max(g_idx[kk], 0), kb - 1);
 #pragma unroll
@@ -186,9 +194,9 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      *reinterpret_cast<f32x4*>(xs + (buf * MT + m) * CH + t * 4) =
+      *reinterpret_cast<f32x4*>(xs + (buf * MT + m) * CH + wave * WCH + sidx) =
           f32x4{xv[m][0], xv[m][1], xv[m][2], xv[m][3]};
-    *reinterpret_cast<i32x4*>(gs + buf * CH + t * 4) = i32x4{gv[0], gv[1], gv[2], gv[3]};
+    *reinterpret_cast<i32x4*>(gs + buf * CH + wave * WCH + sidx) = i32x4{gv[0], gv[1], gv[2], gv[3]};
   };
 
 #pragma unroll
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
     const int* gb = gs + buf * CH;
 #pragma unroll
     for (int i = 0; i < UPC; ++i) {
-      const int kl = (i * 4 * W + s) * P;   // this lane's unit within the chunk
+      const int kl = wave * WCH + (i * 4 + (lane >> 4)) * P;   // this lane's unit, staged
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         float q[R][WPU];
@@ -260,7 +268,11 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
       }
     }
     stage_store(buf ^ 1);
-    __syncthreads();
+    // The wave's own LDS writes and reads run in order: a compiler fence is
+    // all the double buffer needs.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int p = 0; p < PF; ++p)
 #pragma unroll
@@ -270,7 +282,8 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
   }
   // Slices of a wave (lanes c, c + 16, c + 32, c + 48), then the waves in
   // order.
-  float* red = xs;   // [W][MT][CW], free after the last barrier
+  __syncthreads();   // every wave done with its staging before red reuses it
+  float* red = xs;   // [W][MT][CW]
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -321,20 +334,21 @@ hipError_t launch_gemv_r(const MatArgs& a) {
 
 // The route for M <= 4, and M <= 16 when the matrix-core GEMM's grid of
 // 64-column tiles would cover under half the compute units (measured,
-// K 4096 N 14336: M = 2 / 4 30 / 38 us here against 59-60 us on the matrix
-// cores, M = 8 75 us against 60; K 14336 N 4096: M = 2 / 4 / 8 / 16
-// 29 / 42 / 72 / 144 us against 170-176 us): one column per lane (two
-// measured no faster), codes one chunk ahead (two or three chunks ahead
-// measured slower), MT = 1, 2, 4 or 8 rows per launch; 8 waves
-// (32 slices) when the grid has fewer than 512 workgroups and their LDS
-// fits, else 4 waves; 0 when neither fits (another kernel then).
+// K 4096 N 14336: M = 1 / 2 / 4 20 / 32 / 37 us here against 59-60 us on
+// the matrix cores for M >= 2, M = 8 75 us against 60; K 14336 N 4096:
+// M = 1 / 2 / 4 / 8 / 16 21 / 31 / 39 / 62 / 124 us against 170-176 us):
+// one column per lane (two measured no faster), codes one chunk ahead (two
+// or three chunks ahead measured slower), MT = 1, 2, 4 or 8 rows per launch;
+// 8 waves (32 slices) when the grid has fewer than 512 workgroups or for two
+// rows (31 against 40 us with 4 waves at N 14336; one row: 25 against 20),
+// if their LDS fits, else 4 waves; 0 when neither fits (another kernel then).
 int gidx_gemv_rows(int64_t M) { return M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8; }
 
 int gidx_gemv_waves(const MatArgs& a) {
   const bool few = a.M <= 4 || (a.M <= 16 && (a.N + 63) / 64 < 128);
   if (!few || 16 * a.kb * a.blob >= ((int64_t)1 << 31)) return 0;
   const int mt = gidx_gemv_rows(a.M);
-  if ((a.N + 15) / 16 < 512 && gidx_gemv_lds(a.kb, 1, 8, mt) <= GV_LDS_MAX) return 8;
+  if (((a.N + 15) / 16 < 512 || mt == 2) && gidx_gemv_lds(a.kb, 1, 8, mt) <= GV_LDS_MAX) return 8;
   return gidx_gemv_lds(a.kb, 1, 4, mt) <= GV_LDS_MAX ? 4 : 0;
 }
 
