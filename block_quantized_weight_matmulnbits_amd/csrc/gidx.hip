@@ -201,6 +201,7 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
 
 #pragma unroll
   for (int p = 0; p < PF; ++p) load_codes(p, cd[p]);
+  stage_load(0);   // in flight with the table's loads
   // The table: lanes take adjacent groups of one column (adjacent scales);
   // groups past kb go to the spare row kb, which no lookup reads.
   for (int g0 = 0; g0 < kb; g0 += T) {
@@ -216,7 +217,6 @@ __global__ __launch_bounds__(64 * W) void gidx_gemv_kernel(
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc) tab[row * TS + cc] = f32x2{sv[cc], zv[cc] * sv[cc]};
   }
-  stage_load(0);
   stage_store(0);
   __syncthreads();
 
@@ -334,9 +334,9 @@ hipError_t launch_gemv_r(const MatArgs& a) {
 
 // The route for M <= 4, and M <= 16 when the matrix-core GEMM's grid of
 // 64-column tiles would cover under half the compute units (measured,
-// K 4096 N 14336: M = 1 / 2 / 4 20 / 32 / 37 us here against 59-60 us on
+// K 4096 N 14336: M = 1 / 2 / 4 20 / 28 / 37 us here against 59-60 us on
 // the matrix cores for M >= 2, M = 8 75 us against 60; K 14336 N 4096:
-// M = 1 / 2 / 4 / 8 / 16 21 / 31 / 39 / 62 / 124 us against 170-176 us):
+// M = 1 / 2 / 4 / 8 / 16 19 / 22 / 40 / 64 / 127 us against 170-176 us):
 // one column per lane (two measured no faster), codes one chunk ahead (two
 // or three chunks ahead measured slower), MT = 1, 2, 4 or 8 rows per launch;
 // 8 waves (32 slices) when the grid has fewer than 512 workgroups or for two
