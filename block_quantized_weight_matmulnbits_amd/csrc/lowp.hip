@@ -187,29 +187,48 @@ __global__ __launch_bounds__(128 * WM) void lowp_mfma_kernel(
       }
     }
   };
+  // LDS fragment slots, swizzled against bank conflicts (banks are 4 bytes
+  // wide, 64 of them): the entry of (row r of a 16-row tile, lane group g)
+  // is 16 g + (r ^ swz(g)), swz(g) = 4 g for 16-byte slots and g for 32-byte
+  // ones, so that the four groups of one row (stored by adjacent threads)
+  // land in different banks; a 32-byte slot of a row with bit 3 set holds its
+  // two 16-byte halves swapped, so that the two reads of a fragment (16 bytes
+  // at a 32-byte stride) spread lanes l and l + 8 over different banks.  The
+  // reads see each 16-lane group's entries permuted within their 256 or 512
+  // bytes.
+  auto put = [&](uint8_t* base, int slot, int bits, int row, int g, int half, const uint32_t* o) {
+    const int r = row & 15;
+    const int swz = slot == 16 ? 4 * g : g;
+    const int e = ((row >> 4) * 4 + g) * 16 + (r ^ swz);
+    uint32_t* d = reinterpret_cast<uint32_t*>(base + e * slot);
+    const int hs = (slot == 32 && (r & 8)) ? 4 : 0;
+    if (bits == 8) {
+      // A whole 16-byte half: one store.
+      *reinterpret_cast<u32x4*>(d + ((4 * half) ^ hs)) = u32x4{o[0], o[1], o[2], o[3]};
+    } else if (bits == 4) {
+      *reinterpret_cast<u32x2*>(d + 2 * half) = u32x2{o[0], o[1]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) d[(half * 3 + j) ^ hs] = o[j];
+    }
+  };
   auto store = [&](int buf, int st) {
     int g, half;
 #pragma unroll
     for (int p = 0; p < PA; ++p) {
       const int row = RPP * p + lrow;
       piece_slot(LowpFmt<LF>::BITS, g, half);
-      const int fa = ((row >> 4) * 4 + g) * 16 + (row & 15);
       uint32_t o[4];
       pack16<LF>(pa[st][p], o);
-      uint32_t* da = reinterpret_cast<uint32_t*>(As + buf * LST + fa * LS + half * (2 * LowpFmt<LF>::BITS));
-#pragma unroll
-      for (int j = 0; j < LowpFmt<LF>::BITS / 2; ++j) da[j] = o[j];
+      put(As + buf * LST, LS, LowpFmt<LF>::BITS, row, g, half, o);
     }
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
       const int row = RPP * p + lrow;
       piece_slot(LowpFmt<RF>::BITS, g, half);
-      const int fb = ((row >> 4) * 4 + g) * 16 + (row & 15);
       uint32_t o[4];
       pack16<RF>(pb[st][p], o);
-      uint32_t* db = reinterpret_cast<uint32_t*>(Bs + buf * RST + fb * RS + half * (2 * LowpFmt<RF>::BITS));
-#pragma unroll
-      for (int j = 0; j < LowpFmt<RF>::BITS / 2; ++j) db[j] = o[j];
+      put(Bs + buf * RST, RS, LowpFmt<RF>::BITS, row, g, half, o);
     }
     if constexpr (SS) {
 #pragma unroll
@@ -244,13 +263,17 @@ __global__ __launch_bounds__(128 * WM) void lowp_mfma_kernel(
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto frag = [&](const uint8_t* base, int slot, int tile) {
-    // Fragment (tile, lane): 16, 24 or 32 bytes at (tile * 64 + lane) * slot.
-    const uint8_t* p = base + (tile * 64 + lane) * slot;
+    // Fragment (tile, lane): 16, 24 or 32 bytes of the lane's swizzled entry
+    // (see put).
+    const int g = lane >> 4, r = lane & 15;
+    const int e = tile * 64 + g * 16 + (r ^ (slot == 16 ? 4 * g : g));
+    const uint8_t* p = base + e * slot;
+    const int hs = (slot == 32 && (r & 8)) ? 16 : 0;
     v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p + hs);
     v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
     if (slot == 32) {
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(p + (16 - hs));
       v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
     }
     return v;
