@@ -187,18 +187,18 @@ __global__ __launch_bounds__(128 * WM) void lowp_mfma_kernel(
       }
     }
   };
-  // LDS fragment slots, swizzled against bank conflicts (banks are 4 bytes
-  // wide, 64 of them): the entry of (row r of a 16-row tile, lane group g)
-  // is 16 g + (r ^ swz(g)), swz(g) = 4 g for 16-byte slots and g for 32-byte
-  // ones, so that the four groups of one row (stored by adjacent threads)
-  // land in different banks; a 32-byte slot of a row with bit 3 set holds its
+  // LDS fragment slots, swizzled against bank conflicts (these accesses see
+  // 32 banks of 4 bytes, as measured): the entry of (row r of a 16-row tile,
+  // lane group g) is 16 g + (r ^ swz(g)), swz(g) = 2 g for 16-byte slots and
+  // g for 32-byte ones, so that the four groups of one row (stored by
+  // adjacent threads) land in different banks; a 32-byte slot of a row with bit 3 set holds its
   // two 16-byte halves swapped, so that the two reads of a fragment (16 bytes
   // at a 32-byte stride) spread lanes l and l + 8 over different banks.  The
   // reads see each 16-lane group's entries permuted within their 256 or 512
   // bytes.
   auto put = [&](uint8_t* base, int slot, int bits, int row, int g, int half, const uint32_t* o) {
     const int r = row & 15;
-    const int swz = slot == 16 ? 4 * g : g;
+    const int swz = slot == 16 ? 2 * g : g;
     const int e = ((row >> 4) * 4 + g) * 16 + (r ^ swz);
     uint32_t* d = reinterpret_cast<uint32_t*>(base + e * slot);
     const int hs = (slot == 32 && (r & 8)) ? 4 : 0;
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(128 * WM) void lowp_mfma_kernel(
     // Fragment (tile, lane): 16, 24 or 32 bytes of the lane's swizzled entry
     // (see put).
     const int g = lane >> 4, r = lane & 15;
-    const int e = tile * 64 + g * 16 + (r ^ (slot == 16 ? 4 * g : g));
+    const int e = tile * 64 + g * 16 + (r ^ (slot == 16 ? 2 * g : g));
     const uint8_t* p = base + e * slot;
     const int hs = (slot == 32 && (r & 8)) ? 16 : 0;
     v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -376,6 +376,8 @@ __global__ __launch_bounds__(LTPB) void lowp_nvfp4_kernel(
   const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc((void*)rsc, 0, n * nblk, BUF_WORD3);
 
   const int lrow = tid >> 3, lkk = (tid & 7) * 16;
+  // This lane's swizzled fragment entry in K sub-step ks (see put).
+  auto lsw = [&](int ks) { return (lane & 48) | ((lane & 15) ^ (2 * ks + ((lane >> 5) & 1))); };
   u32x4 pa[4], pb[4];
   uint32_t qa[4], qb[4];                  // the pieces' E4M3 scale bytes
   auto load = [&](int k0) {
@@ -421,8 +423,12 @@ __global__ __launch_bounds__(LTPB) void lowp_nvfp4_kernel(
           two(4 * i + j, f32x2{lowp_decode<F>(w[i] >> (8 * j)), lowp_decode<F>(w[i] >> (8 * (j + 1)))});
       }
     }
+    // Fragment entry (row r, lane group g) of K sub-step ks at
+    // 16 g + (r ^ (2 ks + g / 2)): the eight pieces of a row, stored by
+    // adjacent threads, then fall in eight different banks of the 32 these
+    // accesses see (reads permute within a group's 256 bytes).
     const int ks = lkk / 32, g0 = (lkk & 31) / 8;
-    const int t = row >> 4, r = row & 15;
+    const int t = row >> 4, r = (row & 15) ^ (2 * ks + g0 / 2);
     u32x4* d0 = reinterpret_cast<u32x4*>(st + ((((ks * 8 + t) * 4 + g0) * 16 + r) * 16));
     u32x4* d1 = reinterpret_cast<u32x4*>(st + ((((ks * 8 + t) * 4 + g0 + 1) * 16 + r) * 16));
     *d0 = u32x4{pk[0], pk[1], pk[2], pk[3]};
@@ -457,11 +463,11 @@ __global__ __launch_bounds__(LTPB) void lowp_nvfp4_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         b[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                                bs + ((ks * 8 + (wn >> 4) + j) * 64 + lane) * 16));
+                                                bs + ((ks * 8 + (wn >> 4) + j) * 64 + lsw(ks)) * 16));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
-                                                            as + ((ks * 8 + (wm >> 4) + i) * 64 + lane) * 16));
+                                                            as + ((ks * 8 + (wm >> 4) + i) * 64 + lsw(ks)) * 16));
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
