@@ -98,7 +98,19 @@ __device__ __forceinline__ float raw_to_f32(uint16_t h) {
   else return (float)__builtin_bit_cast(_Float16, h);
 }
 
-template <int BITS, int XDT>
+// 16-byte piece slot of logical piece j of unit u when units hold NP pieces
+// (NP = 0: no swizzle).  The pieces of a unit are XOR-permuted by a function
+// of the unit so that the 8 lanes of an LDS read pass (consecutive units,
+// the same logical piece, units 8 NP words apart) fall in distinct banks of
+// the 32 that these accesses see: without it, units 64 bytes apart (4-bit)
+// put lanes 2 apart in one bank.
+template <int NP>
+__device__ __forceinline__ int x_piece(int u, int j) {
+  if constexpr (NP == 0) return u * 0 + j;
+  else return u * NP + (j ^ ((u / (8 / NP)) % NP));
+}
+
+template <int BITS, int XDT, int NP>
 __device__ __forceinline__ void stage_pass(const XRaw<BITS>& r, int base,
                                            uint32_t* __restrict__ xs, float* __restrict__ pw,
                                            int* inexact) {
@@ -153,11 +165,12 @@ __device__ __forceinline__ void stage_pass(const XRaw<BITS>& r, int base,
       pairs[w * (P / 2) + i] = as_u32(h);
     }
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(xs + base / 2);
+  u32x4* dst = reinterpret_cast<u32x4*>(xs);
 #pragma unroll
   for (int j = 0; j < TE / 8; ++j) {
     u32x4 t = {pairs[4 * j], pairs[4 * j + 1], pairs[4 * j + 2], pairs[4 * j + 3]};
-    dst[j] = t;
+    const int pg = base / 8 + j;   // piece of the chunk
+    dst[NP ? x_piece<NP>(pg / (NP ? NP : 1), pg % (NP ? NP : 1)) : pg] = t;
   }
   if ((threadIdx.x % TPU) == 0) pw[base / E] = ldexpf(1.0f, -sh);
 }
@@ -215,6 +228,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
   constexpr int E = G::E;
   constexpr int UW = VEC ? 4 : 1;   // 32-bit words per unit
   constexpr int UE = UW * P;        // activations per unit
+  // 16-byte pieces per unit whose LDS slots are swizzled (16-byte units:
+  // 2, 4 or 8 pieces; 4-byte units are read a word at a time, unswizzled).
+  constexpr int XNP = VEC ? UE / 8 : 0;
   extern __shared__ u32x4 smem_v[];
   // Staged activations per chunk, rounded up to whole 16-byte units of codes.
   const int staged = (chunk_units * UE + E - 1) / E * E;
@@ -313,12 +329,12 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
       // Stage x into LDS.
       if (threadIdx.x == 0) inexact[ci & 1] = 0;
       __syncthreads();
-      if (b0 < len_units) stage_pass<BITS, XDT>(xr0, b0, xs, pw, &inexact[ci & 1]);
-      if (b1 < len_units) stage_pass<BITS, XDT>(xr1, b1, xs, pw, &inexact[ci & 1]);
+      if (b0 < len_units) stage_pass<BITS, XDT, XNP>(xr0, b0, xs, pw, &inexact[ci & 1]);
+      if (b1 < len_units) stage_pass<BITS, XDT, XNP>(xr1, b1, xs, pw, &inexact[ci & 1]);
       for (int b = b1 + G::PASS; b < len_units; b += G::PASS) {
         XRaw<BITS> xr;
         load_x_raw<BITS, XDT>((const uint16_t*)x, c0 * UE + b, K, x_vec, xr);
-        stage_pass<BITS, XDT>(xr, b, xs, pw, &inexact[ci & 1]);
+        stage_pass<BITS, XDT, XNP>(xr, b, xs, pw, &inexact[ci & 1]);
       }
       __syncthreads();
       exact = inexact[ci & 1] != 0;
@@ -337,10 +353,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(
               const int lu = min(lu_raw, c1 - c0 - 1);
               uint32_t xw[UE / 2];
               if constexpr (VEC) {
-                const u32x4* xv = reinterpret_cast<const u32x4*>(xs + lu * (UE / 2));
+                const u32x4* xv = reinterpret_cast<const u32x4*>(xs);
 #pragma unroll
                 for (int j = 0; j < UE / 8; ++j) {
-                  const u32x4 t = xv[j];
+                  const u32x4 t = xv[x_piece<XNP>(lu, j)];
                   xw[4 * j + 0] = t.x; xw[4 * j + 1] = t.y;
                   xw[4 * j + 2] = t.z; xw[4 * j + 3] = t.w;
                 }
